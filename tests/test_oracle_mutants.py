@@ -1,0 +1,163 @@
+"""Each pin must be able to fail: plant one plausible mistake in a copy of
+the oracle (on the CPU) and require that at least one pin catches it."""
+import types
+
+import numpy as np
+import pytest
+
+import pins
+from oracle import quest_oracle as O
+
+
+def _ns(**overrides):
+    ns = types.SimpleNamespace(**{n: getattr(O, n) for n in O.__all__})
+    for k, v in overrides.items():
+        setattr(ns, k, v)
+    return ns
+
+
+# ------------------------------------------------------------- the mutants
+
+def est_dropped_kmin(q, kmin, kmax, pt, lens, S, max_pages=None):
+    return O.estimate(q, kmax, kmax, pt, lens, S, max_pages)
+
+
+def est_min_instead_of_max(q, kmin, kmax, pt, lens, S, max_pages=None):
+    return -O.estimate(-q, kmin, kmax, pt, lens, S, max_pages)  # sum of mins
+
+
+def est_scaled(q, kmin, kmax, pt, lens, S, max_pages=None):
+    return O.estimate(q, kmin, kmax, pt, lens, S, max_pages) / np.sqrt(q.shape[-1])
+
+
+def est_no_indirection(q, kmin, kmax, pt, lens, S, max_pages=None):
+    ident = np.tile(np.arange(pt.shape[1]), (pt.shape[0], 1))
+    ident = np.minimum(ident, kmin.shape[0] - 1)
+    return O.estimate(q, kmin, kmax, ident, lens, S, max_pages)
+
+
+def est_first_head_only(q, kmin, kmax, pt, lens, S, max_pages=None):
+    B, Hq, d = q.shape
+    H = kmin.shape[1]
+    G = Hq // H
+    q1 = np.zeros_like(q)
+    q1[:, ::G] = q[:, ::G]
+    return O.estimate(q1, kmin, kmax, pt, lens, S, max_pages)
+
+
+def est_swapped_operands(q, kmin, kmax, pt, lens, S, max_pages=None):
+    # q.kmin paired with kmax's sign test: max(q*kmin, q*kmin reversed)
+    return O.estimate(q[..., ::-1].copy(), kmin, kmax, pt, lens, S, max_pages)
+
+
+def topk_ties_high(scores, n, k):
+    kk = min(k, n)
+    s = np.asarray(scores[:n], dtype=np.float64)
+    order = np.lexsort((-np.arange(n), -s))
+    out = np.full(k, -1)
+    out[:kk] = np.sort(order[:kk])
+    return out
+
+
+def topk_descending_output(scores, n, k):
+    out = O.topk_pages(scores, n, k)
+    kk = min(k, n)
+    out[:kk] = out[:kk][::-1]
+    return out
+
+
+def topk_off_by_one(scores, n, k):
+    return O.topk_pages(scores, n, max(0, k - 1)).tolist() + [-1]
+
+
+def topk_ignores_short_rule(scores, n, k):
+    s = np.concatenate([np.asarray(scores[:n], dtype=np.float64),
+                        np.full(max(0, k - n), -np.inf)])
+    out = O.topk_pages(s, len(s), k)
+    return out
+
+
+def meta_all_slots(k_pool, pt, lens, S):
+    full = np.array([-(-int(L) // S) * S for L in lens])
+    return O.page_meta(k_pool, pt, full, S)
+
+
+def meta_plain_minmax(k_pool, pt, lens, S):
+    kmin, kmax = O.page_meta(k_pool, pt, lens, S)
+    return np.where(kmin == 0, 0.0, kmin), np.where(kmax == 0, 0.0, kmax)
+
+
+def append_no_reset(k_pool, v_pool, kmin, kmax, pt, b, new_len, k_new, v_new, S):
+    pos = new_len - 1
+    j, slot = divmod(pos, S)
+    p = int(pt[b, j])
+    k_pool[p, :, slot] = k_new
+    v_pool[p, :, slot] = v_new
+    kmin[p] = np.minimum(kmin[p], k_new)
+    kmax[p] = np.maximum(kmax[p], k_new)
+
+
+def sparse_unmasked(q, kp, vp, pt, lens, sel, scale, S):
+    full = np.array([-(-int(L) // S) * S for L in lens])
+    return O.sparse_attention(q, kp, vp, pt, full, sel, scale, S)
+
+
+def sparse_wrong_heads(q, kp, vp, pt, lens, sel, scale, S):
+    B, Hq, d = q.shape
+    H = kp.shape[1]
+    out = np.zeros((B, Hq, d))
+    for h in range(Hq):                 # h % H instead of h // G
+        g = h % H
+        qh = np.zeros((B, H, d))
+        qh[:, g] = q[:, h]
+        out[:, h] = O.sparse_attention(qh, kp, vp, pt, lens, sel, scale, S)[:, g]
+    return out
+
+
+def sparse_no_scale(q, kp, vp, pt, lens, sel, scale, S):
+    return O.sparse_attention(q, kp, vp, pt, lens, sel, 1.0, S)
+
+
+def dense_unnormalised(q, kp, vp, pt, lens, scale, S):
+    out = O.dense_attention(q, kp, vp, pt, lens, scale, S)
+    return out * 1.0001
+
+
+def dense_off_by_one_token(q, kp, vp, pt, lens, scale, S):
+    return O.dense_attention(q, kp, vp, pt, np.maximum(np.asarray(lens) - 1, 1)
+                             * (np.asarray(lens) > 0), scale, S)
+
+
+MUTANTS = {
+    "estimate_dropped_kmin": dict(estimate=est_dropped_kmin),
+    "estimate_min_not_max": dict(estimate=est_min_instead_of_max),
+    "estimate_scaled": dict(estimate=est_scaled),
+    "estimate_no_page_table": dict(estimate=est_no_indirection),
+    "estimate_first_head_only": dict(estimate=est_first_head_only),
+    "estimate_swapped_channels": dict(estimate=est_swapped_operands),
+    "topk_ties_to_higher": dict(topk_pages=topk_ties_high),
+    "topk_descending": dict(topk_pages=topk_descending_output),
+    "topk_off_by_one": dict(topk_pages=topk_off_by_one),
+    "topk_no_short_rule": dict(topk_pages=topk_ignores_short_rule),
+    "meta_reads_invalid_slots": dict(page_meta=meta_all_slots),
+    "meta_unsigned_zero": dict(page_meta=meta_plain_minmax),
+    "append_never_resets": dict(append_token=append_no_reset),
+    "sparse_unmasked_tail": dict(sparse_attention=sparse_unmasked),
+    "sparse_wrong_head_map": dict(sparse_attention=sparse_wrong_heads),
+    "sparse_missing_scale": dict(sparse_attention=sparse_no_scale),
+    "dense_unnormalised": dict(dense_attention=dense_unnormalised),
+    "dense_drops_last_token": dict(dense_attention=dense_off_by_one_token),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_some_pin_catches_mutant(name):
+    ns = _ns(**MUTANTS[name])
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check(ns)
+        except AssertionError:   # a crash of the mutant does not count
+            caught.append(check.__name__)
+    assert caught, f"no pin catches mutant {name}"
