@@ -1,0 +1,186 @@
+/*
+ * quest.h -- C ABI of libquest.so: the decode-step hot path of Quest
+ * (query-aware KV-cache page sparsity) for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page title, section / equation):
+ *   [G] "Guide to Quest: Query-Aware KV Cache Sparsity for LLMs":
+ *       §1 Offline Min-Max Key Vector Bounding Boxes (the min/max equation),
+ *       §2 Fast Query-Aware Logit Upper-Bound Estimation (the bound),
+ *       §3 Top-K Page Selection and Sparse FlashAttention Dispatch,
+ *       "The Memory Bandwidth Bottleneck of Long-Context Decoding"
+ *       (the attention equation), Implementation Steps 1-3 (the interface:
+ *       page append, bound estimation, page selection, sparse forward).
+ *   [Q] "Quest: Query-Aware Sparsity for Efficient Long-Context LLM
+ *       Inference" (paper summary): Summary, Key points.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All array arguments are DEVICE pointers to row-major, contiguous memory,
+ *   16-byte aligned (the kernels read and write 16 bytes per lane).  The
+ *   caller allocates and owns every buffer; the library allocates nothing,
+ *   keeps no state between calls, and may be called from several host
+ *   threads on different streams.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Every call only enqueues work on it and returns; the status reports the
+ *   host-side checks and the launch, never the kernels' completion.
+ * - No call checks device-side VALUES (page ids, lengths): a page id outside
+ *   [0, num_pool_pages) or a length above max_pages_per_seq * page_size is
+ *   undefined behaviour.
+ * - Slots of a page past the sequence's last token, and pool pages no
+ *   request owns, may hold any bits (NaN included): they are never used as
+ *   values.
+ * - Shapes (d = head_dim = 128, S = page_size = 16, G = Hq / Hkv):
+ *     k_pool, v_pool  [num_pool_pages][Hkv][S][d]   (dtype)
+ *     kmin, kmax      [num_pool_pages][Hkv][d]      (dtype)
+ *     page_table      int32 [batch][max_pages_per_seq]; logical page j of
+ *                     request b lives in pool page page_table[b][j]
+ *     seq_lens        int32 [batch]; L_b tokens, n_b = ceil(L_b / S) pages;
+ *                     L_b = 0 is allowed (an empty request)
+ *     q               [batch][Hq][d]                (dtype)
+ *     scores          float32 [batch][Hkv][max_pages_per_seq]
+ *     sel_pages       int32 [batch][Hkv][k_pages]
+ *     out             float32 [batch][Hq][d]
+ *   Query head h reads kv-head h / G.
+ * - Errors: a non-OK status means nothing was enqueued (except
+ *   QUEST_ERR_HIP, which reports a failed launch); quest_last_error() then
+ *   returns a thread-local message naming the argument or the HIP error.
+ */
+#ifndef QUEST_H_
+#define QUEST_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QUEST_API __attribute__((visibility("default")))
+
+typedef enum quest_status {
+  QUEST_OK = 0,
+  QUEST_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, bad count */
+  QUEST_ERR_UNSUPPORTED = 2,      /* shape or dtype this build has no kernel for */
+  QUEST_ERR_WORKSPACE_TOO_SMALL = 3,
+  QUEST_ERR_HIP = 4               /* the HIP runtime reported an error */
+} quest_status;
+
+typedef enum quest_dtype {
+  QUEST_F16 = 0, /* IEEE binary16 */
+  QUEST_BF16 = 1 /* bfloat16 */
+} quest_dtype;
+
+/* Geometry of one paged KV cache (one layer).  Host memory. */
+typedef struct quest_paged_kv {
+  int32_t batch;             /* requests, >= 1 */
+  int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;      /* Hkv, >= 1 */
+  int32_t head_dim;          /* d: must be 128 */
+  int32_t page_size;         /* S: must be 16 */
+  int32_t num_pool_pages;    /* pages in k_pool / v_pool / kmin / kmax */
+  int32_t max_pages_per_seq; /* columns of page_table and scores */
+  int32_t dtype;             /* quest_dtype of q, K, V, kmin, kmax */
+} quest_paged_kv;
+
+/*
+ * Page metadata: per-page, per-channel min and max of the keys.
+ * [G] §1 (min/max equation): Kmin[p] = min_t K[p,t], Kmax[p] = max_t K[p,t]
+ * over the page's valid tokens, stored in K's dtype.  Min/max only select
+ * an input, so the result is exact; signed zeros order as -0 < +0.
+ *
+ * Two modes:
+ *  - Rebuild (k_new == NULL, v_new == NULL): for each request b fold the
+ *    tokens [f_b, L_b) already in k_pool into their pages' boxes, where
+ *    f_b = first_token[b] (first_token == NULL means f_b = 0 for all b).
+ *    A page whose slot 0 lies in [f_b, L_b) is rebuilt from its valid
+ *    tokens; a page entered in mid-page is widened.  first_token all zero
+ *    is a full rebuild.  k_pool and v_pool are not written.
+ *  - Append (k_new, v_new non-NULL, first_token must be NULL): each request
+ *    appends one token at position L_b - 1 (seq_lens already count it):
+ *    k_new/v_new [batch][Hkv][d] are written into slot (L_b-1) % S of
+ *    logical page (L_b-1) / S, then folded into that page's box ([G] §1:
+ *    the box forms as its page forms, here one generated token at a time; a
+ *    token in slot 0 starts a new box).  Requests with L_b = 0 are skipped.
+ * kmin/kmax of pages outside the folded range are left untouched.
+ */
+QUEST_API quest_status quest_update_page_meta(
+    const quest_paged_kv* kv, void* k_pool, void* v_pool, void* kmin,
+    void* kmax, const int32_t* page_table, const int32_t* seq_lens,
+    const int32_t* first_token, const void* k_new, const void* v_new,
+    void* stream);
+
+/*
+ * Query-aware page estimate.  [G] §2 (upper-bound inequality):
+ *   scores[b][g][j] = sum_{h in group g} sum_i max(q[b][h][i] * kmin[p][g][i],
+ *                                                 q[b][h][i] * kmax[p][g][i]),
+ *   p = page_table[b][j], for j < n_b; scores[b][g][j] = -inf for
+ *   n_b <= j < max_pages_per_seq.
+ * Unscaled (no 1/sqrt(d)); a GQA group's score is the sum of its G query
+ * heads' bounds.  Products are exact in float32 for fp16/bf16 inputs of
+ * normal range; the sum rounds in float32.
+ */
+QUEST_API quest_status quest_estimate(
+    const quest_paged_kv* kv, const void* q, const void* kmin,
+    const void* kmax, const int32_t* page_table, const int32_t* seq_lens,
+    float* scores, void* stream);
+
+/*
+ * Top-K page selection.  [G] §3: keep the k_pages pages with the highest
+ * scores; Implementation Step 2: a request with n_b <= k_pages keeps all of
+ * its pages.  For each (b, g) row the kept set is the first min(k_pages, n_b)
+ * logical pages in the order (score descending, page index ascending), with
+ * -0 == +0; sel_pages[b][g] lists it in ASCENDING page order, then -1 up to
+ * k_pages.  Scores must not be NaN.  1 <= k_pages; max_pages_per_seq <=
+ * 32768.
+ */
+QUEST_API quest_status quest_topk_pages(
+    const quest_paged_kv* kv, const float* scores, const int32_t* seq_lens,
+    int32_t k_pages, int32_t* sel_pages, void* stream);
+
+/*
+ * Sparse exact decode attention over the selected pages.  [Q] Summary and
+ * [G] §3: attention runs only over the kept pages' tokens.  For query head
+ * h (kv-head g = h / G) of request b, over the tokens t < v_j of every page
+ * j >= 0 listed in sel_pages[b][g] (v_j = min(S, L_b - j*S)):
+ *   out[b][h] = sum_t softmax(sm_scale * q[b][h].K_t)_t * V_t     (float32)
+ * Entries equal to -1 are skipped; a row with no page yields zeros.  The
+ * listed pages must be distinct and < n_b.  Accumulation is float32
+ * (online softmax, split over pages, merged in float32).
+ * `workspace` (device, >= quest_workspace_size(kv, k_pages) bytes) holds
+ * per-split partial results; its contents on entry do not matter.
+ */
+QUEST_API quest_status quest_sparse_decode_attn(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const int32_t* sel_pages, int32_t k_pages, float sm_scale, float* out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dense decode attention over all L_b tokens (the in-library baseline).
+ * "The Memory Bandwidth Bottleneck of Long-Context Decoding" in [G]:
+ *   out[b][h] = softmax(sm_scale * q K^T) V over every token of request b.
+ * Same kernels, arithmetic and workspace rules as the sparse call; the
+ * workspace must hold quest_workspace_size(kv, max_pages_per_seq) bytes.
+ */
+QUEST_API quest_status quest_decode_attn(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/* Host only: workspace bytes the attention calls need for k_pages selected
+ * pages per row (pass max_pages_per_seq for quest_decode_attn). */
+QUEST_API quest_status quest_workspace_size(const quest_paged_kv* kv,
+                                            int32_t k_pages, size_t* bytes);
+
+/* Host only: static description of a status code. */
+QUEST_API const char* quest_status_string(quest_status status);
+
+/* Host only: detail of the last non-OK status on this thread ("" if none). */
+QUEST_API const char* quest_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUEST_H_ */

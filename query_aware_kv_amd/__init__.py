@@ -1,0 +1,89 @@
+"""Quest decode-step hot path for AMD Instinct MI355X (gfx950).
+
+The computation lives in libquest.so (hand-written HIP kernels behind a C
+ABI, declared in include/quest.h).  This package is its Python binding: the
+five entry points under the C names, plus `SparseDecodeStep`, which strings
+estimate -> Top-K -> sparse attention together on preallocated buffers.
+PyTorch only provides device memory and the stream.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._abi import (  # noqa: F401
+    LIB, LIB_PATH, PagedKV, QuestError, QUEST_BF16, QUEST_F16, QUEST_OK,
+    QUEST_ERR_HIP, QUEST_ERR_INVALID_ARGUMENT, QUEST_ERR_UNSUPPORTED,
+    QUEST_ERR_WORKSPACE_TOO_SMALL, paged_kv, paged_kv_like,
+    quest_decode_attn, quest_estimate, quest_sparse_decode_attn,
+    quest_topk_pages, quest_update_page_meta, quest_workspace_size,
+)
+
+HEAD_DIM = 128
+PAGE_SIZE = 16
+
+
+def default_sm_scale(head_dim: int = HEAD_DIM) -> float:
+    return 1.0 / math.sqrt(head_dim)
+
+
+def alloc_workspace(kv: PagedKV, k_pages: int, device="cuda") -> torch.Tensor:
+    n = quest_workspace_size(kv, k_pages)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def alloc_meta(kv: PagedKV, device="cuda"):
+    shape = (kv.num_pool_pages, kv.num_kv_heads, kv.head_dim)
+    return (torch.empty(shape, dtype=kv.torch_dtype, device=device),
+            torch.empty(shape, dtype=kv.torch_dtype, device=device))
+
+
+class SparseDecodeStep:
+    """Buffers and call sequence of one sparse decode step for a fixed
+    geometry: quest_estimate -> quest_topk_pages -> quest_sparse_decode_attn.
+    """
+
+    def __init__(self, kv: PagedKV, k_pages: int, sm_scale: float | None = None,
+                 device="cuda"):
+        self.kv = kv
+        self.k_pages = int(k_pages)
+        self.sm_scale = default_sm_scale(kv.head_dim) if sm_scale is None else sm_scale
+        B, Hq, Hkv = kv.batch, kv.num_q_heads, kv.num_kv_heads
+        self.scores = torch.empty(B, Hkv, kv.max_pages_per_seq,
+                                  dtype=torch.float32, device=device)
+        self.sel = torch.empty(B, Hkv, self.k_pages, dtype=torch.int32,
+                               device=device)
+        self.out = torch.empty(B, Hq, kv.head_dim, dtype=torch.float32,
+                               device=device)
+        self.workspace = alloc_workspace(kv, self.k_pages, device)
+
+    def __call__(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_lens,
+                 stream=None) -> torch.Tensor:
+        quest_estimate(self.kv, q, kmin, kmax, page_table, seq_lens,
+                       self.scores, stream)
+        quest_topk_pages(self.kv, self.scores, seq_lens, self.k_pages,
+                         self.sel, stream)
+        quest_sparse_decode_attn(self.kv, q, k_pool, v_pool, page_table,
+                                 seq_lens, self.sel, self.k_pages,
+                                 self.sm_scale, self.out, self.workspace,
+                                 stream)
+        return self.out
+
+
+class DenseDecode:
+    """Buffers of the dense baseline (quest_decode_attn) for a geometry."""
+
+    def __init__(self, kv: PagedKV, sm_scale: float | None = None,
+                 device="cuda"):
+        self.kv = kv
+        self.sm_scale = default_sm_scale(kv.head_dim) if sm_scale is None else sm_scale
+        self.out = torch.empty(kv.batch, kv.num_q_heads, kv.head_dim,
+                               dtype=torch.float32, device=device)
+        self.workspace = alloc_workspace(kv, kv.max_pages_per_seq, device)
+
+    def __call__(self, q, k_pool, v_pool, page_table, seq_lens,
+                 stream=None) -> torch.Tensor:
+        quest_decode_attn(self.kv, q, k_pool, v_pool, page_table, seq_lens,
+                          self.sm_scale, self.out, self.workspace, stream)
+        return self.out

@@ -1,0 +1,269 @@
+// C ABI of libquest.so: argument validation, dispatch and error reporting.
+// Every entry point checks its arguments on the host, then enqueues kernels
+// on the caller's stream; nothing is allocated and no state is kept.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+#include "launch.h"
+#include "quest.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+quest_status fail(quest_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+quest_status ok() {
+  g_last_error[0] = '\0';
+  return QUEST_OK;
+}
+
+quest_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(QUEST_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+#define REQUIRE_PTR(p, align_ok)                                               \
+  do {                                                                         \
+    if ((p) == nullptr)                                                        \
+      return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: `%s` is NULL", fn, #p);     \
+    if (!(align_ok))                                                           \
+      return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: `%s` is misaligned", fn, #p); \
+  } while (0)
+
+quest_status check_kv(const quest_paged_kv* kv, const char* fn) {
+  if (kv == nullptr)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: `kv` is NULL", fn);
+  if (kv->batch < 1 || kv->num_kv_heads < 1 || kv->num_q_heads < 1 ||
+      kv->num_pool_pages < 1 || kv->max_pages_per_seq < 1)
+    return fail(QUEST_ERR_INVALID_ARGUMENT,
+                "%s: batch, heads, num_pool_pages and max_pages_per_seq must "
+                "be >= 1", fn);
+  if (kv->num_q_heads % kv->num_kv_heads != 0)
+    return fail(QUEST_ERR_INVALID_ARGUMENT,
+                "%s: num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                fn, kv->num_q_heads, kv->num_kv_heads);
+  if (kv->head_dim != quest::kHeadDim)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: head_dim %d (only 128)", fn,
+                kv->head_dim);
+  if (kv->page_size != quest::kPageSize)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: page_size %d (only 16)", fn,
+                kv->page_size);
+  if (kv->dtype != QUEST_F16 && kv->dtype != QUEST_BF16)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: dtype %d", fn, kv->dtype);
+  if ((int64_t)kv->batch * kv->num_q_heads > (int64_t)1 << 30 ||
+      (int64_t)kv->batch * kv->num_kv_heads > 65535)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: batch x heads too large", fn);
+  return QUEST_OK;
+}
+
+quest_status check_group(const quest_paged_kv* kv, const char* fn) {
+  const int G = kv->num_q_heads / kv->num_kv_heads;
+  if (!quest::estimate_supported(G) || !quest::attention_supported(G))
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: group size %d (1, 2, 4 or 8)", fn, G);
+  return QUEST_OK;
+}
+
+quest_status check_attention_common(const quest_paged_kv* kv, const void* q,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* page_table,
+                                    const int32_t* seq_lens, float sm_scale,
+                                    const float* out, const char* fn) {
+  quest_status s = check_kv(kv, fn);
+  if (s != QUEST_OK) return s;
+  if ((s = check_group(kv, fn)) != QUEST_OK) return s;
+  REQUIRE_PTR(q, aligned16(q));
+  REQUIRE_PTR(k_pool, aligned16(k_pool));
+  REQUIRE_PTR(v_pool, aligned16(v_pool));
+  REQUIRE_PTR(page_table, aligned4(page_table));
+  REQUIRE_PTR(seq_lens, aligned4(seq_lens));
+  REQUIRE_PTR(out, aligned4(out));
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: sm_scale is not finite", fn);
+  return QUEST_OK;
+}
+
+quest_status run_attention(const quest_paged_kv* kv, const void* q,
+                           const void* k_pool, const void* v_pool,
+                           const int32_t* page_table, const int32_t* seq_lens,
+                           const int32_t* sel, int list_len, float sm_scale,
+                           float* out, void* workspace, size_t workspace_bytes,
+                           void* stream, const char* fn) {
+  const size_t need = quest::attention_workspace_bytes(*kv, list_len);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(QUEST_ERR_WORKSPACE_TOO_SMALL,
+                  "%s: workspace needs %zu bytes, got %zu", fn, need,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (!aligned16(workspace))
+      return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: `workspace` is misaligned", fn);
+  }
+  return hip_status(
+      quest::launch_attention(*kv, q, k_pool, v_pool, page_table, seq_lens, sel,
+                              list_len, sm_scale, out, workspace,
+                              static_cast<hipStream_t>(stream)),
+      fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+QUEST_API quest_status quest_update_page_meta(
+    const quest_paged_kv* kv, void* k_pool, void* v_pool, void* kmin,
+    void* kmax, const int32_t* page_table, const int32_t* seq_lens,
+    const int32_t* first_token, const void* k_new, const void* v_new,
+    void* stream) {
+  const char* fn = "quest_update_page_meta";
+  quest_status s = check_kv(kv, fn);
+  if (s != QUEST_OK) return s;
+  REQUIRE_PTR(k_pool, aligned16(k_pool));
+  REQUIRE_PTR(kmin, aligned16(kmin));
+  REQUIRE_PTR(kmax, aligned16(kmax));
+  REQUIRE_PTR(page_table, aligned4(page_table));
+  REQUIRE_PTR(seq_lens, aligned4(seq_lens));
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(QUEST_ERR_INVALID_ARGUMENT,
+                "%s: k_new and v_new must both be set (append) or both NULL "
+                "(rebuild)", fn);
+  if (k_new == nullptr) {
+    if (first_token != nullptr && !aligned4(first_token))
+      return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: `first_token` is misaligned", fn);
+    return hip_status(quest::launch_meta_rebuild(
+                          *kv, k_pool, kmin, kmax, page_table, seq_lens,
+                          first_token, static_cast<hipStream_t>(stream)),
+                      fn);
+  }
+  if (first_token != nullptr)
+    return fail(QUEST_ERR_INVALID_ARGUMENT,
+                "%s: first_token must be NULL in append mode", fn);
+  REQUIRE_PTR(v_pool, aligned16(v_pool));
+  REQUIRE_PTR(k_new, aligned16(k_new));
+  REQUIRE_PTR(v_new, aligned16(v_new));
+  return hip_status(quest::launch_meta_append(*kv, k_pool, v_pool, kmin, kmax,
+                                              page_table, seq_lens, k_new,
+                                              v_new,
+                                              static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+QUEST_API quest_status quest_estimate(const quest_paged_kv* kv, const void* q,
+                                      const void* kmin, const void* kmax,
+                                      const int32_t* page_table,
+                                      const int32_t* seq_lens, float* scores,
+                                      void* stream) {
+  const char* fn = "quest_estimate";
+  quest_status s = check_kv(kv, fn);
+  if (s != QUEST_OK) return s;
+  if ((s = check_group(kv, fn)) != QUEST_OK) return s;
+  REQUIRE_PTR(q, aligned16(q));
+  REQUIRE_PTR(kmin, aligned16(kmin));
+  REQUIRE_PTR(kmax, aligned16(kmax));
+  REQUIRE_PTR(page_table, aligned4(page_table));
+  REQUIRE_PTR(seq_lens, aligned4(seq_lens));
+  REQUIRE_PTR(scores, aligned4(scores));
+  return hip_status(quest::launch_estimate(*kv, q, kmin, kmax, page_table,
+                                           seq_lens, scores,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+QUEST_API quest_status quest_topk_pages(const quest_paged_kv* kv,
+                                        const float* scores,
+                                        const int32_t* seq_lens,
+                                        int32_t k_pages, int32_t* sel_pages,
+                                        void* stream) {
+  const char* fn = "quest_topk_pages";
+  quest_status s = check_kv(kv, fn);
+  if (s != QUEST_OK) return s;
+  REQUIRE_PTR(scores, aligned4(scores));
+  REQUIRE_PTR(seq_lens, aligned4(seq_lens));
+  REQUIRE_PTR(sel_pages, aligned4(sel_pages));
+  if (k_pages < 1)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  if (kv->max_pages_per_seq > quest::kTopkMaxPages)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: max_pages_per_seq %d > %d", fn,
+                kv->max_pages_per_seq, quest::kTopkMaxPages);
+  return hip_status(quest::launch_topk(*kv, scores, seq_lens, k_pages,
+                                       sel_pages,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+QUEST_API quest_status quest_sparse_decode_attn(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const int32_t* sel_pages, int32_t k_pages, float sm_scale, float* out,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "quest_sparse_decode_attn";
+  quest_status s = check_attention_common(kv, q, k_pool, v_pool, page_table,
+                                          seq_lens, sm_scale, out, fn);
+  if (s != QUEST_OK) return s;
+  REQUIRE_PTR(sel_pages, aligned4(sel_pages));
+  if (k_pages < 1)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  return run_attention(kv, q, k_pool, v_pool, page_table, seq_lens, sel_pages,
+                       k_pages, sm_scale, out, workspace, workspace_bytes,
+                       stream, fn);
+}
+
+QUEST_API quest_status quest_decode_attn(const quest_paged_kv* kv,
+                                         const void* q, const void* k_pool,
+                                         const void* v_pool,
+                                         const int32_t* page_table,
+                                         const int32_t* seq_lens,
+                                         float sm_scale, float* out,
+                                         void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  const char* fn = "quest_decode_attn";
+  quest_status s = check_attention_common(kv, q, k_pool, v_pool, page_table,
+                                          seq_lens, sm_scale, out, fn);
+  if (s != QUEST_OK) return s;
+  return run_attention(kv, q, k_pool, v_pool, page_table, seq_lens, nullptr,
+                       kv->max_pages_per_seq, sm_scale, out, workspace,
+                       workspace_bytes, stream, fn);
+}
+
+QUEST_API quest_status quest_workspace_size(const quest_paged_kv* kv,
+                                            int32_t k_pages, size_t* bytes) {
+  const char* fn = "quest_workspace_size";
+  quest_status s = check_kv(kv, fn);
+  if (s != QUEST_OK) return s;
+  if ((s = check_group(kv, fn)) != QUEST_OK) return s;
+  if (bytes == nullptr)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: `bytes` is NULL", fn);
+  if (k_pages < 1)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  *bytes = quest::attention_workspace_bytes(*kv, k_pages);
+  return ok();
+}
+
+QUEST_API const char* quest_status_string(quest_status status) {
+  switch (status) {
+    case QUEST_OK: return "ok";
+    case QUEST_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case QUEST_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case QUEST_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case QUEST_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+QUEST_API const char* quest_last_error(void) { return g_last_error; }
+
+}  // extern "C"

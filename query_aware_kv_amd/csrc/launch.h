@@ -1,0 +1,46 @@
+// Host-side launchers of the Quest kernels (one per .hip file).  Each
+// enqueues on `stream` and returns the launch status; arguments have been
+// validated by the C ABI layer (api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "quest.h"
+
+namespace quest {
+
+hipError_t launch_meta_rebuild(const quest_paged_kv& kv, const void* k_pool,
+                               void* kmin, void* kmax,
+                               const int32_t* page_table,
+                               const int32_t* seq_lens,
+                               const int32_t* first_token, hipStream_t stream);
+
+hipError_t launch_meta_append(const quest_paged_kv& kv, void* k_pool,
+                              void* v_pool, void* kmin, void* kmax,
+                              const int32_t* page_table,
+                              const int32_t* seq_lens, const void* k_new,
+                              const void* v_new, hipStream_t stream);
+
+// True when an estimate kernel exists for this group size.
+bool estimate_supported(int group);
+hipError_t launch_estimate(const quest_paged_kv& kv, const void* q,
+                           const void* kmin, const void* kmax,
+                           const int32_t* page_table, const int32_t* seq_lens,
+                           float* scores, hipStream_t stream);
+
+// Largest max_pages_per_seq the Top-K kernel handles.
+constexpr int kTopkMaxPages = 32768;
+hipError_t launch_topk(const quest_paged_kv& kv, const float* scores,
+                       const int32_t* seq_lens, int k_pages, int32_t* sel,
+                       hipStream_t stream);
+
+// Attention (sparse when sel != nullptr, else dense over all pages).
+bool attention_supported(int group);
+size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len);
+hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
+                            const void* k_pool, const void* v_pool,
+                            const int32_t* page_table, const int32_t* seq_lens,
+                            const int32_t* sel, int list_len, float sm_scale,
+                            float* out, void* workspace, hipStream_t stream);
+
+}  // namespace quest

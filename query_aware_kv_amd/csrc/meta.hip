@@ -1,0 +1,173 @@
+// Page metadata kernels: per-page, per-channel min/max of the keys.
+//
+// "Guide to Quest: Query-Aware KV Cache Sparsity for LLMs", §1 (min/max
+// equation): a page's box is the channelwise min and max of its keys.  Both
+// are exact selections, done here on a total order of the 16-bit encodings
+// (ord16), so fp16 and bf16 share one kernel and the result is bit-exact
+// with -0 < +0.
+//
+// Layout: K tile of (page p, kv-head g) = 16 rows x 128 channels x 2 B =
+// 4 KiB contiguous at ((p * Hkv + g) * 16) * 128 elements.  A wave covers
+// one tile: lane = 16 * r + c reads 16 B (8 channels, chunk c) of rows
+// r, r+4, r+8, r+12, so each load instruction reads 1 KiB contiguous.
+#include <climits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace quest {
+namespace {
+
+__device__ __forceinline__ void fold8(const uint4& x, int32_t (&mn)[8],
+                                      int32_t (&mx)[8]) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t lo = ord16(w[i] & 0xffffu), hi = ord16(w[i] >> 16);
+    mn[2 * i] = min(mn[2 * i], lo);
+    mx[2 * i] = max(mx[2 * i], lo);
+    mn[2 * i + 1] = min(mn[2 * i + 1], hi);
+    mx[2 * i + 1] = max(mx[2 * i + 1], hi);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const int32_t (&k)[8]) {
+  uint4 r;
+  r.x = unord16(k[0]) | (unord16(k[1]) << 16);
+  r.y = unord16(k[2]) | (unord16(k[3]) << 16);
+  r.z = unord16(k[4]) | (unord16(k[5]) << 16);
+  r.w = unord16(k[6]) | (unord16(k[7]) << 16);
+  return r;
+}
+
+// One wave per (request b, logical page j, kv-head g).
+__global__ void __launch_bounds__(256)
+meta_rebuild_kernel(const uint16_t* __restrict__ k_pool,
+                    uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
+                    const int32_t* __restrict__ page_table,
+                    const int32_t* __restrict__ seq_lens,
+                    const int32_t* __restrict__ first_token, int Hkv,
+                    int max_pages, int num_pool_pages) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= max_pages * Hkv) return;
+  const int j = unit / Hkv, g = unit - (unit / Hkv) * Hkv;
+  const int L = seq_lens[b];
+  const int v = min(kPageSize, L - j * kPageSize);  // valid tokens in page j
+  if (v <= 0) return;
+  const int f = first_token ? first_token[b] : 0;
+  const int t0 = max(0, f - j * kPageSize);          // first token to fold
+  if (t0 >= v) return;
+  const int64_t p = page_table[(int64_t)b * max_pages + j];
+  if (p < 0 || p >= num_pool_pages) return;  // not a pool page: nothing to read
+  const int64_t tile = (p * Hkv + g) * (kPageSize * kHeadDim);
+  const uint4* src = reinterpret_cast<const uint4*>(k_pool + tile);
+  const int c = lane & 15, r = lane >> 4;
+
+  int32_t mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { mn[e] = INT_MAX; mx[e] = INT_MIN; }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = r + 4 * i;
+    if (t >= t0 && t < v) fold8(src[t * 16 + c], mn, mx);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mn[e] = min(mn[e], __shfl_xor(mn[e], 16, kWave));
+    mx[e] = max(mx[e], __shfl_xor(mx[e], 16, kWave));
+    mn[e] = min(mn[e], __shfl_xor(mn[e], 32, kWave));
+    mx[e] = max(mx[e], __shfl_xor(mx[e], 32, kWave));
+  }
+  const int64_t m = (p * Hkv + g) * kHeadDim + c * 8;
+  uint4* dmin = reinterpret_cast<uint4*>(kmin + m);
+  uint4* dmax = reinterpret_cast<uint4*>(kmax + m);
+  if (t0 > 0) {  // entered mid-page: widen the existing box
+    fold8(*dmin, mn, mx);
+    fold8(*dmax, mn, mx);
+  }
+  if (r == 0) *dmin = pack8(mn);
+  if (r == 1) *dmax = pack8(mx);
+}
+
+// One wave per (request b, kv-head g): write the appended token, fold it.
+__global__ void __launch_bounds__(256)
+meta_append_kernel(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+                   uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
+                   const int32_t* __restrict__ page_table,
+                   const int32_t* __restrict__ seq_lens,
+                   const uint16_t* __restrict__ k_new,
+                   const uint16_t* __restrict__ v_new, int Hkv, int max_pages,
+                   int num_pool_pages) {
+  const int b = blockIdx.y;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= Hkv || lane >= 32) return;
+  const int L = seq_lens[b];
+  if (L <= 0) return;
+  const int pos = L - 1;
+  const int j = pos / kPageSize, slot = pos - j * kPageSize;
+  if (j >= max_pages) return;
+  const int64_t p = page_table[(int64_t)b * max_pages + j];
+  if (p < 0 || p >= num_pool_pages) return;
+  const int c = lane & 15;
+  const int64_t row = ((p * Hkv + g) * kPageSize + slot) * kHeadDim + c * 8;
+  const int64_t src = ((int64_t)b * Hkv + g) * kHeadDim + c * 8;
+  if (lane >= 16) {
+    *reinterpret_cast<uint4*>(v_pool + row) =
+        *reinterpret_cast<const uint4*>(v_new + src);
+    return;
+  }
+  const uint4 x = *reinterpret_cast<const uint4*>(k_new + src);
+  *reinterpret_cast<uint4*>(k_pool + row) = x;
+  const int64_t m = (p * Hkv + g) * kHeadDim + c * 8;
+  uint4* dmin = reinterpret_cast<uint4*>(kmin + m);
+  uint4* dmax = reinterpret_cast<uint4*>(kmax + m);
+  if (slot == 0) {
+    *dmin = x;
+    *dmax = x;
+    return;
+  }
+  int32_t mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { mn[e] = INT_MAX; mx[e] = INT_MIN; }
+  fold8(x, mn, mx);
+  fold8(*dmin, mn, mx);
+  fold8(*dmax, mn, mx);
+  *dmin = pack8(mn);
+  *dmax = pack8(mx);
+}
+
+}  // namespace
+
+hipError_t launch_meta_rebuild(const quest_paged_kv& kv, const void* k_pool,
+                               void* kmin, void* kmax,
+                               const int32_t* page_table,
+                               const int32_t* seq_lens,
+                               const int32_t* first_token, hipStream_t stream) {
+  const int64_t units = (int64_t)kv.max_pages_per_seq * kv.num_kv_heads;
+  dim3 grid((unsigned)((units + 3) / 4), (unsigned)kv.batch);
+  meta_rebuild_kernel<<<grid, 256, 0, stream>>>(
+      static_cast<const uint16_t*>(k_pool), static_cast<uint16_t*>(kmin),
+      static_cast<uint16_t*>(kmax), page_table, seq_lens, first_token,
+      kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages);
+  return hipGetLastError();
+}
+
+hipError_t launch_meta_append(const quest_paged_kv& kv, void* k_pool,
+                              void* v_pool, void* kmin, void* kmax,
+                              const int32_t* page_table,
+                              const int32_t* seq_lens, const void* k_new,
+                              const void* v_new, hipStream_t stream) {
+  dim3 grid((unsigned)((kv.num_kv_heads + 3) / 4), (unsigned)kv.batch);
+  meta_append_kernel<<<grid, 256, 0, stream>>>(
+      static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
+      static_cast<uint16_t*>(kmin), static_cast<uint16_t*>(kmax), page_table,
+      seq_lens, static_cast<const uint16_t*>(k_new),
+      static_cast<const uint16_t*>(v_new), kv.num_kv_heads,
+      kv.max_pages_per_seq, kv.num_pool_pages);
+  return hipGetLastError();
+}
+
+}  // namespace quest

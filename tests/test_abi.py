@@ -1,0 +1,168 @@
+"""The C ABI on the host: libquest.so loads, exports every symbol
+include/quest.h declares, and rejects bad arguments with the documented
+status before any HIP call (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import query_aware_kv_amd as qa
+from query_aware_kv_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "quest.h")
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced here
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"QUEST_API\s+[\w\s\*]+?\b(quest_\w+)\s*\(", text)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_symbols()
+    assert set(names) >= {"quest_update_page_meta", "quest_estimate",
+                          "quest_topk_pages", "quest_sparse_decode_attn",
+                          "quest_decode_attn", "quest_workspace_size",
+                          "quest_status_string", "quest_last_error"}
+    lib = ctypes.CDLL(_abi.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def kv(**kw):
+    base = dict(batch=1, num_q_heads=32, num_kv_heads=32, head_dim=128,
+                page_size=16, num_pool_pages=2048, max_pages_per_seq=2048,
+                dtype=_abi.QUEST_F16)
+    base.update(kw)
+    return _abi.PagedKV(**base)
+
+
+def ws_size(k, pages=128):
+    n = ctypes.c_size_t(0)
+    st = qa.LIB.quest_workspace_size(ctypes.byref(k), pages, ctypes.byref(n))
+    return st, n.value
+
+
+def test_status_strings():
+    assert qa.LIB.quest_status_string(0) == b"ok"
+    assert b"workspace" in qa.LIB.quest_status_string(3)
+    assert qa.LIB.quest_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, _abi.QUEST_ERR_UNSUPPORTED),
+    ("page_size", 32, _abi.QUEST_ERR_UNSUPPORTED),
+    ("dtype", 7, _abi.QUEST_ERR_UNSUPPORTED),
+    ("num_kv_heads", 5, _abi.QUEST_ERR_INVALID_ARGUMENT),   # 32 % 5 != 0
+    ("num_q_heads", 96, _abi.QUEST_ERR_UNSUPPORTED),        # G = 3
+    ("batch", 0, _abi.QUEST_ERR_INVALID_ARGUMENT),
+    ("max_pages_per_seq", 0, _abi.QUEST_ERR_INVALID_ARGUMENT),
+])
+def test_geometry_validation(field, value, status):
+    st, _ = ws_size(kv(**{field: value}))
+    assert st == status
+    assert qa.LIB.quest_last_error().decode()
+
+
+def test_null_kv_and_null_out_param():
+    n = ctypes.c_size_t(0)
+    assert qa.LIB.quest_workspace_size(None, 8, ctypes.byref(n)) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+    k = kv()
+    assert qa.LIB.quest_workspace_size(ctypes.byref(k), 8, None) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert qa.LIB.quest_workspace_size(ctypes.byref(k), 0, ctypes.byref(n)) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_size_grows_with_pages_and_zero_when_unsplit():
+    st, small = ws_size(kv(), 128)
+    assert st == 0 and small > 0
+    st, big = ws_size(kv(), 2048)
+    assert st == 0 and big > small
+    # 4 pages fit one workgroup: no split, no workspace
+    st, none = ws_size(kv(num_q_heads=1, num_kv_heads=1), 4)
+    assert st == 0 and none == 0
+
+
+def test_estimate_rejects_null_and_misaligned():
+    k = kv()
+    P = ctypes.c_void_p
+    args = [P(FAKE)] * 6
+    for i, name in enumerate(["q", "kmin", "kmax", "page_table", "seq_lens",
+                              "scores"]):
+        bad = list(args)
+        bad[i] = None
+        st = qa.LIB.quest_estimate(ctypes.byref(k), *bad, None)
+        assert st == _abi.QUEST_ERR_INVALID_ARGUMENT
+        assert name in qa.LIB.quest_last_error().decode()
+    bad = list(args)
+    bad[0] = P(FAKE + 8)                     # q must be 16-byte aligned
+    assert qa.LIB.quest_estimate(ctypes.byref(k), *bad, None) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert "misaligned" in qa.LIB.quest_last_error().decode()
+
+
+def test_topk_validation():
+    k = kv()
+    P = ctypes.c_void_p
+    assert qa.LIB.quest_topk_pages(ctypes.byref(k), P(FAKE), P(FAKE), 0,
+                                   P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+    big = kv(max_pages_per_seq=40000)
+    assert qa.LIB.quest_topk_pages(ctypes.byref(big), P(FAKE), P(FAKE), 8,
+                                   P(FAKE), None) == _abi.QUEST_ERR_UNSUPPORTED
+
+
+def test_attention_workspace_and_scale_checks():
+    k = kv()
+    P = ctypes.c_void_p
+    st, need = ws_size(k, 128)
+    common = [P(FAKE)] * 6                 # q, k_pool, v_pool, pt, lens, sel
+    st = qa.LIB.quest_sparse_decode_attn(ctypes.byref(k), *common, 128, 0.088,
+                                         P(FAKE), P(FAKE), need - 1, None)
+    assert st == _abi.QUEST_ERR_WORKSPACE_TOO_SMALL
+    st = qa.LIB.quest_sparse_decode_attn(ctypes.byref(k), *common, 128, 0.088,
+                                         P(FAKE), None, need, None)
+    assert st == _abi.QUEST_ERR_WORKSPACE_TOO_SMALL
+    st = qa.LIB.quest_sparse_decode_attn(ctypes.byref(k), *common, 128,
+                                         float("nan"), P(FAKE), P(FAKE), need,
+                                         None)
+    assert st == _abi.QUEST_ERR_INVALID_ARGUMENT
+    st = qa.LIB.quest_sparse_decode_attn(ctypes.byref(k), *common, 0, 0.088,
+                                         P(FAKE), P(FAKE), need, None)
+    assert st == _abi.QUEST_ERR_INVALID_ARGUMENT
+    st, dneed = ws_size(k, k.max_pages_per_seq)
+    st = qa.LIB.quest_decode_attn(ctypes.byref(k), *common[:5], 0.088,
+                                  P(FAKE), P(FAKE), dneed - 16, None)
+    assert st == _abi.QUEST_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_meta_mode_validation():
+    k = kv()
+    P = ctypes.c_void_p
+    f = qa.LIB.quest_update_page_meta
+    # k_new without v_new
+    assert f(ctypes.byref(k), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+             P(FAKE), None, P(FAKE), None, None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+    # append mode with first_token
+    assert f(ctypes.byref(k), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+             P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+    # append mode needs v_pool
+    assert f(ctypes.byref(k), P(FAKE), None, P(FAKE), P(FAKE), P(FAKE),
+             P(FAKE), None, P(FAKE), P(FAKE), None) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+    # rebuild mode with a null kmin
+    assert f(ctypes.byref(k), P(FAKE), None, None, P(FAKE), P(FAKE), P(FAKE),
+             None, None, None, None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    k = qa.paged_kv(1, 1, 1, 4, 4, torch.float16)
+    t = torch.zeros(1, 1, 128, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        qa.quest_estimate(k, t, t, t, t, t, t)
