@@ -23,9 +23,10 @@
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   Every call only enqueues work on it and returns; the status reports the
  *   host-side checks and the launch, never the kernels' completion.
- * - No call checks device-side VALUES (page ids, lengths): a page id outside
- *   [0, num_pool_pages) or a length above max_pages_per_seq * page_size is
- *   undefined behaviour.
+ * - Device-side VALUES are not validated, but they cannot cause an
+ *   out-of-bounds read: a page id outside [0, num_pool_pages) is treated as
+ *   an absent page (never read; its score is -inf), and a length above
+ *   max_pages_per_seq * page_size is clamped to it.
  * - Slots of a page past the sequence's last token, and pool pages no
  *   request owns, may hold any bits (NaN included): they are never used as
  *   values.
@@ -167,6 +168,31 @@ QUEST_API quest_status quest_decode_attn(
     const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
     float sm_scale, float* out, void* workspace, size_t workspace_bytes,
     void* stream);
+
+/*
+ * One whole sparse decode step -- quest_estimate, quest_topk_pages and
+ * quest_sparse_decode_attn -- in a single persistent launch, with the same
+ * three outputs (scores, sel_pages, out) and the same arithmetic and tie
+ * rules.  Each (request, kv-head) row's Top-K runs as soon as that row's
+ * estimate is complete, overlapping the estimate and attention of other rows.
+ * Requires max_pages_per_seq <= 8192 (QUEST_ERR_UNSUPPORTED otherwise).
+ *
+ * `workspace` (device, >= quest_step_workspace_size(kv, k_pages) bytes) holds
+ * work-queue counters, per-row flags and split partials.  Its bytes must be
+ * ZERO before its first use (e.g. allocated zeroed); every call leaves the
+ * counters at zero again.  A workspace serves one stream at a time: calls
+ * that may overlap need their own workspaces.
+ */
+QUEST_API quest_status quest_sparse_decode_step(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const void* kmin, const void* kmax,
+    const int32_t* page_table, const int32_t* seq_lens, int32_t k_pages,
+    float sm_scale, float* scores, int32_t* sel_pages, float* out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host only: workspace bytes quest_sparse_decode_step needs. */
+QUEST_API quest_status quest_step_workspace_size(const quest_paged_kv* kv,
+                                                 int32_t k_pages, size_t* bytes);
 
 /* Host only: workspace bytes the attention calls need for k_pages selected
  * pages per row (pass max_pages_per_seq for quest_decode_attn). */

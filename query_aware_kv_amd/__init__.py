@@ -17,7 +17,8 @@ from ._abi import (  # noqa: F401
     QUEST_ERR_HIP, QUEST_ERR_INVALID_ARGUMENT, QUEST_ERR_UNSUPPORTED,
     QUEST_ERR_WORKSPACE_TOO_SMALL, paged_kv, paged_kv_like,
     quest_decode_attn, quest_estimate, quest_sparse_decode_attn,
-    quest_topk_pages, quest_update_page_meta, quest_workspace_size,
+    quest_sparse_decode_step, quest_step_workspace_size, quest_topk_pages,
+    quest_update_page_meta, quest_workspace_size,
 )
 
 HEAD_DIM = 128
@@ -69,6 +70,31 @@ class SparseDecodeStep:
                                  self.sm_scale, self.out, self.workspace,
                                  stream)
         return self.out
+
+
+class FusedDecodeStep(SparseDecodeStep):
+    """The same step as `SparseDecodeStep` in one launch
+    (quest_sparse_decode_step).  Owns a zero-initialised workspace, which
+    every call leaves zeroed again; use one instance per stream."""
+
+    def __init__(self, kv: PagedKV, k_pages: int, sm_scale: float | None = None,
+                 device="cuda"):
+        super().__init__(kv, k_pages, sm_scale, device)
+        n = quest_step_workspace_size(kv, self.k_pages)
+        self.workspace = torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+    def __call__(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_lens,
+                 stream=None) -> torch.Tensor:
+        quest_sparse_decode_step(self.kv, q, k_pool, v_pool, kmin, kmax,
+                                 page_table, seq_lens, self.k_pages,
+                                 self.sm_scale, self.scores, self.sel,
+                                 self.out, self.workspace, stream)
+        return self.out
+
+    def control_words(self) -> torch.Tensor:
+        """The work-queue counters (ticket, exited, stalls): zero between
+        calls, stalls zero always."""
+        return self.workspace[:12].view(torch.int32)
 
 
 class DenseDecode:

@@ -32,7 +32,8 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
-SOURCES = ["api.cpp", "meta.hip", "estimate.hip", "topk.hip", "attention.hip"]
+SOURCES = ["api.cpp", "meta.hip", "estimate.hip", "topk.hip", "attention.hip",
+           "step.hip"]
 
 
 def _compile(src: str) -> str:

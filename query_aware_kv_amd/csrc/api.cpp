@@ -239,6 +239,52 @@ QUEST_API quest_status quest_decode_attn(const quest_paged_kv* kv,
                        workspace_bytes, stream, fn);
 }
 
+QUEST_API quest_status quest_sparse_decode_step(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const void* kmin, const void* kmax,
+    const int32_t* page_table, const int32_t* seq_lens, int32_t k_pages,
+    float sm_scale, float* scores, int32_t* sel_pages, float* out,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "quest_sparse_decode_step";
+  quest_status s = check_attention_common(kv, q, k_pool, v_pool, page_table,
+                                          seq_lens, sm_scale, out, fn);
+  if (s != QUEST_OK) return s;
+  REQUIRE_PTR(kmin, aligned16(kmin));
+  REQUIRE_PTR(kmax, aligned16(kmax));
+  REQUIRE_PTR(scores, aligned4(scores));
+  REQUIRE_PTR(sel_pages, aligned4(sel_pages));
+  if (k_pages < 1)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  if (kv->max_pages_per_seq > quest::kStepMaxPages)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: max_pages_per_seq %d > %d", fn,
+                kv->max_pages_per_seq, quest::kStepMaxPages);
+  const size_t need = quest::step_workspace_bytes(*kv, k_pages);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(QUEST_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu",
+                fn, need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: `workspace` must be 256-byte aligned", fn);
+  return hip_status(quest::launch_step(*kv, q, k_pool, v_pool, kmin, kmax,
+                                       page_table, seq_lens, k_pages, sm_scale,
+                                       scores, sel_pages, out, workspace,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+QUEST_API quest_status quest_step_workspace_size(const quest_paged_kv* kv,
+                                                 int32_t k_pages, size_t* bytes) {
+  const char* fn = "quest_step_workspace_size";
+  quest_status s = check_kv(kv, fn);
+  if (s != QUEST_OK) return s;
+  if ((s = check_group(kv, fn)) != QUEST_OK) return s;
+  if (bytes == nullptr)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: `bytes` is NULL", fn);
+  if (k_pages < 1)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  *bytes = quest::step_workspace_bytes(*kv, k_pages);
+  return ok();
+}
+
 QUEST_API quest_status quest_workspace_size(const quest_paged_kv* kv,
                                             int32_t k_pages, size_t* bytes) {
   const char* fn = "quest_workspace_size";

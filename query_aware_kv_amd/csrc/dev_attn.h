@@ -1,0 +1,235 @@
+// Flash-decoding building blocks: online-softmax attention of G query heads
+// over 16-token pages, and the merge of split partial results.
+//
+// "Quest: Query-Aware Sparsity for Efficient Long-Context LLM Inference"
+// (paper summary), Summary, and "Guide to Quest", §3: exact softmax attention
+// over the kept pages; the attention equation of "The Memory Bandwidth
+// Bottleneck of Long-Context Decoding" (Guide to Quest) for the dense case.
+//
+// Lane = 16 r + c of a wave holds channels 8c..8c+7 of token rows r, r+4,
+// r+8, r+12 of a page: each 16-byte load instruction reads 1 KiB contiguous
+// and every byte is read by one lane.  A row's q.k is a DPP row reduction.
+// Each row group r keeps its own online-softmax state over its tokens, so
+// the page loop needs no cross-row traffic; row groups, waves and splits are
+// combined afterwards with the usual rescaling.  Softmax runs in the exp2
+// domain (q pre-scaled by sm_scale * log2 e); accumulation is float32.
+// Tokens past a request's end are masked by selection, never by
+// multiplication, so unused slots may hold NaN.
+#pragma once
+
+#include "common.h"
+
+namespace quest {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int G>
+struct AttnState {
+  float m[G], l[G], o[G][8];
+};
+
+template <int G>
+__device__ __forceinline__ void attn_init(AttnState<G>& st) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = -INFINITY;
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.o[h][e] = 0.f;
+  }
+}
+
+template <DType T, int G>
+__device__ __forceinline__ void attn_load_q(const uint16_t* __restrict__ q,
+                                            int64_t first_head, int c, float qscale,
+                                            float (&qf)[G][8]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    widen8<T>(*reinterpret_cast<const uint4*>(q + (first_head + h) * kHeadDim + c * 8),
+              qf[h]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[h][e] *= qscale;
+  }
+}
+
+// 16-byte pieces of one (page, kv-head) tile for lane (r, c).
+__device__ __forceinline__ void attn_load_tile(const uint16_t* __restrict__ k_pool,
+                                               const uint16_t* __restrict__ v_pool,
+                                               int64_t p, int Hkv, int g, int r, int c,
+                                               uint4 (&kx)[4], uint4 (&vx)[4]) {
+  const int64_t tile = (p * Hkv + g) * (kPageSize * kHeadDim) + c * 8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kx[i] = *reinterpret_cast<const uint4*>(k_pool + tile + (r + 4 * i) * kHeadDim);
+    vx[i] = *reinterpret_cast<const uint4*>(v_pool + tile + (r + 4 * i) * kHeadDim);
+  }
+}
+
+// Fold one page (v valid tokens) into the row group's state.
+template <DType T, int G>
+__device__ __forceinline__ void attn_page(AttnState<G>& st, const float (&qf)[G][8],
+                                          const uint4 (&kx)[4], const uint4 (&vx)[4],
+                                          int v, int r) {
+  bool valid[4];
+  float kf[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    valid[i] = r + 4 * i < v;
+    widen8<T>(kx[i], kf[i]);
+  }
+  float z[G][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(qf[h][e], kf[i][e], acc);
+      z[h][i] = row16_sum(acc);
+    }
+  float vf[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    widen8<T>(vx[i], vf[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vf[i][e] = valid[i] ? vf[i][e] : 0.f;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = st.m[h];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = valid[i] ? fmaxf(mx, z[h][i]) : mx;
+    const float alpha = exp2_or_zero(st.m[h], mx);
+    float p[4], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = valid[i] ? exp2f(z[h][i] - mx) : 0.f;
+      ps += p[i];
+    }
+    st.l[h] = st.l[h] * alpha + ps;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc = st.o[h][e] * alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf(p[i], vf[i][e], acc);
+      st.o[h][e] = acc;
+    }
+    st.m[h] = mx;
+  }
+}
+
+// Combine the four row groups of a wave (lanes c, c+16, c+32, c+48).
+template <int G>
+__device__ __forceinline__ void attn_combine_rows(AttnState<G>& st) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float mo = shfl_xor_f(st.m[h], off), lo = shfl_xor_f(st.l[h], off);
+      const float M = fmaxf(st.m[h], mo);
+      const float sa = exp2_or_zero(st.m[h], M), sb = exp2_or_zero(mo, M);
+      st.l[h] = st.l[h] * sa + lo * sb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        st.o[h][e] = st.o[h][e] * sa + shfl_xor_f(st.o[h][e], off) * sb;
+      st.m[h] = M;
+    }
+  }
+}
+
+constexpr int kAttnWaves = 4;  // waves per attention workgroup
+
+template <int G>
+struct AttnSmem {
+  float o[kAttnWaves][G][kHeadDim];
+  float m[kAttnWaves][G], l[kAttnWaves][G];
+};
+
+// Publish each wave's (row-combined) state to LDS.  Caller syncs after.
+template <int G>
+__device__ __forceinline__ void attn_stage_wave(const AttnState<G>& st,
+                                                AttnSmem<G>& sm, int wid, int r,
+                                                int c) {
+  if (r == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.o[wid][h][c * 8 + e] = st.o[h][e];
+      if (c == 0) {
+        sm.m[wid][h] = st.m[h];
+        sm.l[wid][h] = st.l[h];
+      }
+    }
+  }
+}
+
+// The workgroup's combined (M, den, num[ch]) for head h, channel ch.
+template <int G>
+__device__ __forceinline__ void attn_wg_partial(const AttnSmem<G>& sm, int h, int ch,
+                                                float& M, float& den, float& num) {
+  M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm.m[w][h]);
+  den = 0.f;
+  num = 0.f;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) {
+    const float s = exp2_or_zero(sm.m[w][h], M);
+    den += sm.l[w][h] * s;
+    num += sm.o[w][h][ch] * s;
+  }
+}
+
+struct MergeSmem {
+  float red[kAttnWaves];
+  float half[kHeadDim];
+  float M, den;
+};
+
+// Merge nsplit partials of one (request, query head) into out_row[128] with
+// a 256-thread workgroup: partial s is (o[s*128 .. +128], ml[2s] = M,
+// ml[2s+1] = den).  All loads of a phase are independent, so they overlap.
+__device__ __forceinline__ void merge_splits(const float* __restrict__ o,
+                                             const float* __restrict__ ml,
+                                             int nsplit, float* __restrict__ out_row,
+                                             MergeSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  float mloc = -INFINITY;
+  for (int s = tid; s < nsplit; s += 256) mloc = fmaxf(mloc, ml[2 * s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, shfl_xor_f(mloc, off));
+  if (lane == 0) sm.red[wid] = mloc;
+  __syncthreads();
+  float M = sm.red[0];
+#pragma unroll
+  for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, sm.red[w]);
+  float dloc = 0.f;
+  for (int s = tid; s < nsplit; s += 256) dloc += ml[2 * s + 1] * exp2_or_zero(ml[2 * s], M);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dloc += shfl_xor_f(dloc, off);
+  __syncthreads();
+  if (lane == 0) sm.red[wid] = dloc;
+  const int ch = tid & (kHeadDim - 1), half = tid >> 7;
+  float num = 0.f;
+  int s = half;
+  for (; s + 6 < nsplit; s += 8) {
+    float w[4], x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u] = ml[2 * (s + 2 * u)];
+      x[u] = o[(int64_t)(s + 2 * u) * kHeadDim + ch];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) num += x[u] * exp2_or_zero(w[u], M);
+  }
+  for (; s < nsplit; s += 2) num += o[(int64_t)s * kHeadDim + ch] * exp2_or_zero(ml[2 * s], M);
+  if (half == 1) sm.half[ch] = num;
+  __syncthreads();
+  if (half == 0) {
+    const float den = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+    num += sm.half[ch];
+    out_row[ch] = den > 0.f ? num / den : 0.f;
+  }
+}
+
+}  // namespace quest

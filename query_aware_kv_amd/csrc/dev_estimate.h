@@ -1,0 +1,92 @@
+// Query-aware page estimate for a block of 4 consecutive pages of one
+// (request, kv-head) row, computed by one 16-lane DPP row.
+//
+// "Guide to Quest: Query-Aware KV Cache Sparsity for LLMs", §2 (upper-bound
+// inequality): a page's score is sum_i max(q_i * kmin_i, q_i * kmax_i); here
+// unscaled, and a GQA group sums the bounds of its G query heads.
+//
+// Lane c of the row holds channels 8c..8c+7 of the G query heads (G*8 floats)
+// and reads 16 B of kmin and 16 B of kmax per page, so a page's 512 B of
+// metadata is read once with 16-byte loads; the 16 partial sums of a page
+// meet in a DPP row reduction.  Products of two fp16 (or bf16) values are
+// exact in float32; only the sum rounds.
+#pragma once
+
+#include "common.h"
+
+namespace quest {
+
+constexpr int kEstPages = 4;  // pages per 16-lane row per block
+
+template <DType T, int G>
+__device__ __forceinline__ void est_load_q(const uint16_t* __restrict__ q,
+                                           int64_t first_head, int c,
+                                           float (&qf)[G][8]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    widen8<T>(*reinterpret_cast<const uint4*>(q + (first_head + h) * kHeadDim + c * 8),
+              qf[h]);
+}
+
+// Pool pages of logical pages j0..j0+3 (-1 past n or outside the pool).
+__device__ __forceinline__ void est_page_ids(const int32_t* __restrict__ pt_row,
+                                             int n, int j0, int num_pool_pages,
+                                             int (&pid)[kEstPages]) {
+#pragma unroll
+  for (int u = 0; u < kEstPages; ++u) {
+    const int j = j0 + u;
+    int p = j < n ? pt_row[j] : -1;
+    pid[u] = (p >= 0 && p < num_pool_pages) ? p : -1;
+  }
+}
+
+__device__ __forceinline__ void est_load_meta(const uint16_t* __restrict__ kmin,
+                                              const uint16_t* __restrict__ kmax,
+                                              const int (&pid)[kEstPages], int Hkv,
+                                              int g, int c, uint4 (&lo)[kEstPages],
+                                              uint4 (&hi)[kEstPages]) {
+#pragma unroll
+  for (int u = 0; u < kEstPages; ++u) {
+    if (pid[u] >= 0) {
+      const int64_t m = ((int64_t)pid[u] * Hkv + g) * kHeadDim + c * 8;
+      lo[u] = *reinterpret_cast<const uint4*>(kmin + m);
+      hi[u] = *reinterpret_cast<const uint4*>(kmax + m);
+    }
+  }
+}
+
+// Bound of each of the 4 pages (every lane of the row gets all 4).
+template <DType T, int G>
+__device__ __forceinline__ void est_score(const float (&qf)[G][8],
+                                          const int (&pid)[kEstPages],
+                                          const uint4 (&lo)[kEstPages],
+                                          const uint4 (&hi)[kEstPages],
+                                          float (&s)[kEstPages]) {
+#pragma unroll
+  for (int u = 0; u < kEstPages; ++u) {
+    float acc = 0.f;
+    if (pid[u] >= 0) {
+      float a[8], z[8];
+      widen8<T>(lo[u], a);
+      widen8<T>(hi[u], z);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += fmaxf(qf[h][e] * a[e], qf[h][e] * z[e]);
+    }
+    s[u] = row16_sum(acc);
+  }
+}
+
+// Lanes 0..3 of the row store the 4 scores (-inf where there is no page).
+__device__ __forceinline__ void est_store(float* __restrict__ srow, int j0,
+                                          int max_pages, int c,
+                                          const int (&pid)[kEstPages],
+                                          const float (&s)[kEstPages]) {
+  // one predicated store per page, constant register indices only
+#pragma unroll
+  for (int u = 0; u < kEstPages; ++u)
+    if (c == u && j0 + u < max_pages) srow[j0 + u] = pid[u] >= 0 ? s[u] : -INFINITY;
+}
+
+}  // namespace quest

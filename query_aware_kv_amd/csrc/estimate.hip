@@ -1,25 +1,18 @@
-// Query-aware page estimate.
+// quest_estimate: the query-aware upper bound of every page of every
+// (request, kv-head) row ("Guide to Quest", §2 upper-bound inequality; the
+// arithmetic lives in dev_estimate.h).
 //
-// "Guide to Quest: Query-Aware KV Cache Sparsity for LLMs", §2 (upper-bound
-// inequality): a page's score is sum_i max(q_i * kmin_i, q_i * kmax_i); here
-// unscaled, and a GQA group sums the bounds of its G query heads.
-//
-// Work mapping: a "row" of 16 lanes (one DPP row) owns one kv-head g of one
-// request and walks blocks of 4 consecutive logical pages; lane c of the row
-// holds channels 8c..8c+7 of the G query heads in registers (G*8 floats) and
-// reads 16 B of kmin and 16 B of kmax per page, so each page's 512 B of
-// metadata is read exactly once with 16-byte loads.  Rows of one wave take
-// consecutive kv-heads, which sit next to each other in the metadata.  The
-// 16 partial sums of a page meet through a DPP row reduction.  Products of
-// two fp16 (or bf16) values are exact in float32; only the sum rounds.
-#include "common.h"
+// Work mapping: a 16-lane DPP row owns one kv-head g of one request and walks
+// blocks of 4 consecutive pages, prefetching the next block's page ids while
+// it scores the current one.  Rows of one wave take consecutive kv-heads,
+// whose metadata sit next to each other in the pool.
+#include "dev_estimate.h"
 #include "launch.h"
 
 namespace quest {
 namespace {
 
 constexpr int kRowsPerBlock = 16;  // 256 threads
-constexpr int kPagesPerIter = 4;
 
 template <DType T, int G>
 __global__ void __launch_bounds__(256)
@@ -40,62 +33,22 @@ estimate_kernel(const uint16_t* __restrict__ q,
   const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
 
   float qf[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const int64_t off = (((int64_t)b * Hkv + g) * G + h) * kHeadDim + c * 8;
-    widen8<T>(*reinterpret_cast<const uint4*>(q + off), qf[h]);
-  }
-  const int32_t* pt = page_table + (int64_t)b * max_pages;
+  est_load_q<T, G>(q, ((int64_t)b * Hkv + g) * G, c, qf);
+  const int32_t* pt_row = page_table + (int64_t)b * max_pages;
   float* srow = scores + ((int64_t)b * Hkv + g) * max_pages;
 
-  auto load_ids = [&](int jb, int (&pid)[kPagesPerIter]) {
+  int pid[kEstPages];
+  est_page_ids(pt_row, n, jb0 * kEstPages, num_pool_pages, pid);
+  for (int jb = jb0; jb * kEstPages < max_pages; jb += rows_per_head) {
+    uint4 lo[kEstPages], hi[kEstPages];
+    est_load_meta(kmin, kmax, pid, Hkv, g, c, lo, hi);
+    int cur[kEstPages];
 #pragma unroll
-    for (int u = 0; u < kPagesPerIter; ++u) {
-      const int j = jb * kPagesPerIter + u;
-      pid[u] = j < n ? pt[j] : -1;
-      if (pid[u] >= num_pool_pages) pid[u] = -1;  // not a pool page
-    }
-  };
-
-  int pid[kPagesPerIter];
-  load_ids(jb0, pid);
-  for (int jb = jb0; jb * kPagesPerIter < max_pages; jb += rows_per_head) {
-    uint4 lo[kPagesPerIter], hi[kPagesPerIter];
-#pragma unroll
-    for (int u = 0; u < kPagesPerIter; ++u) {
-      if (pid[u] >= 0) {
-        const int64_t m = ((int64_t)pid[u] * Hkv + g) * kHeadDim + c * 8;
-        lo[u] = *reinterpret_cast<const uint4*>(kmin + m);
-        hi[u] = *reinterpret_cast<const uint4*>(kmax + m);
-      }
-    }
-    int cur[kPagesPerIter];
-#pragma unroll
-    for (int u = 0; u < kPagesPerIter; ++u) cur[u] = pid[u];
-    load_ids(jb + rows_per_head, pid);  // prefetch the next block's page ids
-
-    float s[kPagesPerIter];
-#pragma unroll
-    for (int u = 0; u < kPagesPerIter; ++u) {
-      float acc = 0.f;
-      if (cur[u] >= 0) {
-        float a[8], z[8];
-        widen8<T>(lo[u], a);
-        widen8<T>(hi[u], z);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            acc += fmaxf(qf[h][e] * a[e], qf[h][e] * z[e]);
-      }
-      s[u] = row16_sum(acc);
-    }
-    if (c < kPagesPerIter) {
-      const int j = jb * kPagesPerIter + c;
-      const float v = c == 0 ? s[0] : c == 1 ? s[1] : c == 2 ? s[2] : s[3];
-      const int id = c == 0 ? cur[0] : c == 1 ? cur[1] : c == 2 ? cur[2] : cur[3];
-      if (j < max_pages) srow[j] = id >= 0 ? v : -INFINITY;  // id < 0: j >= n
-    }
+    for (int u = 0; u < kEstPages; ++u) cur[u] = pid[u];
+    est_page_ids(pt_row, n, (jb + rows_per_head) * kEstPages, num_pool_pages, pid);
+    float s[kEstPages];
+    est_score<T, G>(qf, cur, lo, hi, s);
+    est_store(srow, jb * kEstPages, max_pages, c, cur, s);
   }
 }
 
@@ -104,8 +57,7 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
               const void* kmax, const int32_t* page_table,
               const int32_t* seq_lens, float* scores, hipStream_t stream) {
   const int Hkv = kv.num_kv_heads;
-  const int blocks_per_head =
-      (kv.max_pages_per_seq + kPagesPerIter - 1) / kPagesPerIter;
+  const int blocks_per_head = (kv.max_pages_per_seq + kEstPages - 1) / kEstPages;
   // Enough rows to keep ~24 waves per CU busy on 256 CUs, and never more
   // rows per head than 4-page blocks.
   const int64_t target_rows = 24576;
@@ -122,16 +74,15 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
 }
 
 template <DType T>
-bool dispatch_group(int G, const quest_paged_kv& kv, const void* q,
+void dispatch_group(int G, const quest_paged_kv& kv, const void* q,
                     const void* kmin, const void* kmax,
                     const int32_t* page_table, const int32_t* seq_lens,
                     float* scores, hipStream_t stream) {
   switch (G) {
-    case 1: launch_t<T, 1>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); return true;
-    case 2: launch_t<T, 2>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); return true;
-    case 4: launch_t<T, 4>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); return true;
-    case 8: launch_t<T, 8>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); return true;
-    default: return false;
+    case 1: launch_t<T, 1>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
+    case 2: launch_t<T, 2>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
+    case 4: launch_t<T, 4>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
+    default: launch_t<T, 8>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
   }
 }
 

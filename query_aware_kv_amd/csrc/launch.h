@@ -43,4 +43,15 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
                             const int32_t* sel, int list_len, float sm_scale,
                             float* out, void* workspace, hipStream_t stream);
 
+// Fused step (estimate -> Top-K -> attention in one launch).
+constexpr int kStepMaxPages = 8192;
+size_t step_workspace_bytes(const quest_paged_kv& kv, int k_pages);
+hipError_t launch_step(const quest_paged_kv& kv, const void* q,
+                       const void* k_pool, const void* v_pool,
+                       const void* kmin, const void* kmax,
+                       const int32_t* page_table, const int32_t* seq_lens,
+                       int k_pages, float sm_scale, float* scores,
+                       int32_t* sel, float* out, void* workspace,
+                       hipStream_t stream);
+
 }  // namespace quest
