@@ -38,7 +38,7 @@ namespace {
 
 constexpr int kStepThreads = 256;
 constexpr int kEstItemPages = (kStepThreads / 16) * kEstPages;  // 64
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kSpinLimit = 1u << 20;
 
 struct StepCtrl {
   uint32_t ticket;  // next work item
@@ -144,12 +144,18 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, uint32_t t, StepSme
   const int L = a.seq_lens[b];
   const int n = row_pages(a, b);
   if (tid == 0) {
+    // Poll with relaxed loads (no cache invalidation per poll); the single
+    // acquire fence below orders what follows after the flag.  The first
+    // wait to reach the limit raises `stalls`, which ends every other wait.
     uint32_t spins = 0;
-    while (__hip_atomic_load(&a.ready[row], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+    while (__hip_atomic_load(&a.ready[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
       if (++spins > kSpinLimit) {
         atomicAdd(&a.ctrl->stalls, 1u);
         break;
       }
+      if ((spins & 63u) == 0u &&
+          __hip_atomic_load(&a.ctrl->stalls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+        break;
       __builtin_amdgcn_s_sleep(2);
     }
   }
@@ -287,10 +293,12 @@ StepPlan step_plan(const quest_paged_kv& kv, int k) {
   return p;
 }
 
-template <typename K>
-int grid_for(K kernel, uint32_t items) {
-  static int per_cu = -1, cus = -1;  // same for every call of one kernel
+// Resident workgroups of one kernel on the whole device (cached per kernel).
+template <DType T, int G, int KPT, int PPW>
+int grid_for(uint32_t items) {
+  static int per_cu = -1, cus = -1;  // one cache per kernel instantiation
   if (per_cu < 0) {
+    auto kernel = step_kernel<T, G, KPT, PPW>;
     int dev = 0, nb = 0, ncu = 0;
     (void)hipGetDevice(&dev);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kStepThreads, 0) != hipSuccess || nb < 1)
@@ -306,9 +314,8 @@ int grid_for(K kernel, uint32_t items) {
 
 template <DType T, int G, int KPT, int PPW>
 void launch_t(const StepArgs& a, hipStream_t stream) {
-  auto kern = step_kernel<T, G, KPT, PPW>;
-  const int grid = grid_for(kern, a.n_est + a.n_attn);
-  kern<<<grid, kStepThreads, 0, stream>>>(a);
+  const int grid = grid_for<T, G, KPT, PPW>(a.n_est + a.n_attn);
+  step_kernel<T, G, KPT, PPW><<<grid, kStepThreads, 0, stream>>>(a);
 }
 
 template <DType T, int G>
