@@ -2,9 +2,8 @@
 
     python bench.py [--steps K] [--warmup W] [--workload longchat]
 
-A "step" is one pass of the whole hot path -- estimate -> Top-K -> sparse
-attention, as the one-launch quest_sparse_decode_step (the three separate
-calls are timed too and reported beside it) -- over one LongChat-7B-shaped
+A "step" is one pass of the whole hot path -- quest_estimate ->
+quest_topk_pages -> quest_sparse_decode_attn -- over one LongChat-7B-shaped
 layer (32 heads, 32K context, 2048-token budget, fp16).  Inputs are seeded
 synthetic caches drawn on the GPU and resident in HBM before timing starts.
 Consecutive steps rotate over several independent caches whose touched bytes
@@ -123,20 +122,13 @@ def run_gpu(args):
     kv = insts[0]["kv"]
     sm = 1.0 / math.sqrt(128)
     seps = [qa.SparseDecodeStep(kv, base.k_pages, sm) for _ in range(rot)]
-    fused = [qa.FusedDecodeStep(kv, base.k_pages, sm) for _ in range(rot)]
     dense = qa.DenseDecode(kv, sm)
     stream = torch.cuda.current_stream()
 
-    def args_of(i):
-        c = insts[i % rot]
-        return (c["q"], c["k_pool"], c["v_pool"], c["kmin"], c["kmax"],
-                c["page_table"], c["seq_lens"])
-
-    def fused_step(i):
-        fused[i % rot](*args_of(i))
-
     def sep_step(i):
-        seps[i % rot](*args_of(i))
+        c = insts[i % rot]
+        seps[i % rot](c["q"], c["k_pool"], c["v_pool"], c["kmin"], c["kmax"],
+                      c["page_table"], c["seq_lens"])
 
     def dense_step(i):
         c = insts[i % rot]
@@ -152,15 +144,12 @@ def run_gpu(args):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / k * 1e6
 
-    us_step = timed(fused_step, args.steps, args.warmup)
-    us_sep = timed(sep_step, args.steps, args.warmup)
+    us_step = timed(sep_step, args.steps, args.warmup)
     us_dense = (float("nan") if args.no_dense else
                 timed(dense_step, max(10, args.steps // 4), args.warmup))
 
-    # HIP-event kernel times on the launch stream, K more steps each
-    t_fused, t_est, t_topk, t_attn = (KernelTimer(torch, stream) for _ in range(4))
-    for i in range(args.steps):
-        t_fused.around(lambda: fused_step(i))
+    # HIP-event kernel times on the launch stream over K more steps
+    t_est, t_topk, t_attn = (KernelTimer(torch, stream) for _ in range(3))
     for i in range(args.steps):
         c = insts[i % rot]
         st = seps[i % rot]
@@ -172,27 +161,32 @@ def run_gpu(args):
         t_attn.around(lambda: qa.quest_sparse_decode_attn(
             kv, c["q"], c["k_pool"], c["v_pool"], c["page_table"],
             c["seq_lens"], st.sel, st.k_pages, sm, st.out, st.workspace))
-    us_fused = t_fused.mean_us()
     us_est, us_topk, us_attn = t_est.mean_us(), t_topk.mean_us(), t_attn.mean_us()
-    stalls = sum(int(f.control_words()[2]) for f in fused)
 
     # algorithmic bytes from the selections actually made
-    sels = [f.sel.cpu().numpy() for f in fused]
+    sels = [st.sel.cpu().numpy() for st in seps]
     lens = [int(x) for x in insts[0]["seq_lens"].cpu()]
     bstep = [step_bytes(lens, kv.num_kv_heads, kv.num_q_heads, base.k_pages,
                         sel=s) for s in sels]
     avg = {k: sum(b[k] for b in bstep) / len(bstep) for k in bstep[0]}
-    achieved = avg["total"] / (us_fused * 1e-6) / 1e9
+    est_bytes = avg["meta"] + avg["q"] + avg["table"] + \
+        kv.num_kv_heads * kv.max_pages_per_seq * 4 * len(lens)
+    attn_bytes = avg["kv"] + avg["q"] + avg["out"] + \
+        kv.num_kv_heads * base.k_pages * 4 * len(lens)
+    kern = {"quest_estimate (estimate_kernel)": (us_est, est_bytes),
+            "quest_sparse_decode_attn (attn_split_kernel + attn_merge_kernel)":
+                (us_attn, attn_bytes)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    d_us, d_bytes = kern[dom]
+    achieved = d_bytes / (d_us * 1e-6) / 1e9
     return dict(
-        us_step=us_step, us_sep=us_sep, us_dense=us_dense, bytes=avg,
-        us_fused_kernel=us_fused, us_est=us_est, us_topk=us_topk,
-        us_attn=us_attn, stalls=stalls,
+        us_step=us_step, us_dense=us_dense, bytes=avg, us_est=us_est,
+        us_topk=us_topk, us_attn=us_attn,
         roofline={"bound": "hbm", "achieved": round(achieved, 1),
                   "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                  "kernel": "step_kernel (quest_sparse_decode_step)",
-                  "kernel_us": round(us_fused, 3),
-                  "bytes_per_launch": int(avg["total"])},
+                  "kernel": dom, "kernel_us": round(d_us, 3),
+                  "bytes_per_launch": int(d_bytes)},
         dense_bytes=dense_bytes(lens, kv.num_kv_heads, kv.num_q_heads),
         gpu=torch.cuda.get_device_name(0), insts=insts, kv=kv,
         k_pages=base.k_pages, sm=sm)
@@ -288,12 +282,9 @@ def main():
         "dense_us_per_step": round(g["us_dense"], 3),
         "speedup_vs_dense": round(g["us_dense"] / us, 3),
         "dense_effective_GBps": round(g["dense_bytes"] / (g["us_dense"] * 1e-6) / 1e9, 1),
-        "separate_calls_us_per_step": round(g["us_sep"], 3),
-        "kernel_us": {"quest_sparse_decode_step": round(g["us_fused_kernel"], 3),
-                      "quest_estimate": round(g["us_est"], 3),
+        "kernel_us": {"quest_estimate": round(g["us_est"], 3),
                       "quest_topk_pages": round(g["us_topk"], 3),
                       "quest_sparse_decode_attn": round(g["us_attn"], 3)},
-        "step_wait_stalls": g["stalls"],
         "roofline": g["roofline"],
         "gpu": g["gpu"],
     }

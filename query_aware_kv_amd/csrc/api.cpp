@@ -13,6 +13,11 @@
 
 namespace {
 
+// The one-launch step kernel (step.hip) did not complete on gfx950 in its
+// first runs, and the cause is not yet found; its entry point refuses work
+// before any launch until it is.
+constexpr bool kFusedStepEnabled = false;
+
 thread_local char g_last_error[512] = "";
 
 quest_status fail(quest_status s, const char* fmt, ...) {
@@ -249,6 +254,12 @@ QUEST_API quest_status quest_sparse_decode_step(
   quest_status s = check_attention_common(kv, q, k_pool, v_pool, page_table,
                                           seq_lens, sm_scale, out, fn);
   if (s != QUEST_OK) return s;
+  if (!kFusedStepEnabled)
+    return fail(QUEST_ERR_UNSUPPORTED,
+                "%s: the one-launch step is switched off in this build (its "
+                "kernel did not complete on gfx950; cause not yet found) -- "
+                "use quest_estimate + quest_topk_pages + "
+                "quest_sparse_decode_attn", fn);
   REQUIRE_PTR(kmin, aligned16(kmin));
   REQUIRE_PTR(kmax, aligned16(kmax));
   REQUIRE_PTR(scores, aligned4(scores));

@@ -166,3 +166,14 @@ def test_python_binding_rejects_host_tensors():
     t = torch.zeros(1, 1, 128, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         qa.quest_estimate(k, t, t, t, t, t, t)
+
+
+def test_fused_step_is_switched_off():
+    """The one-launch step refuses work before any launch in this build."""
+    k = kv()
+    P = ctypes.c_void_p
+    st = qa.LIB.quest_sparse_decode_step(
+        ctypes.byref(k), *([P(FAKE)] * 7), 128, 0.088, P(FAKE), P(FAKE),
+        P(FAKE), P(FAKE), 1 << 30, None)
+    assert st == _abi.QUEST_ERR_UNSUPPORTED
+    assert "switched off" in qa.LIB.quest_last_error().decode()

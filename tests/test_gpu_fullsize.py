@@ -2,7 +2,7 @@
 benchmark times.  The oracle recomputes sampled (request, kv-head) units one
 by one from host copies of the same inputs; every unit is also checked for
 properties that hold at any size (valid ascending selections, planted pages
-kept, fused path == separate calls)."""
+kept)."""
 import math
 
 import numpy as np
@@ -80,30 +80,24 @@ def check_units(c, step, units, k, G, check_meta=None):
 
 
 def run_paths(c, k):
+    """The separate-call step (the one-launch step is switched off)."""
     kmin, kmax = C.gpu_meta(c)
-    fused = qa.FusedDecodeStep(c["kv"], k, SM)
     sep = qa.SparseDecodeStep(c["kv"], k, SM)
-    args = (c["q"], c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"],
-            c["seq_lens"])
-    fused(*args)
-    sep(*args)
+    sep(c["q"], c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"],
+        c["seq_lens"])
     torch.cuda.synchronize()
-    assert torch.equal(fused.sel, sep.sel)
-    assert torch.equal(fused.scores.view(torch.int32), sep.scores.view(torch.int32))
-    assert (fused.out - sep.out).abs().max().item() <= 1e-5
-    assert fused.control_words().tolist() == [0, 0, 0]
-    return fused, (kmin, kmax)
+    return sep, (kmin, kmax)
 
 
 def test_longchat_layer_32k_budget_2048():
     wl = synth.longchat_layer_workload()
     C.say(f"[case] {wl.name}: 32 heads, ctx 32768, k={wl.k_pages}")
     c = build(wl)
-    fused, meta = run_paths(c, wl.k_pages)
-    worst = check_units(c, fused, [(0, [0, 7]), (0, [19, 31])], wl.k_pages, 1,
+    step, meta = run_paths(c, wl.k_pages)
+    worst = check_units(c, step, [(0, [0, 7]), (0, [19, 31])], wl.k_pages, 1,
                         check_meta=meta)
     C.say(f"  sampled attention max err {worst:.2e}")
-    sel = fused.sel.cpu().numpy()
+    sel = step.sel.cpu().numpy()
     for g in range(32):   # the planted pages are kept in every head
         plant = set(synth.planted_pages(wl, 0, 0, g, 2048).tolist())
         assert plant <= set(sel[0, g].tolist()), g
@@ -115,21 +109,21 @@ def test_sweep_point(ctx, budget):
     wl = synth.sweep_workload(ctx, budget)
     C.say(f"[case] {wl.name}")
     c = build(wl)
-    fused, meta = run_paths(c, wl.k_pages)
-    check_units(c, fused, [(0, [5]), (0, [26])], wl.k_pages, 1, check_meta=meta)
+    step, meta = run_paths(c, wl.k_pages)
+    check_units(c, step, [(0, [5]), (0, [26])], wl.k_pages, 1, check_meta=meta)
     if wl.k_pages >= wl.max_pages:  # every page kept: the step is dense
         dense = qa.DenseDecode(c["kv"], SM)
         d = dense(c["q"], c["k_pool"], c["v_pool"], c["page_table"], c["seq_lens"])
         torch.cuda.synchronize()
-        assert (fused.out - d).abs().max().item() <= 1e-5
+        assert (step.out - d).abs().max().item() <= 1e-5
 
 
 def test_ragged_batch_bf16():
     wl = synth.ragged_batch_workload()
     C.say(f"[case] {wl.name}: lens {min(wl.seq_lens)}..{max(wl.seq_lens)} bf16")
     c = build(wl)
-    fused, meta = run_paths(c, wl.k_pages)
-    check_units(c, fused, [(0, [0]), (9, [13]), (17, [31]), (31, [2])],
+    step, meta = run_paths(c, wl.k_pages)
+    check_units(c, step, [(0, [0]), (9, [13]), (17, [31]), (31, [2])],
                 wl.k_pages, 1, check_meta=meta)
 
 
@@ -155,7 +149,7 @@ def test_gqa_multistep_three_layers():
         o["kmin"], o["kmax"] = O.page_meta(o["kp"], o["pt"],
                                            c["seq_lens"].cpu().numpy(), 16)
         layers.append(dict(c=c, kv=kv, kmin=kmin, kmax=kmax, o=o,
-                           fused=qa.FusedDecodeStep(kv, k, SM),
+                           step=qa.SparseDecodeStep(kv, k, SM),
                            dense=qa.DenseDecode(kv, SM)))
     L = wl.seq_lens[0]
     for step in range(wl.steps):
@@ -171,7 +165,7 @@ def test_gqa_multistep_three_layers():
             if layer < wl.dense_layers:
                 out = st["dense"](q, c["k_pool"], c["v_pool"], c["page_table"], lens)
             else:
-                out = st["fused"](q, c["k_pool"], c["v_pool"], st["kmin"],
+                out = st["step"](q, c["k_pool"], c["v_pool"], st["kmin"],
                                   st["kmax"], c["page_table"], lens)
             torch.cuda.synchronize()
             o = st["o"]
@@ -183,7 +177,7 @@ def test_gqa_multistep_three_layers():
             if layer < wl.dense_layers:
                 C.assert_attention_close(got, out_o)
             else:
-                f = st["fused"]
+                f = st["step"]
                 s_gpu = f.scores.cpu().numpy().astype(np.float64)[:, heads]
                 C.assert_scores_close(s_gpu, s_o, np.array([L]))
                 sel = f.sel.cpu().numpy().astype(np.int64)[:, heads]
@@ -191,7 +185,6 @@ def test_gqa_multistep_three_layers():
                 ref = O.sparse_attention(C.to64(q[:, qh]), o["kp"], o["vp"],
                                          o["pt"], np.array([L]), sel, SM, 16)
                 C.assert_attention_close(got, ref)
-                assert f.control_words().tolist() == [0, 0, 0]
     # boxes after the appends equal the oracle's running boxes, bit for bit
     for st in layers:
         n = -(-L // 16)
