@@ -30,8 +30,9 @@ def default_sm_scale(head_dim: int = HEAD_DIM) -> float:
 
 
 def alloc_workspace(kv: PagedKV, k_pages: int, device="cuda") -> torch.Tensor:
+    """Zero-filled attention workspace (the calls keep its counters zero)."""
     n = quest_workspace_size(kv, k_pages)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def alloc_meta(kv: PagedKV, device="cuda"):

@@ -6,7 +6,9 @@
 // skipped) or 0..n_b-1 -- and issues all of their K and V loads before any
 // arithmetic (PPW * 8 KiB in flight per wave).  The four waves meet in LDS;
 // with one split per row the workgroup writes the output directly, otherwise
-// a partial (o[128], M, den) per query head, which the merge kernel combines.
+// a partial (o[128], M, den) per query head; the workgroup that completes a
+// row's last split (a per-row counter in the workspace elects it; nobody
+// waits) merges the row's partials and resets the counter.
 #include "dev_attn.h"
 #include "launch.h"
 
@@ -22,39 +24,43 @@ attn_split_kernel(const uint16_t* __restrict__ q,
                   const int32_t* __restrict__ seq_lens,
                   const int32_t* __restrict__ sel, int list_len, int Hkv,
                   int max_pages, int num_pool_pages, float qscale,
-                  float* __restrict__ out, float* __restrict__ ws_o,
-                  float* __restrict__ ws_ml) {
-  __shared__ AttnSmem<G> sm;
+                  float* __restrict__ out, uint32_t* __restrict__ done,
+                  float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  __shared__ union {
+    AttnSmem<G> attn;
+    MergeSmem merge;
+  } sm;
+  __shared__ uint32_t sh_last;
   const int unit = blockIdx.y;  // b * Hkv + g
   const int b = unit / Hkv, g = unit - (unit / Hkv) * Hkv;
   const int split = blockIdx.x, nsplit = gridDim.x;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int c = lane & 15, r = lane >> 4;
-  const int L = seq_lens[b];
-  const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
 
-  float qf[G][8];
-  attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
-
+  // List entries, then their table entries: neither waits for the length
+  // (both are in bounds on their own); the length only masks afterwards.
   const int i0 = (split * kAttnWaves + wid) * PPW;
-  int pj[PPW];
+  int jr[PPW];
   int64_t pp[PPW];
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi) {
     const int i = i0 + pi;
-    int j = -1;
-    if (sel) {
-      if (i < list_len) j = sel[(int64_t)unit * list_len + i];
-    } else if (i < n) {
-      j = i;
-    }
-    pj[pi] = (j >= 0 && j < n) ? j : -1;
+    jr[pi] = sel ? (i < list_len ? sel[(int64_t)unit * list_len + i] : -1)
+                 : (i < max_pages ? i : -1);
   }
 #pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
-    pp[pi] = pj[pi] >= 0 ? page_table[(int64_t)b * max_pages + pj[pi]] : -1;
-    if (pp[pi] < 0 || pp[pi] >= num_pool_pages) pj[pi] = -1;  // not a pool page
-  }
+  for (int pi = 0; pi < PPW; ++pi)
+    pp[pi] = (jr[pi] >= 0 && jr[pi] < max_pages)
+                 ? page_table[(int64_t)b * max_pages + jr[pi]] : -1;
+  const int L = seq_lens[b];
+  float qf[G][8];
+  attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
+  const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
+  int pj[PPW];
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi)
+    pj[pi] = (jr[pi] >= 0 && jr[pi] < n && pp[pi] >= 0 && pp[pi] < num_pool_pages)
+                 ? jr[pi] : -1;
   uint4 kx[PPW][4], vx[PPW][4];
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi)
@@ -67,14 +73,14 @@ attn_split_kernel(const uint16_t* __restrict__ q,
     if (pj[pi] >= 0)
       attn_page<T, G>(st, qf, kx[pi], vx[pi], min(kPageSize, L - pj[pi] * kPageSize), r);
   attn_combine_rows(st);
-  attn_stage_wave(st, sm, wid, r, c);
+  attn_stage_wave(st, sm.attn, wid, r, c);
   __syncthreads();
 
   const int Hq = Hkv * G;
   for (int idx = tid; idx < G * kHeadDim; idx += 256) {
     const int h = idx / kHeadDim, ch = idx - h * kHeadDim;
     float M, den, num;
-    attn_wg_partial(sm, h, ch, M, den, num);
+    attn_wg_partial(sm.attn, h, ch, M, den, num);
     const int64_t qh = (int64_t)b * Hq + g * G + h;
     if (nsplit == 1) {
       out[qh * kHeadDim + ch] = den > 0.f ? num / den : 0.f;
@@ -87,17 +93,24 @@ attn_split_kernel(const uint16_t* __restrict__ q,
       }
     }
   }
-}
-
-// One workgroup per (request, query head): combine its splits.
-__global__ void __launch_bounds__(256)
-attn_merge_kernel(const float* __restrict__ ws_o,
-                  const float* __restrict__ ws_ml, int nsplit,
-                  float* __restrict__ out) {
-  __shared__ MergeSmem sm;
-  const int64_t qh = blockIdx.x;
-  merge_splits(ws_o + qh * nsplit * kHeadDim, ws_ml + qh * nsplit * 2, nsplit,
-               out + qh * kHeadDim, sm);
+  if (nsplit == 1) return;
+  // The workgroup that completes a row's last split merges the row.  No
+  // workgroup ever waits for another: the counter only elects the merger.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0)
+    sh_last = __hip_atomic_fetch_add(&done[unit], 1u, __ATOMIC_ACQ_REL,
+                                     __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsplit - 1);
+  __syncthreads();
+  if (!sh_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int h = 0; h < G; ++h) {
+    const int64_t qh = (int64_t)b * Hq + g * G + h;
+    merge_splits(ws_o + qh * nsplit * kHeadDim, ws_ml + qh * nsplit * 2, nsplit,
+                 out + qh * kHeadDim, sm.merge);
+    __syncthreads();
+  }
+  if (tid == 0) done[unit] = 0;  // leave the counter at zero for the next call
 }
 
 int max_ppw(int G) { return G == 1 ? 4 : G <= 4 ? 2 : 1; }
@@ -125,14 +138,14 @@ template <DType T, int G, int PPW>
 void launch_split(const quest_paged_kv& kv, const void* q, const void* k_pool,
                   const void* v_pool, const int32_t* page_table,
                   const int32_t* seq_lens, const int32_t* sel, int list_len,
-                  float qscale, float* out, float* ws_o, float* ws_ml,
-                  int nsplit, hipStream_t stream) {
+                  float qscale, float* out, uint32_t* done, float* ws_o,
+                  float* ws_ml, int nsplit, hipStream_t stream) {
   dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
   attn_split_kernel<T, G, PPW><<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), page_table, seq_lens, sel,
       list_len, kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages,
-      qscale, out, ws_o, ws_ml);
+      qscale, out, done, ws_o, ws_ml);
 }
 
 template <DType T>
@@ -140,10 +153,12 @@ void dispatch(int G, int ppw, const quest_paged_kv& kv, const void* q,
               const void* k_pool, const void* v_pool,
               const int32_t* page_table, const int32_t* seq_lens,
               const int32_t* sel, int list_len, float qscale, float* out,
-              float* ws_o, float* ws_ml, int nsplit, hipStream_t stream) {
+              uint32_t* done, float* ws_o, float* ws_ml, int nsplit,
+              hipStream_t stream) {
 #define QUEST_SPLIT(GG, PP)                                                   \
   launch_split<T, GG, PP>(kv, q, k_pool, v_pool, page_table, seq_lens, sel,  \
-                          list_len, qscale, out, ws_o, ws_ml, nsplit, stream)
+                          list_len, qscale, out, done, ws_o, ws_ml, nsplit,   \
+                          stream)
   if (G == 1) {
     if (ppw == 4) QUEST_SPLIT(1, 4);
     else if (ppw == 2) QUEST_SPLIT(1, 2);
@@ -160,6 +175,22 @@ void dispatch(int G, int ppw, const quest_paged_kv& kv, const void* q,
 #undef QUEST_SPLIT
 }
 
+struct WsLayout {
+  size_t off_o, off_ml, bytes;
+};
+
+// [per-row split counters][partial o][partial (M, den)], 256-byte aligned.
+WsLayout ws_layout(const quest_paged_kv& kv, int nsplit) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t units = (size_t)kv.batch * kv.num_kv_heads;
+  const size_t slots = (size_t)kv.batch * kv.num_q_heads * nsplit;
+  WsLayout w;
+  w.off_o = al(units * sizeof(uint32_t));
+  w.off_ml = w.off_o + al(slots * kHeadDim * sizeof(float));
+  w.bytes = w.off_ml + al(slots * 2 * sizeof(float));
+  return w;
+}
+
 }  // namespace
 
 bool attention_supported(int group) {
@@ -169,8 +200,7 @@ bool attention_supported(int group) {
 size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len) {
   const Plan pl = plan(kv, list_len);
   if (pl.nsplit == 1) return 0;
-  const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
-  return slots * (kHeadDim + 2) * sizeof(float);
+  return ws_layout(kv, pl.nsplit).bytes;
 }
 
 hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
@@ -180,20 +210,20 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
                             float* out, void* workspace, hipStream_t stream) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
   const Plan pl = plan(kv, list_len);
-  const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_ml = ws_o ? ws_o + slots * kHeadDim : nullptr;
+  const WsLayout w = ws_layout(kv, pl.nsplit);
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* done = ws ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+  float* ws_o = ws ? reinterpret_cast<float*>(ws + w.off_o) : nullptr;
+  float* ws_ml = ws ? reinterpret_cast<float*>(ws + w.off_ml) : nullptr;
   const float qscale = sm_scale * kLog2e;
   if (kv.dtype == QUEST_F16)
     dispatch<DType::F16>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                         sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit, stream);
+                         sel, list_len, qscale, out, done, ws_o, ws_ml, pl.nsplit,
+                         stream);
   else
     dispatch<DType::BF16>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                          sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit, stream);
-  if (pl.nsplit > 1) {
-    attn_merge_kernel<<<kv.batch * kv.num_q_heads, 256, 0, stream>>>(
-        ws_o, ws_ml, pl.nsplit, out);
-  }
+                          sel, list_len, qscale, out, done, ws_o, ws_ml, pl.nsplit,
+                          stream);
   return hipGetLastError();
 }
 

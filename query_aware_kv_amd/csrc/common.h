@@ -62,6 +62,31 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Integer DPP move: lanes whose source is out of range (or masked off by
+// row_mask) get 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: row_shr by
+// 1, 2, 4, 8 scans each 16-lane row, then row_bcast:15 and row_bcast:31
+// carry the row totals into the rows above.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+  x += dpp_u<0x111>(x);        // row_shr:1
+  x += dpp_u<0x112>(x);        // row_shr:2
+  x += dpp_u<0x114>(x);        // row_shr:4
+  x += dpp_u<0x118>(x);        // row_shr:8
+  x += dpp_u<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_u<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Broadcast of lane 63 (the total of an inclusive scan).
+__device__ __forceinline__ uint32_t wave_last(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 __device__ __forceinline__ float shfl_xor_f(float x, int m) {
   return __shfl_xor(x, m, kWave);
 }

@@ -28,15 +28,24 @@ __device__ __forceinline__ void est_load_q(const uint16_t* __restrict__ q,
               qf[h]);
 }
 
+// Page-table entries of logical pages j0..j0+3.  Entries up to max_pages
+// are always in bounds, so they are read without waiting for the length.
+__device__ __forceinline__ void est_table(const int32_t* __restrict__ pt_row,
+                                          int max_pages, int j0,
+                                          int (&ent)[kEstPages]) {
+#pragma unroll
+  for (int u = 0; u < kEstPages; ++u)
+    ent[u] = j0 + u < max_pages ? pt_row[j0 + u] : -1;
+}
+
 // Pool pages of logical pages j0..j0+3 (-1 past n or outside the pool).
-__device__ __forceinline__ void est_page_ids(const int32_t* __restrict__ pt_row,
-                                             int n, int j0, int num_pool_pages,
+__device__ __forceinline__ void est_page_ids(const int (&ent)[kEstPages], int n,
+                                             int j0, int num_pool_pages,
                                              int (&pid)[kEstPages]) {
 #pragma unroll
   for (int u = 0; u < kEstPages; ++u) {
-    const int j = j0 + u;
-    int p = j < n ? pt_row[j] : -1;
-    pid[u] = (p >= 0 && p < num_pool_pages) ? p : -1;
+    const int p = ent[u];
+    pid[u] = (j0 + u < n && p >= 0 && p < num_pool_pages) ? p : -1;
   }
 }
 

@@ -36,33 +36,39 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = min(x, (uint32_t)__shfl_xor(x, off, kWave));
-  return x;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint32_t)__shfl_xor(x, off, kWave));
-  return x;
+// Wave min / max with DPP: rows by row_ror, then across rows by readlane.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t x) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x124, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x122, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x121, 0xf, 0xf, false));
+  const uint32_t r0 = __builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = __builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = __builtin_amdgcn_readlane((int)x, 48);
+  return op(op(r0, r1), op(r2, r3));
 }
 
 // Select for one row.  The whole block (BLOCK threads) must call it.
-//   s      : the row's n fp32 scores (n <= BLOCK * KPT)
+//   v      : this thread's scores from topk_load (the row has n <= BLOCK*KPT)
 //   out    : k slots; kept logical page indices ascending, then -1
 //   pt_row : if non-null, phys[slot] = pt_row[page] for each kept page and
 //            -1 for the padding (the physical page list used by attention)
+// Load a thread's KPT consecutive scores; entries below `limit` are in
+// bounds (limit = the row's length in the buffer), so callers can issue this
+// before they know n.
 template <int BLOCK, int KPT>
-__device__ __forceinline__ void topk_row(const float* __restrict__ s, int n, int k,
+__device__ __forceinline__ void topk_load(const float* __restrict__ s, int limit,
+                                          float (&v)[KPT]) {
+  const int base = threadIdx.x * KPT;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) v[i] = base + i < limit ? s[base + i] : 0.f;
+}
+
+template <int BLOCK, int KPT>
+__device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
                          int32_t* __restrict__ out,
                          const int32_t* __restrict__ pt_row,
                          int32_t* __restrict__ phys, TopkSmem<BLOCK>& sm) {
@@ -82,14 +88,14 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ s, int n, int
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const bool ok = base + i < n;
-    key[i] = ok ? score_key(s[base + i]) : 0u;
+    key[i] = ok ? score_key(v[i]) : 0u;
     if (ok) {
       kmn = min(kmn, key[i]);
       kmx = max(kmx, key[i]);
     }
   }
-  kmn = wave_min_u32(kmn);
-  kmx = wave_max_u32(kmx);
+  kmn = wave_minmax_u32<false>(kmn);
+  kmx = wave_minmax_u32<true>(kmx);
   if (lane == 0) {
     sm.red[0][wid] = kmn;
     sm.red[1][wid] = kmx;
@@ -123,22 +129,17 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ s, int n, int
       }
       __syncthreads();
       if (wid == 0) {
-        // lane l owns digits 4l..4l+3; find the digit whose bin holds the
-        // need-th largest candidate, scanning from the top digit down.
+        // lane l owns digits 255-4l down to 252-4l, so a prefix sum over the
+        // lanes counts candidates from the top digit down; find the digit
+        // whose bin holds the need-th largest candidate.
         uint32_t h[4], tot = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { h[e] = sm.hist[buf][4 * lane + e]; tot += h[e]; }
-        uint32_t incl = tot;  // inclusive suffix sum over lanes >= lane
+        for (int e = 0; e < 4; ++e) { h[e] = sm.hist[buf][255 - 4 * lane - e]; tot += h[e]; }
+        uint32_t above = wave_scan_incl(tot) - tot;  // candidates in higher digits
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const uint32_t y = __shfl_down(incl, off, kWave);
-          if (lane + off < kWave) incl += y;
-        }
-        uint32_t above = incl - tot;
-#pragma unroll
-        for (int e = 3; e >= 0; --e) {
+        for (int e = 0; e < 4; ++e) {
           if (above < need && above + h[e] >= need) {
-            sm.prefix = (prefix & ~(0xffu << shift)) | ((uint32_t)(4 * lane + e) << shift);
+            sm.prefix = (prefix & ~(0xffu << shift)) | ((uint32_t)(255 - 4 * lane - e) << shift);
             sm.need = need - above;
             sm.count = h[e];
           }
@@ -170,7 +171,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ s, int n, int
     }
   }
   const uint32_t packed = (gt << 16) | eq;  // both < 65536 (n <= 65535)
-  const uint32_t incl = wave_incl_scan_u32(packed, lane);
+  const uint32_t incl = wave_scan_incl(packed);
   if (lane == kWave - 1) sm.scan[wid] = incl;
   __syncthreads();
   uint32_t before = incl - packed;

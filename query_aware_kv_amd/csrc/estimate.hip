@@ -29,26 +29,25 @@ estimate_kernel(const uint16_t* __restrict__ q,
   if (row >= rows_per_head * Hkv) return;  // whole 16-lane rows exit together
   const int g = row % Hkv;
   const int jb0 = row / Hkv;
-  const int L = seq_lens[b];
-  const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
-
-  float qf[G][8];
-  est_load_q<T, G>(q, ((int64_t)b * Hkv + g) * G, c, qf);
   const int32_t* pt_row = page_table + (int64_t)b * max_pages;
   float* srow = scores + ((int64_t)b * Hkv + g) * max_pages;
+  // The length, the first table entries and q are independent loads.
+  int ent[kEstPages];
+  est_table(pt_row, max_pages, jb0 * kEstPages, ent);
+  const int L = seq_lens[b];
+  float qf[G][8];
+  est_load_q<T, G>(q, ((int64_t)b * Hkv + g) * G, c, qf);
+  const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
 
-  int pid[kEstPages];
-  est_page_ids(pt_row, n, jb0 * kEstPages, num_pool_pages, pid);
   for (int jb = jb0; jb * kEstPages < max_pages; jb += rows_per_head) {
+    int pid[kEstPages];
+    est_page_ids(ent, n, jb * kEstPages, num_pool_pages, pid);
     uint4 lo[kEstPages], hi[kEstPages];
     est_load_meta(kmin, kmax, pid, Hkv, g, c, lo, hi);
-    int cur[kEstPages];
-#pragma unroll
-    for (int u = 0; u < kEstPages; ++u) cur[u] = pid[u];
-    est_page_ids(pt_row, n, (jb + rows_per_head) * kEstPages, num_pool_pages, pid);
+    est_table(pt_row, max_pages, (jb + rows_per_head) * kEstPages, ent);  // prefetch
     float s[kEstPages];
-    est_score<T, G>(qf, cur, lo, hi, s);
-    est_store(srow, jb * kEstPages, max_pages, c, cur, s);
+    est_score<T, G>(qf, pid, lo, hi, s);
+    est_store(srow, jb * kEstPages, max_pages, c, pid, s);
   }
 }
 

@@ -108,8 +108,9 @@ __device__ __forceinline__ void est_item(const StepArgs& a, uint32_t t, StepSmem
   if (j0 < a.max_pages) {
     float qf[G][8];
     est_load_q<T, G>(a.q, (int64_t)row * G, c, qf);
-    int pid[kEstPages];
-    est_page_ids(pt_row, n, j0, a.num_pool_pages, pid);
+    int ent[kEstPages], pid[kEstPages];
+    est_table(pt_row, a.max_pages, j0, ent);
+    est_page_ids(ent, n, j0, a.num_pool_pages, pid);
     uint4 lo[kEstPages], hi[kEstPages];
     est_load_meta(a.kmin, a.kmax, pid, a.Hkv, g, c, lo, hi);
     float s[kEstPages];
@@ -124,7 +125,9 @@ __device__ __forceinline__ void est_item(const StepArgs& a, uint32_t t, StepSmem
   if (!flag) return;
   // Last estimate item of this row: select now.
   fence_acquire();
-  topk_row<kStepThreads, KPT>(srow, n, a.k, a.sel + (int64_t)row * a.k, pt_row,
+  float v[KPT];
+  topk_load<kStepThreads, KPT>(srow, n, v);
+  topk_row<kStepThreads, KPT>(v, n, a.k, a.sel + (int64_t)row * a.k, pt_row,
                               a.phys + (int64_t)row * a.k, sm.topk);
   fence_release();
   __syncthreads();

@@ -14,10 +14,11 @@ topk_kernel(const float* __restrict__ scores,
   __shared__ TopkSmem<BLOCK> sm;
   const int rowid = blockIdx.x;  // b * Hkv + g
   const int b = rowid / Hkv;
+  float v[KPT];  // issued together with the length load
+  topk_load<BLOCK, KPT>(scores + (int64_t)rowid * max_pages, max_pages, v);
   const int L = seq_lens[b];
   const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
-  topk_row<BLOCK, KPT>(scores + (int64_t)rowid * max_pages, n, k,
-                       sel + (int64_t)rowid * k, nullptr, nullptr, sm);
+  topk_row<BLOCK, KPT>(v, n, k, sel + (int64_t)rowid * k, nullptr, nullptr, sm);
 }
 
 template <int BLOCK, int KPT>
