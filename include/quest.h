@@ -148,11 +148,8 @@ QUEST_API quest_status quest_topk_pages(
  * listed pages must be distinct and < n_b.  Accumulation is float32
  * (online softmax, split over pages, merged in float32).
  * `workspace` (device, >= quest_workspace_size(kv, k_pages) bytes) holds
- * per-split partial results and one split counter per (request, kv-head):
- * its bytes must be ZERO before its first use (e.g. allocated zeroed), and
- * every call leaves the counters at zero again.  The workgroup that
- * completes a row's last split merges the row (no workgroup waits for
- * another).  A workspace serves one stream at a time.
+ * per-split partial results; its contents on entry do not matter.  A
+ * workspace serves one stream at a time.
  */
 QUEST_API quest_status quest_sparse_decode_attn(
     const quest_paged_kv* kv, const void* q, const void* k_pool,
@@ -164,9 +161,8 @@ QUEST_API quest_status quest_sparse_decode_attn(
  * Dense decode attention over all L_b tokens (the in-library baseline).
  * "The Memory Bandwidth Bottleneck of Long-Context Decoding" in [G]:
  *   out[b][h] = softmax(sm_scale * q K^T) V over every token of request b.
- * Same kernels, arithmetic and workspace rules as the sparse call (zeroed
- * before first use, left zeroed); the workspace must hold
- * quest_workspace_size(kv, max_pages_per_seq) bytes.
+ * Same kernels, arithmetic and workspace rules as the sparse call; the
+ * workspace must hold quest_workspace_size(kv, max_pages_per_seq) bytes.
  */
 QUEST_API quest_status quest_decode_attn(
     const quest_paged_kv* kv, const void* q, const void* k_pool,

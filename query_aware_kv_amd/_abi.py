@@ -61,7 +61,7 @@ class QuestError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built: run `python -m query_aware_kv_amd.build` "
+            f"{LIB_PATH} is not built: run `python query_aware_kv_amd/build.py` "
             "(or __graft_entry__.build()) first; there is no fallback path")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p

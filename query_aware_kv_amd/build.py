@@ -1,6 +1,6 @@
 """Build libquest.so (gfx950 only) in-tree with hipcc.
 
-    python -m query_aware_kv_amd.build          # or __graft_entry__.build()
+    python query_aware_kv_amd/build.py          # or __graft_entry__.build()
 
 Objects go to query_aware_kv_amd/_build/, the library to
 query_aware_kv_amd/libquest.so.  Every call compiles from scratch.

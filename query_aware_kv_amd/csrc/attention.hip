@@ -6,9 +6,7 @@
 // skipped) or 0..n_b-1 -- and issues all of their K and V loads before any
 // arithmetic (PPW * 8 KiB in flight per wave).  The four waves meet in LDS;
 // with one split per row the workgroup writes the output directly, otherwise
-// a partial (o[128], M, den) per query head; the workgroup that completes a
-// row's last split (a per-row counter in the workspace elects it; nobody
-// waits) merges the row's partials and resets the counter.
+// a partial (o[128], M, den) per query head, which the merge kernel combines.
 #include "dev_attn.h"
 #include "launch.h"
 
@@ -24,13 +22,9 @@ attn_split_kernel(const uint16_t* __restrict__ q,
                   const int32_t* __restrict__ seq_lens,
                   const int32_t* __restrict__ sel, int list_len, int Hkv,
                   int max_pages, int num_pool_pages, float qscale,
-                  float* __restrict__ out, uint32_t* __restrict__ done,
-                  float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  __shared__ union {
-    AttnSmem<G> attn;
-    MergeSmem merge;
-  } sm;
-  __shared__ uint32_t sh_last;
+                  float* __restrict__ out, float* __restrict__ ws_o,
+                  float* __restrict__ ws_ml) {
+  __shared__ AttnSmem<G> sm;
   const int unit = blockIdx.y;  // b * Hkv + g
   const int b = unit / Hkv, g = unit - (unit / Hkv) * Hkv;
   const int split = blockIdx.x, nsplit = gridDim.x;
@@ -73,14 +67,14 @@ attn_split_kernel(const uint16_t* __restrict__ q,
     if (pj[pi] >= 0)
       attn_page<T, G>(st, qf, kx[pi], vx[pi], min(kPageSize, L - pj[pi] * kPageSize), r);
   attn_combine_rows(st);
-  attn_stage_wave(st, sm.attn, wid, r, c);
+  attn_stage_wave(st, sm, wid, r, c);
   __syncthreads();
 
   const int Hq = Hkv * G;
   for (int idx = tid; idx < G * kHeadDim; idx += 256) {
     const int h = idx / kHeadDim, ch = idx - h * kHeadDim;
     float M, den, num;
-    attn_wg_partial(sm.attn, h, ch, M, den, num);
+    attn_wg_partial(sm, h, ch, M, den, num);
     const int64_t qh = (int64_t)b * Hq + g * G + h;
     if (nsplit == 1) {
       out[qh * kHeadDim + ch] = den > 0.f ? num / den : 0.f;
@@ -93,24 +87,19 @@ attn_split_kernel(const uint16_t* __restrict__ q,
       }
     }
   }
-  if (nsplit == 1) return;
-  // The workgroup that completes a row's last split merges the row.  No
-  // workgroup ever waits for another: the counter only elects the merger.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid == 0)
-    sh_last = __hip_atomic_fetch_add(&done[unit], 1u, __ATOMIC_ACQ_REL,
-                                     __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsplit - 1);
-  __syncthreads();
-  if (!sh_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int h = 0; h < G; ++h) {
-    const int64_t qh = (int64_t)b * Hq + g * G + h;
-    merge_splits(ws_o + qh * nsplit * kHeadDim, ws_ml + qh * nsplit * 2, nsplit,
-                 out + qh * kHeadDim, sm.merge);
-    __syncthreads();
-  }
-  if (tid == 0) done[unit] = 0;  // leave the counter at zero for the next call
+}
+
+// One workgroup per (request, query head): combine its splits.  A separate
+// launch: the kernel boundary publishes every split's partials, which is far
+// cheaper here than per-workgroup L2 write-backs for an in-kernel hand-off.
+__global__ void __launch_bounds__(256)
+attn_merge_kernel(const float* __restrict__ ws_o,
+                  const float* __restrict__ ws_ml, int nsplit,
+                  float* __restrict__ out) {
+  __shared__ MergeSmem sm;
+  const int64_t qh = blockIdx.x;
+  merge_splits(ws_o + qh * nsplit * kHeadDim, ws_ml + qh * nsplit * 2, nsplit,
+               out + qh * kHeadDim, sm);
 }
 
 int max_ppw(int G) { return G == 1 ? 4 : G <= 4 ? 2 : 1; }
@@ -138,14 +127,14 @@ template <DType T, int G, int PPW>
 void launch_split(const quest_paged_kv& kv, const void* q, const void* k_pool,
                   const void* v_pool, const int32_t* page_table,
                   const int32_t* seq_lens, const int32_t* sel, int list_len,
-                  float qscale, float* out, uint32_t* done, float* ws_o,
-                  float* ws_ml, int nsplit, hipStream_t stream) {
+                  float qscale, float* out, float* ws_o, float* ws_ml,
+                  int nsplit, hipStream_t stream) {
   dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
   attn_split_kernel<T, G, PPW><<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), page_table, seq_lens, sel,
       list_len, kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages,
-      qscale, out, done, ws_o, ws_ml);
+      qscale, out, ws_o, ws_ml);
 }
 
 template <DType T>
@@ -153,12 +142,10 @@ void dispatch(int G, int ppw, const quest_paged_kv& kv, const void* q,
               const void* k_pool, const void* v_pool,
               const int32_t* page_table, const int32_t* seq_lens,
               const int32_t* sel, int list_len, float qscale, float* out,
-              uint32_t* done, float* ws_o, float* ws_ml, int nsplit,
-              hipStream_t stream) {
+              float* ws_o, float* ws_ml, int nsplit, hipStream_t stream) {
 #define QUEST_SPLIT(GG, PP)                                                   \
   launch_split<T, GG, PP>(kv, q, k_pool, v_pool, page_table, seq_lens, sel,  \
-                          list_len, qscale, out, done, ws_o, ws_ml, nsplit,   \
-                          stream)
+                          list_len, qscale, out, ws_o, ws_ml, nsplit, stream)
   if (G == 1) {
     if (ppw == 4) QUEST_SPLIT(1, 4);
     else if (ppw == 2) QUEST_SPLIT(1, 2);
@@ -176,17 +163,15 @@ void dispatch(int G, int ppw, const quest_paged_kv& kv, const void* q,
 }
 
 struct WsLayout {
-  size_t off_o, off_ml, bytes;
+  size_t off_ml, bytes;
 };
 
-// [per-row split counters][partial o][partial (M, den)], 256-byte aligned.
+// [partial o][partial (M, den)], 256-byte aligned.
 WsLayout ws_layout(const quest_paged_kv& kv, int nsplit) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t units = (size_t)kv.batch * kv.num_kv_heads;
   const size_t slots = (size_t)kv.batch * kv.num_q_heads * nsplit;
   WsLayout w;
-  w.off_o = al(units * sizeof(uint32_t));
-  w.off_ml = w.off_o + al(slots * kHeadDim * sizeof(float));
+  w.off_ml = al(slots * kHeadDim * sizeof(float));
   w.bytes = w.off_ml + al(slots * 2 * sizeof(float));
   return w;
 }
@@ -212,18 +197,20 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
   const Plan pl = plan(kv, list_len);
   const WsLayout w = ws_layout(kv, pl.nsplit);
   char* ws = static_cast<char*>(workspace);
-  uint32_t* done = ws ? reinterpret_cast<uint32_t*>(ws) : nullptr;
-  float* ws_o = ws ? reinterpret_cast<float*>(ws + w.off_o) : nullptr;
+  float* ws_o = reinterpret_cast<float*>(ws);
   float* ws_ml = ws ? reinterpret_cast<float*>(ws + w.off_ml) : nullptr;
   const float qscale = sm_scale * kLog2e;
   if (kv.dtype == QUEST_F16)
     dispatch<DType::F16>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                         sel, list_len, qscale, out, done, ws_o, ws_ml, pl.nsplit,
+                         sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit,
                          stream);
   else
     dispatch<DType::BF16>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                          sel, list_len, qscale, out, done, ws_o, ws_ml, pl.nsplit,
+                          sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit,
                           stream);
+  if (pl.nsplit > 1)
+    attn_merge_kernel<<<kv.batch * kv.num_q_heads, 256, 0, stream>>>(
+        ws_o, ws_ml, pl.nsplit, out);
   return hipGetLastError();
 }
 

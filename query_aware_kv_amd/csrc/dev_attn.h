@@ -181,54 +181,60 @@ __device__ __forceinline__ void attn_wg_partial(const AttnSmem<G>& sm, int h, in
 }
 
 struct MergeSmem {
-  float red[kAttnWaves];
-  float half[kHeadDim];
-  float M, den;
+  float m[kHeadDim], num[kHeadDim], den[kHeadDim];
 };
 
 // Merge nsplit partials of one (request, query head) into out_row[128] with
 // a 256-thread workgroup: partial s is (o[s*128 .. +128], ml[2s] = M,
-// ml[2s+1] = den).  All loads of a phase are independent, so they overlap.
+// ml[2s+1] = den).  Thread (half, ch) folds channel ch of the splits of its
+// parity with a running max (online softmax), 8 splits per chunk whose
+// loads are all issued together -- one memory round trip per chunk; the
+// two halves then meet in LDS.
 __device__ __forceinline__ void merge_splits(const float* __restrict__ o,
                                              const float* __restrict__ ml,
                                              int nsplit, float* __restrict__ out_row,
                                              MergeSmem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  float mloc = -INFINITY;
-  for (int s = tid; s < nsplit; s += 256) mloc = fmaxf(mloc, ml[2 * s]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, shfl_xor_f(mloc, off));
-  if (lane == 0) sm.red[wid] = mloc;
-  __syncthreads();
-  float M = sm.red[0];
-#pragma unroll
-  for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, sm.red[w]);
-  float dloc = 0.f;
-  for (int s = tid; s < nsplit; s += 256) dloc += ml[2 * s + 1] * exp2_or_zero(ml[2 * s], M);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) dloc += shfl_xor_f(dloc, off);
-  __syncthreads();
-  if (lane == 0) sm.red[wid] = dloc;
+  constexpr int kChunk = 8;
+  const int tid = threadIdx.x;
   const int ch = tid & (kHeadDim - 1), half = tid >> 7;
-  float num = 0.f;
-  int s = half;
-  for (; s + 6 < nsplit; s += 8) {
-    float w[4], x[4];
+  float mr = -INFINITY, num = 0.f, den = 0.f;
+  for (int s0 = half; s0 < nsplit; s0 += 2 * kChunk) {
+    float w[kChunk], l[kChunk], x[kChunk];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      w[u] = ml[2 * (s + 2 * u)];
-      x[u] = o[(int64_t)(s + 2 * u) * kHeadDim + ch];
+    for (int u = 0; u < kChunk; ++u) {
+      const int s = s0 + 2 * u;
+      const bool ok = s < nsplit;
+      w[u] = ok ? ml[2 * s] : -INFINITY;
+      l[u] = ok ? ml[2 * s + 1] : 0.f;
+      x[u] = ok ? o[(int64_t)s * kHeadDim + ch] : 0.f;
     }
+    float mc = mr;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) num += x[u] * exp2_or_zero(w[u], M);
+    for (int u = 0; u < kChunk; ++u) mc = fmaxf(mc, w[u]);
+    const float sc = exp2_or_zero(mr, mc);
+    num *= sc;
+    den *= sc;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const float e = exp2_or_zero(w[u], mc);
+      num += x[u] * e;
+      den += l[u] * e;
+    }
+    mr = mc;
   }
-  for (; s < nsplit; s += 2) num += o[(int64_t)s * kHeadDim + ch] * exp2_or_zero(ml[2 * s], M);
-  if (half == 1) sm.half[ch] = num;
+  if (half == 1) {
+    sm.m[ch] = mr;
+    sm.num[ch] = num;
+    sm.den[ch] = den;
+  }
   __syncthreads();
   if (half == 0) {
-    const float den = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
-    num += sm.half[ch];
-    out_row[ch] = den > 0.f ? num / den : 0.f;
+    const float mo = sm.m[ch];
+    const float M = fmaxf(mr, mo);
+    const float sa = exp2_or_zero(mr, M), sb = exp2_or_zero(mo, M);
+    const float d = den * sa + sm.den[ch] * sb;
+    const float nm = num * sa + sm.num[ch] * sb;
+    out_row[ch] = d > 0.f ? nm / d : 0.f;
   }
 }
 

@@ -299,26 +299,24 @@ def test_sparse_selection_order_irrelevant():
     assert np.max(np.abs(o2.cpu().numpy() - out)) <= 1e-5
 
 
-def test_split_counters_return_to_zero():
-    """The attention calls elect each row's merger with a per-row counter in
-    the workspace; after every call the counters are zero again, and a
-    reused workspace gives identical results."""
+def test_workspace_reuse_is_stateless():
+    """Reusing one workspace across calls (and filling it with garbage in
+    between) changes nothing: the attention calls keep no state in it."""
     wl, c = make("gqa4_f16")
     kv = c["kv"]
     kmin, kmax = C.gpu_meta(c)
     step = qa.SparseDecodeStep(kv, wl.k_pages, SM)
     dense = qa.DenseDecode(kv, SM)
-    units = kv.batch * kv.num_kv_heads
     args = (c["q"], c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"],
             c["seq_lens"])
     first = step(*args).clone()
     d_first = dense(c["q"], c["k_pool"], c["v_pool"], c["page_table"],
                     c["seq_lens"]).clone()
-    for _ in range(10):
+    for i in range(5):
+        step.workspace.fill_(0xA5 + i)
+        dense.workspace.fill_(0x5A + i)
         step(*args)
         dense(c["q"], c["k_pool"], c["v_pool"], c["page_table"], c["seq_lens"])
         torch.cuda.synchronize()
         assert torch.equal(step.out, first)
         assert torch.equal(dense.out, d_first)
-        assert int(step.workspace[:4 * units].view(torch.int32).abs().sum()) == 0
-        assert int(dense.workspace[:4 * units].view(torch.int32).abs().sum()) == 0
