@@ -3,7 +3,8 @@
     python bench.py [--steps K] [--warmup W] [--workload longchat]
 
 A "step" is one pass of the whole hot path -- quest_estimate ->
-quest_topk_pages -> quest_sparse_decode_attn -- over one LongChat-7B-shaped
+quest_topk_sparse_decode_attn (Top-K + sparse attention + split merge) --
+replayed as a HIP graph, over one LongChat-7B-shaped
 layer (32 heads, 32K context, 2048-token budget, fp16).  Inputs are seeded
 synthetic caches drawn on the GPU and resident in HBM before timing starts.
 Consecutive steps rotate over several independent caches whose touched bytes
@@ -120,68 +121,99 @@ def run_gpu(args):
         insts.append(c)
     torch.cuda.synchronize()
     kv = insts[0]["kv"]
+    k = base.k_pages
     sm = 1.0 / math.sqrt(128)
-    seps = [qa.SparseDecodeStep(kv, base.k_pages, sm) for _ in range(rot)]
-    dense = qa.DenseDecode(kv, sm)
+    steps = [qa.SparseDecodeStep(kv, k, sm) for _ in range(rot)]
+    denses = [qa.DenseDecode(kv, sm) for _ in range(rot)]
     stream = torch.cuda.current_stream()
 
-    def sep_step(i):
-        c = insts[i % rot]
-        seps[i % rot](c["q"], c["k_pool"], c["v_pool"], c["kmin"], c["kmax"],
-                      c["page_table"], c["seq_lens"])
+    def step_call(i):
+        c = insts[i]
+        steps[i](c["q"], c["k_pool"], c["v_pool"], c["kmin"], c["kmax"],
+                 c["page_table"], c["seq_lens"])
 
-    def dense_step(i):
-        c = insts[i % rot]
-        dense(c["q"], c["k_pool"], c["v_pool"], c["page_table"], c["seq_lens"])
+    def dense_call(i):
+        c = insts[i]
+        denses[i](c["q"], c["k_pool"], c["v_pool"], c["page_table"], c["seq_lens"])
 
-    def timed(fn, k, w):
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    for i in range(rot):                 # eager warm-up before capture
+        step_call(i)
+        dense_call(i)
+    torch.cuda.synchronize()
+    step_graphs = [capture(lambda i=i: step_call(i)) for i in range(rot)]
+    dense_graphs = [capture(lambda i=i: dense_call(i)) for i in range(rot)]
+
+    def timed(fn, n, w):
         for i in range(w):
-            fn(i)
+            fn(i % rot)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(k):
-            fn(w + i)
+        for i in range(n):
+            fn(i % rot)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / k * 1e6
+        return (time.perf_counter() - t0) / n * 1e6
 
-    us_step = timed(sep_step, args.steps, args.warmup)
+    us_step = timed(lambda i: step_graphs[i].replay(), args.steps, args.warmup)
+    us_eager = timed(step_call, args.steps, args.warmup)
     us_dense = (float("nan") if args.no_dense else
-                timed(dense_step, max(10, args.steps // 4), args.warmup))
+                timed(lambda i: dense_graphs[i].replay(), max(20, args.steps // 4),
+                      args.warmup))
 
-    # HIP-event kernel times on the launch stream over K more steps
-    t_est, t_topk, t_attn = (KernelTimer(torch, stream) for _ in range(3))
-    for i in range(args.steps):
-        c = insts[i % rot]
-        st = seps[i % rot]
-        t_est.around(lambda: qa.quest_estimate(
-            kv, c["q"], c["kmin"], c["kmax"], c["page_table"], c["seq_lens"],
-            st.scores))
-        t_topk.around(lambda: qa.quest_topk_pages(
-            kv, st.scores, c["seq_lens"], st.k_pages, st.sel))
-        t_attn.around(lambda: qa.quest_sparse_decode_attn(
+    # Per-call device time: HIP events on the launch stream around replays of
+    # a graph holding one launch of the call per cache (8 back to back).
+    def call_us(call, reps=max(10, args.steps // rot)):
+        g = capture(lambda: [call(i) for i in range(rot)])
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * rot)
+
+    def est(i):
+        c, st = insts[i], steps[i]
+        qa.quest_estimate(kv, c["q"], c["kmin"], c["kmax"], c["page_table"],
+                          c["seq_lens"], st.scores)
+
+    def topk_attn(i):
+        c, st = insts[i], steps[i]
+        qa.quest_topk_sparse_decode_attn(
             kv, c["q"], c["k_pool"], c["v_pool"], c["page_table"],
-            c["seq_lens"], st.sel, st.k_pages, sm, st.out, st.workspace))
-    us_est, us_topk, us_attn = t_est.mean_us(), t_topk.mean_us(), t_attn.mean_us()
+            c["seq_lens"], st.scores, k, sm, st.sel, st.out, st.workspace)
+
+    us_est = call_us(est)
+    us_ta = call_us(topk_attn)
 
     # algorithmic bytes from the selections actually made
-    sels = [st.sel.cpu().numpy() for st in seps]
+    sels = [st.sel.cpu().numpy() for st in steps]
     lens = [int(x) for x in insts[0]["seq_lens"].cpu()]
-    bstep = [step_bytes(lens, kv.num_kv_heads, kv.num_q_heads, base.k_pages,
-                        sel=s) for s in sels]
-    avg = {k: sum(b[k] for b in bstep) / len(bstep) for k in bstep[0]}
+    bstep = [step_bytes(lens, kv.num_kv_heads, kv.num_q_heads, k, sel=s)
+             for s in sels]
+    avg = {key: sum(b[key] for b in bstep) / len(bstep) for key in bstep[0]}
+    B = len(lens)
     est_bytes = avg["meta"] + avg["q"] + avg["table"] + \
-        kv.num_kv_heads * kv.max_pages_per_seq * 4 * len(lens)
-    attn_bytes = avg["kv"] + avg["q"] + avg["out"] + \
-        kv.num_kv_heads * base.k_pages * 4 * len(lens)
-    kern = {"quest_estimate (estimate_kernel)": (us_est, est_bytes),
-            "quest_sparse_decode_attn (attn_split_kernel + attn_merge_kernel)":
-                (us_attn, attn_bytes)}
-    dom = max(kern, key=lambda k: kern[k][0])
-    d_us, d_bytes = kern[dom]
+        kv.num_kv_heads * kv.max_pages_per_seq * 4 * B
+    ta_bytes = avg["kv"] + avg["q"] + avg["out"] + \
+        kv.num_kv_heads * (kv.max_pages_per_seq + k) * 4 * B
+    calls = {"quest_estimate [estimate_kernel]": (us_est, est_bytes),
+             "quest_topk_sparse_decode_attn [topk_attn_kernel + attn_merge_kernel]":
+                 (us_ta, ta_bytes)}
+    dom = max(calls, key=lambda c: calls[c][0])
+    d_us, d_bytes = calls[dom]
     achieved = d_bytes / (d_us * 1e-6) / 1e9
     return dict(
-        us_step=us_step, us_dense=us_dense, bytes=avg, us_est=us_est,
-        us_topk=us_topk, us_attn=us_attn,
+        us_step=us_step, us_eager=us_eager, us_dense=us_dense, bytes=avg,
+        calls={c: round(v[0], 3) for c, v in calls.items()},
         roofline={"bound": "hbm", "achieved": round(achieved, 1),
                   "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -189,7 +221,7 @@ def run_gpu(args):
                   "bytes_per_launch": int(d_bytes)},
         dense_bytes=dense_bytes(lens, kv.num_kv_heads, kv.num_q_heads),
         gpu=torch.cuda.get_device_name(0), insts=insts, kv=kv,
-        k_pages=base.k_pages, sm=sm)
+        k_pages=k, sm=sm)
 
 
 # ------------------------------------------------------------- CPU oracle
@@ -282,9 +314,10 @@ def main():
         "dense_us_per_step": round(g["us_dense"], 3),
         "speedup_vs_dense": round(g["us_dense"] / us, 3),
         "dense_effective_GBps": round(g["dense_bytes"] / (g["us_dense"] * 1e-6) / 1e9, 1),
-        "kernel_us": {"quest_estimate": round(g["us_est"], 3),
-                      "quest_topk_pages": round(g["us_topk"], 3),
-                      "quest_sparse_decode_attn": round(g["us_attn"], 3)},
+        "timing": "HIP-graph replay of the step (one graph per cache, 8 caches "
+                  "rotated); eager = the same calls issued from Python",
+        "eager_us_per_step": round(g["us_eager"], 3),
+        "call_us": g["calls"],
         "roofline": g["roofline"],
         "gpu": g["gpu"],
     }

@@ -158,6 +158,22 @@ QUEST_API quest_status quest_sparse_decode_attn(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * quest_topk_pages followed by quest_sparse_decode_attn, in one launch (plus
+ * the split merge): the same outputs sel_pages and out, bit for bit.  Every
+ * attention workgroup of a (request, kv-head) row recomputes the row's exact
+ * Top-K from `scores` (float32 [batch][Hkv][max_pages_per_seq], e.g. from
+ * quest_estimate) and keeps it in LDS, so no workgroup waits for another and
+ * the selection makes no round trip through memory.  Requires
+ * max_pages_per_seq <= 8192 and k_pages <= 8192.  Workspace as for
+ * quest_sparse_decode_attn with the same k_pages.
+ */
+QUEST_API quest_status quest_topk_sparse_decode_attn(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const float* scores, int32_t k_pages, float sm_scale, int32_t* sel_pages,
+    float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Dense decode attention over all L_b tokens (the in-library baseline).
  * "The Memory Bandwidth Bottleneck of Long-Context Decoding" in [G]:
  *   out[b][h] = softmax(sm_scale * q K^T) V over every token of request b.

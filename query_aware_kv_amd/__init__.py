@@ -18,7 +18,8 @@ from ._abi import (  # noqa: F401
     QUEST_ERR_WORKSPACE_TOO_SMALL, paged_kv, paged_kv_like,
     quest_decode_attn, quest_estimate, quest_sparse_decode_attn,
     quest_sparse_decode_step, quest_step_workspace_size, quest_topk_pages,
-    quest_update_page_meta, quest_workspace_size,
+    quest_topk_sparse_decode_attn, quest_update_page_meta,
+    quest_workspace_size,
 )
 
 HEAD_DIM = 128
@@ -41,13 +42,18 @@ def alloc_meta(kv: PagedKV, device="cuda"):
             torch.empty(shape, dtype=kv.torch_dtype, device=device))
 
 
+TOPK_ATTN_MAX_PAGES = 8192
+
+
 class SparseDecodeStep:
     """Buffers and call sequence of one sparse decode step for a fixed
-    geometry: quest_estimate -> quest_topk_pages -> quest_sparse_decode_attn.
+    geometry: quest_estimate, then quest_topk_sparse_decode_attn (Top-K and
+    attention in one launch) -- or, with ``fused_topk=False`` or beyond its
+    size limit, quest_topk_pages then quest_sparse_decode_attn.
     """
 
     def __init__(self, kv: PagedKV, k_pages: int, sm_scale: float | None = None,
-                 device="cuda"):
+                 device="cuda", fused_topk: bool = True):
         self.kv = kv
         self.k_pages = int(k_pages)
         self.sm_scale = default_sm_scale(kv.head_dim) if sm_scale is None else sm_scale
@@ -59,11 +65,20 @@ class SparseDecodeStep:
         self.out = torch.empty(B, Hq, kv.head_dim, dtype=torch.float32,
                                device=device)
         self.workspace = alloc_workspace(kv, self.k_pages, device)
+        self.fused_topk = bool(fused_topk) and \
+            kv.max_pages_per_seq <= TOPK_ATTN_MAX_PAGES and \
+            self.k_pages <= TOPK_ATTN_MAX_PAGES
 
     def __call__(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_lens,
                  stream=None) -> torch.Tensor:
         quest_estimate(self.kv, q, kmin, kmax, page_table, seq_lens,
                        self.scores, stream)
+        if self.fused_topk:
+            quest_topk_sparse_decode_attn(
+                self.kv, q, k_pool, v_pool, page_table, seq_lens, self.scores,
+                self.k_pages, self.sm_scale, self.sel, self.out,
+                self.workspace, stream)
+            return self.out
         quest_topk_pages(self.kv, self.scores, seq_lens, self.k_pages,
                          self.sel, stream)
         quest_sparse_decode_attn(self.kv, q, k_pool, v_pool, page_table,

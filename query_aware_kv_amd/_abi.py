@@ -79,6 +79,8 @@ def _load():
         "quest_sparse_decode_step": [KV, P, P, P, P, P, P, P, I, ctypes.c_float,
                                      P, P, P, P, ctypes.c_size_t, P],
         "quest_step_workspace_size": [KV, I, ctypes.POINTER(ctypes.c_size_t)],
+        "quest_topk_sparse_decode_attn": [KV, P, P, P, P, P, P, I, ctypes.c_float,
+                                          P, P, P, ctypes.c_size_t, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -276,3 +278,26 @@ def quest_step_workspace_size(kv: PagedKV, k_pages: int) -> int:
     _check(LIB.quest_step_workspace_size(ctypes.byref(kv), int(k_pages),
                                          ctypes.byref(n)))
     return int(n.value)
+
+
+def quest_topk_sparse_decode_attn(kv: PagedKV, q, k_pool, v_pool, page_table,
+                                  seq_lens, scores, k_pages: int,
+                                  sm_scale: float, sel_pages, out, workspace,
+                                  stream=None) -> None:
+    dt = kv.torch_dtype
+    i32 = torch.int32
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.quest_topk_sparse_decode_attn(
+        ctypes.byref(kv),
+        _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv)),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv)),
+        _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
+        _ptr(seq_lens, "seq_lens", i32, (kv.batch,)),
+        _ptr(scores, "scores", torch.float32,
+             (kv.batch, kv.num_kv_heads, kv.max_pages_per_seq)),
+        int(k_pages), float(sm_scale),
+        _ptr(sel_pages, "sel_pages", i32, (kv.batch, kv.num_kv_heads, k_pages)),
+        _ptr(out, "out", torch.float32, (kv.batch, kv.num_q_heads, kv.head_dim)),
+        _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes),
+        _stream(stream)))

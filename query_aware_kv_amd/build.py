@@ -33,7 +33,7 @@ COMMON_FLAGS = [
 ]
 
 SOURCES = ["api.cpp", "meta.hip", "estimate.hip", "topk.hip", "attention.hip",
-           "step.hip"]
+           "topk_attn.hip", "step.hip"]
 
 
 def _compile(src: str) -> str:

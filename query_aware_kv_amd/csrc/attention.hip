@@ -104,14 +104,13 @@ attn_merge_kernel(const float* __restrict__ ws_o,
 
 int max_ppw(int G) { return G == 1 ? 4 : G <= 4 ? 2 : 1; }
 
-struct Plan {
-  int ppw;
-  int nsplit;
-};
+using Plan = AttnPlan;
+
+}  // namespace
 
 // Pages per wave: as many as the group size allows while the grid keeps at
 // least ~1024 workgroups (4 per CU) to spread the loads over all 256 CUs.
-Plan plan(const quest_paged_kv& kv, int list_len) {
+AttnPlan attention_plan(const quest_paged_kv& kv, int list_len) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
   const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
   int ppw = 1;
@@ -122,6 +121,21 @@ Plan plan(const quest_paged_kv& kv, int list_len) {
   const int nsplit = (list_len + kAttnWaves * ppw - 1) / (kAttnWaves * ppw);
   return {ppw, nsplit < 1 ? 1 : nsplit};
 }
+
+// Workspace: [partial o: slots x 128 floats][partial (M, den): slots x 2],
+// the second part 256-byte aligned.
+size_t attention_ml_offset(size_t slots) {
+  return ((slots * kHeadDim * sizeof(float) + 255) & ~(size_t)255) / sizeof(float);
+}
+
+void launch_merge(const quest_paged_kv& kv, const float* ws_o,
+                  const float* ws_ml, int nsplit, float* out,
+                  hipStream_t stream) {
+  attn_merge_kernel<<<kv.batch * kv.num_q_heads, 256, 0, stream>>>(
+      ws_o, ws_ml, nsplit, out);
+}
+
+namespace {
 
 template <DType T, int G, int PPW>
 void launch_split(const quest_paged_kv& kv, const void* q, const void* k_pool,
@@ -162,20 +176,6 @@ void dispatch(int G, int ppw, const quest_paged_kv& kv, const void* q,
 #undef QUEST_SPLIT
 }
 
-struct WsLayout {
-  size_t off_ml, bytes;
-};
-
-// [partial o][partial (M, den)], 256-byte aligned.
-WsLayout ws_layout(const quest_paged_kv& kv, int nsplit) {
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t slots = (size_t)kv.batch * kv.num_q_heads * nsplit;
-  WsLayout w;
-  w.off_ml = al(slots * kHeadDim * sizeof(float));
-  w.bytes = w.off_ml + al(slots * 2 * sizeof(float));
-  return w;
-}
-
 }  // namespace
 
 bool attention_supported(int group) {
@@ -183,9 +183,10 @@ bool attention_supported(int group) {
 }
 
 size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len) {
-  const Plan pl = plan(kv, list_len);
+  const Plan pl = attention_plan(kv, list_len);
   if (pl.nsplit == 1) return 0;
-  return ws_layout(kv, pl.nsplit).bytes;
+  const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
+  return (attention_ml_offset(slots) + slots * 2) * sizeof(float);
 }
 
 hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
@@ -194,11 +195,10 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
                             const int32_t* sel, int list_len, float sm_scale,
                             float* out, void* workspace, hipStream_t stream) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
-  const Plan pl = plan(kv, list_len);
-  const WsLayout w = ws_layout(kv, pl.nsplit);
-  char* ws = static_cast<char*>(workspace);
-  float* ws_o = reinterpret_cast<float*>(ws);
-  float* ws_ml = ws ? reinterpret_cast<float*>(ws + w.off_ml) : nullptr;
+  const Plan pl = attention_plan(kv, list_len);
+  const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_ml = ws_o ? ws_o + attention_ml_offset(slots) : nullptr;
   const float qscale = sm_scale * kLog2e;
   if (kv.dtype == QUEST_F16)
     dispatch<DType::F16>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
@@ -208,9 +208,7 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
     dispatch<DType::BF16>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
                           sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit,
                           stream);
-  if (pl.nsplit > 1)
-    attn_merge_kernel<<<kv.batch * kv.num_q_heads, 256, 0, stream>>>(
-        ws_o, ws_ml, pl.nsplit, out);
+  if (pl.nsplit > 1) launch_merge(kv, ws_o, ws_ml, pl.nsplit, out, stream);
   return hipGetLastError();
 }
 

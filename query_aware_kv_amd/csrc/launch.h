@@ -35,6 +35,15 @@ hipError_t launch_topk(const quest_paged_kv& kv, const float* scores,
                        hipStream_t stream);
 
 // Attention (sparse when sel != nullptr, else dense over all pages).
+struct AttnPlan {
+  int ppw;     // pages per wave
+  int nsplit;  // workgroups (splits) per (request, kv-head) row
+};
+AttnPlan attention_plan(const quest_paged_kv& kv, int list_len);
+size_t attention_ml_offset(size_t slots);  // in floats, into the workspace
+void launch_merge(const quest_paged_kv& kv, const float* ws_o,
+                  const float* ws_ml, int nsplit, float* out,
+                  hipStream_t stream);
 bool attention_supported(int group);
 size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len);
 hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
@@ -42,6 +51,15 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
                             const int32_t* page_table, const int32_t* seq_lens,
                             const int32_t* sel, int list_len, float sm_scale,
                             float* out, void* workspace, hipStream_t stream);
+
+// Top-K + sparse attention in one launch (each workgroup selects its row).
+constexpr int kTopkAttnMaxPages = 8192;
+hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* page_table,
+                                 const int32_t* seq_lens, const float* scores,
+                                 int k_pages, float sm_scale, int32_t* sel,
+                                 float* out, void* workspace, hipStream_t stream);
 
 // Fused step (estimate -> Top-K -> attention in one launch).
 constexpr int kStepMaxPages = 8192;

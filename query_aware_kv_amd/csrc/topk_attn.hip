@@ -1,0 +1,174 @@
+// quest_topk_sparse_decode_attn: Top-K selection and sparse attention of a
+// decode step in one launch (plus the split merge), with no hand-off between
+// workgroups.
+//
+// The steps are those of quest_topk_pages and quest_sparse_decode_attn
+// ("Guide to Quest" §3 and Implementation Step 2; the paper summary's exact
+// attention over the kept pages); the arithmetic is dev_topk.h and
+// dev_attn.h.  What changes is where the selection lives: every attention
+// workgroup of a (request, kv-head) row reads the row's scores (a few KiB)
+// and runs the row's Top-K itself, keeping the kept-page list in LDS.  All
+// workgroups of a row compute the identical list (the selection is exact and
+// deterministic), so none has to wait for another; each then writes its own
+// slice of sel_pages and attends over the same slice of the list.  This
+// removes a launch and the global round trip of the selection.
+#include "dev_attn.h"
+#include "dev_topk.h"
+#include "launch.h"
+
+namespace quest {
+namespace {
+
+template <DType T, int G, int KPT, int PPW>
+__global__ void __launch_bounds__(256)
+topk_attn_kernel(const uint16_t* __restrict__ q,
+                 const uint16_t* __restrict__ k_pool,
+                 const uint16_t* __restrict__ v_pool,
+                 const int32_t* __restrict__ page_table,
+                 const int32_t* __restrict__ seq_lens,
+                 const float* __restrict__ scores, int k, int Hkv,
+                 int max_pages, int num_pool_pages, float qscale,
+                 int32_t* __restrict__ sel, float* __restrict__ out,
+                 float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  __shared__ union {
+    TopkSmem<256> topk;
+    AttnSmem<G> attn;
+  } sm;
+  extern __shared__ int32_t kept[];  // k entries: the row's selection
+  const int unit = blockIdx.y;       // b * Hkv + g
+  const int b = unit / Hkv, g = unit - (unit / Hkv) * Hkv;
+  const int split = blockIdx.x, nsplit = gridDim.x;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, r = lane >> 4;
+
+  float v[KPT];
+  topk_load<256, KPT>(scores + (int64_t)unit * max_pages, max_pages, v);
+  const int L = seq_lens[b];
+  float qf[G][8];
+  attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
+  const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
+  topk_row<256, KPT>(v, n, k, kept, nullptr, nullptr, sm.topk);
+  __syncthreads();
+
+  // This workgroup's slice of the list: publish it, then attend over it.
+  const int s0 = split * kAttnWaves * PPW;
+  for (int i = tid; i < kAttnWaves * PPW && s0 + i < k; i += 256)
+    sel[(int64_t)unit * k + s0 + i] = kept[s0 + i];
+  const int i0 = s0 + wid * PPW;
+  int pj[PPW];
+  int64_t pp[PPW];
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi) {
+    const int i = i0 + pi;
+    const int j = i < k ? kept[i] : -1;
+    pp[pi] = (j >= 0 && j < n) ? page_table[(int64_t)b * max_pages + j] : -1;
+    pj[pi] = (pp[pi] >= 0 && pp[pi] < num_pool_pages) ? j : -1;
+  }
+  uint4 kx[PPW][4], vx[PPW][4];
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi)
+    if (pj[pi] >= 0) attn_load_tile(k_pool, v_pool, pp[pi], Hkv, g, r, c, kx[pi], vx[pi]);
+  AttnState<G> st;
+  attn_init(st);
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi)
+    if (pj[pi] >= 0)
+      attn_page<T, G>(st, qf, kx[pi], vx[pi], min(kPageSize, L - pj[pi] * kPageSize), r);
+  attn_combine_rows(st);
+  __syncthreads();  // the Top-K scratch becomes the attention scratch
+  attn_stage_wave(st, sm.attn, wid, r, c);
+  __syncthreads();
+
+  const int Hq = Hkv * G;
+  for (int idx = tid; idx < G * kHeadDim; idx += 256) {
+    const int h = idx / kHeadDim, ch = idx - h * kHeadDim;
+    float M, den, num;
+    attn_wg_partial(sm.attn, h, ch, M, den, num);
+    const int64_t qh = (int64_t)b * Hq + g * G + h;
+    if (nsplit == 1) {
+      out[qh * kHeadDim + ch] = den > 0.f ? num / den : 0.f;
+    } else {
+      const int64_t slot = qh * nsplit + split;
+      ws_o[slot * kHeadDim + ch] = num;
+      if (ch == 0) {
+        ws_ml[slot * 2] = M;
+        ws_ml[slot * 2 + 1] = den;
+      }
+    }
+  }
+}
+
+template <DType T, int G, int KPT, int PPW>
+void launch_t(const quest_paged_kv& kv, const void* q, const void* k_pool,
+              const void* v_pool, const int32_t* page_table,
+              const int32_t* seq_lens, const float* scores, int k, float qscale,
+              int32_t* sel, float* out, float* ws_o, float* ws_ml, int nsplit,
+              hipStream_t stream) {
+  dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
+  topk_attn_kernel<T, G, KPT, PPW><<<grid, 256, (size_t)k * sizeof(int32_t), stream>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
+      static_cast<const uint16_t*>(v_pool), page_table, seq_lens, scores, k,
+      kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages, qscale, sel, out,
+      ws_o, ws_ml);
+}
+
+template <DType T, int KPT>
+void dispatch_g(int G, int ppw, const quest_paged_kv& kv, const void* q,
+                const void* k_pool, const void* v_pool, const int32_t* page_table,
+                const int32_t* seq_lens, const float* scores, int k, float qscale,
+                int32_t* sel, float* out, float* ws_o, float* ws_ml, int nsplit,
+                hipStream_t s) {
+#define QUEST_TA(GG, PP)                                                         \
+  launch_t<T, GG, KPT, PP>(kv, q, k_pool, v_pool, page_table, seq_lens, scores, \
+                           k, qscale, sel, out, ws_o, ws_ml, nsplit, s)
+  if (G == 1) {
+    if (ppw == 4) QUEST_TA(1, 4);
+    else if (ppw == 2) QUEST_TA(1, 2);
+    else QUEST_TA(1, 1);
+  } else if (G == 2) {
+    if (ppw == 2) QUEST_TA(2, 2);
+    else QUEST_TA(2, 1);
+  } else if (G == 4) {
+    if (ppw == 2) QUEST_TA(4, 2);
+    else QUEST_TA(4, 1);
+  } else {
+    QUEST_TA(8, 1);
+  }
+#undef QUEST_TA
+}
+
+}  // namespace
+
+hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* page_table,
+                                 const int32_t* seq_lens, const float* scores,
+                                 int k_pages, float sm_scale, int32_t* sel,
+                                 float* out, void* workspace, hipStream_t stream) {
+  const int G = kv.num_q_heads / kv.num_kv_heads;
+  const AttnPlan pl = attention_plan(kv, k_pages);
+  const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_ml = ws_o ? ws_o + attention_ml_offset(slots) : nullptr;
+  const float qscale = sm_scale * kLog2e;
+  const int mp = kv.max_pages_per_seq;
+  if (kv.dtype == QUEST_F16) {
+    if (mp <= 2048)
+      dispatch_g<DType::F16, 8>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
+                                scores, k_pages, qscale, sel, out, ws_o, ws_ml, pl.nsplit, stream);
+    else
+      dispatch_g<DType::F16, 32>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
+                                 scores, k_pages, qscale, sel, out, ws_o, ws_ml, pl.nsplit, stream);
+  } else {
+    if (mp <= 2048)
+      dispatch_g<DType::BF16, 8>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
+                                 scores, k_pages, qscale, sel, out, ws_o, ws_ml, pl.nsplit, stream);
+    else
+      dispatch_g<DType::BF16, 32>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
+                                  scores, k_pages, qscale, sel, out, ws_o, ws_ml, pl.nsplit, stream);
+  }
+  if (pl.nsplit > 1) launch_merge(kv, ws_o, ws_ml, pl.nsplit, out, stream);
+  return hipGetLastError();
+}
+
+}  // namespace quest

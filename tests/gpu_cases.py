@@ -129,8 +129,8 @@ def oracle_inputs(c, heads=None):
                 seq_lens=c["seq_lens"].cpu().numpy().astype(np.int64))
 
 
-def run_gpu_step(c, k_pages, kmin, kmax, sm_scale):
-    step = qa.SparseDecodeStep(c["kv"], k_pages, sm_scale)
+def run_gpu_step(c, k_pages, kmin, kmax, sm_scale, fused_topk=True):
+    step = qa.SparseDecodeStep(c["kv"], k_pages, sm_scale, fused_topk=fused_topk)
     out = step(c["q"], c["k_pool"], c["v_pool"], kmin, kmax,
                c["page_table"], c["seq_lens"])
     torch.cuda.synchronize()

@@ -213,12 +213,14 @@ def test_topk_kernel_bitexact(mp, k):
         assert np.array_equal(got[r, 0], ref), f"row {r} n={n_list[r]}"
 
 
+@pytest.mark.parametrize("fused_topk", [True, False], ids=["topk_attn", "separate"])
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_sparse_step_matches_oracle(name):
+def test_sparse_step_matches_oracle(name, fused_topk):
     wl, c = make(name)
     kv = c["kv"]
     kmin, kmax = C.gpu_meta(c)
-    s_gpu, sel_gpu, out_gpu = C.run_gpu_step(c, wl.k_pages, kmin, kmax, SM)
+    s_gpu, sel_gpu, out_gpu = C.run_gpu_step(c, wl.k_pages, kmin, kmax, SM,
+                                             fused_topk=fused_topk)
     o = C.oracle_inputs(c)
     omin, omax = O.page_meta(o["k_pool"], o["page_table"], o["seq_lens"], 16)
     s_ora = O.estimate(o["q"], omin, omax, o["page_table"], o["seq_lens"], 16,
@@ -320,3 +322,58 @@ def test_workspace_reuse_is_stateless():
         torch.cuda.synchronize()
         assert torch.equal(step.out, first)
         assert torch.equal(dense.out, d_first)
+
+
+@pytest.mark.parametrize("k_extra", [None, 1, 2, 5, 10000])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_topk_attn_equals_separate_calls(name, k_extra):
+    """quest_topk_sparse_decode_attn == quest_topk_pages then
+    quest_sparse_decode_attn, bit for bit, and it writes every slot of
+    sel_pages (which starts out full of a sentinel)."""
+    wl, c = make(name)
+    k = wl.k_pages if k_extra is None else k_extra
+    kv = c["kv"]
+    kmin, kmax = C.gpu_meta(c)
+    a = qa.SparseDecodeStep(kv, k, SM, fused_topk=True)
+    b = qa.SparseDecodeStep(kv, k, SM, fused_topk=False)
+    if not a.fused_topk:
+        pytest.skip("beyond the one-launch Top-K size limit")
+    a.sel.fill_(-777)
+    args = (c["q"], c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"],
+            c["seq_lens"])
+    a(*args)
+    b(*args)
+    torch.cuda.synchronize()
+    assert int((a.sel == -777).sum()) == 0
+    assert torch.equal(a.sel, b.sel)
+    assert torch.equal(a.out.view(torch.int32), b.out.view(torch.int32))
+
+
+@pytest.mark.parametrize("fused_topk", [True, False], ids=["topk_attn", "separate"])
+def test_graph_replay_matches_eager(fused_topk):
+    """The step captured in a HIP graph: every replay, with eager work and
+    synchronisations in between and new queries copied in, equals an eager
+    step on the same inputs."""
+    wl, c = make("mha_ragged_f16")
+    kv = c["kv"]
+    kmin, kmax = C.gpu_meta(c)
+    step = qa.SparseDecodeStep(kv, wl.k_pages, SM, fused_topk=fused_topk)
+    ref = qa.SparseDecodeStep(kv, wl.k_pages, SM, fused_topk=fused_topk)
+    q = c["q"].clone()
+    args = lambda qq: (qq, c["k_pool"], c["v_pool"], kmin, kmax,
+                       c["page_table"], c["seq_lens"])
+    step(*args(q))                      # warm up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(*args(q))
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    for i in range(5):
+        q.copy_(torch.randn(q.shape, generator=gen, device="cuda").to(q.dtype))
+        g.replay()
+        torch.cuda.synchronize()
+        ref(*args(q))                   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(step.sel, ref.sel), i
+        assert torch.equal(step.out.view(torch.int32), ref.out.view(torch.int32)), i
+        assert torch.equal(step.scores.view(torch.int32), ref.scores.view(torch.int32)), i
