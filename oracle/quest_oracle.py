@@ -31,7 +31,9 @@ with its reason in the design notes):
   * ties in the Top-K go to the lower page index, and scores compare as
     numbers (-0 == +0); the selection is returned in ascending page order,
     padded with -1;
-  * no forced sink/local pages on this path;
+  * no forced sink/local pages in the plain selection; ``topk_pages_forced``
+    is the variant with them: the caller keeps n_sink + n_local <= k, so the
+    result has exactly min(k, n) pages, and n_local = 0 means no window;
   * metadata and attention cover only a page's valid tokens
     (t < min(page_size, L - j*page_size));
   * min/max order signed zeros as -0 < +0 (IEEE 754-2019 minimum/maximum);
@@ -50,8 +52,8 @@ import numpy as np
 
 __all__ = [
     "page_valid_tokens", "page_meta", "append_token", "estimate",
-    "topk_pages", "sparse_attention", "dense_attention", "decode_step",
-    "layer_step",
+    "topk_pages", "topk_pages_forced", "sparse_attention", "dense_attention",
+    "decode_step", "layer_step",
 ]
 
 
@@ -170,6 +172,35 @@ def topk_pages(scores: np.ndarray, n_pages: int, k: int) -> np.ndarray:
     chosen = np.sort(order[:kk])
     out = np.full(k, -1, dtype=np.int64)
     out[:kk] = chosen
+    return out
+
+
+def topk_pages_forced(scores: np.ndarray, n_pages: int, k: int, n_sink: int,
+                      n_local: int) -> np.ndarray:
+    """Top-K with mandatory sink and local-window pages, one row.
+
+    [G] §3: the first pages (attention sinks) and the most recent pages
+    (the local window) are always kept; the remaining budget is filled by
+    the highest bounds among the other pages.  [G] Step 2: a sequence with
+    no more pages than the budget keeps all of them.  Requires
+    0 <= n_sink, 0 <= n_local, n_sink + n_local <= k; n_local = 0 is no
+    window.  Ties among the competing pages go to the lower index.
+    Returns int64 [k]: kept logical pages ascending, then -1s.
+    """
+    if n_sink < 0 or n_local < 0 or n_sink + n_local > k:
+        raise ValueError("need 0 <= n_sink, n_local and n_sink + n_local <= k")
+    if n_pages <= k:
+        return topk_pages(scores, n_pages, k)
+    # n_pages > k >= n_sink + n_local, so the two forced ranges are disjoint
+    forced = set(range(n_sink)) | set(range(n_pages - n_local, n_pages))
+    cand = np.array([j for j in range(n_pages) if j not in forced], dtype=np.int64)
+    s = np.asarray(scores, dtype=np.float64)[cand]
+    order = np.lexsort((cand, -s))                 # score desc, index asc
+    competing = cand[order[:k - len(forced)]]
+    kept = np.sort(np.concatenate([np.array(sorted(forced), dtype=np.int64),
+                                   competing]))
+    out = np.full(k, -1, dtype=np.int64)
+    out[:len(kept)] = kept
     return out
 
 

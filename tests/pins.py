@@ -368,6 +368,72 @@ def check_topk_library(O, seed=12):
         assert np.array_equal(got[:kk], ref)
 
 
+def check_forced_golden(O):
+    g = load_golden("topk_forced.json")
+    s = np.array([float(x) for x in g["scores"]])
+    for case in g["cases"]:
+        got = O.topk_pages_forced(s, len(s), case["k"], case["sink"], case["local"])
+        assert list(got) == case["expect"], (case, got)
+
+
+def check_forced_bruteforce(O, seed=21):
+    """Exhaustive search over every subset of n <= 10 pages: among the
+    subsets of size min(k, n) that hold every forced page, exactly one has
+    every kept competing page beat every dropped one, and it is selected."""
+    rng = np.random.default_rng(seed)
+    for trial in range(80):
+        n = int(rng.integers(1, 11))
+        k = int(rng.integers(1, 12))
+        ns = int(rng.integers(0, k + 1))
+        nl = int(rng.integers(0, k - ns + 1))
+        s = rng.integers(-3, 4, n).astype(np.float64)
+        kk = min(k, n)
+        forced = set(range(min(ns, n))) | set(range(max(0, n - nl), n)) \
+            if n > k else set(range(n))
+        winners = []
+        for S in itertools.combinations(range(n), kk):
+            S = set(S)
+            if not forced <= S:
+                continue
+            comp = S - forced
+            rest = [y for y in range(n) if y not in S]
+            if all(s[x] > s[y] or (s[x] == s[y] and x < y)
+                   for x in comp for y in rest):
+                winners.append(S)
+        assert len(winners) == 1, (n, k, ns, nl)
+        got = O.topk_pages_forced(s, n, k, ns, nl)
+        assert list(got[:kk]) == sorted(winners[0])
+        assert list(got[kk:]) == [-1] * (k - kk)
+
+
+def check_forced_special_cases(O, seed=22):
+    rng = np.random.default_rng(seed)
+    # no forced pages is the plain rule
+    for _ in range(20):
+        n = int(rng.integers(1, 200))
+        k = int(rng.integers(1, 60))
+        sc = np.round(rng.standard_normal(n), 1)
+        assert np.array_equal(O.topk_pages_forced(sc, n, k, 0, 0),
+                              O.topk_pages(sc, n, k))
+    # forced pages are kept however low their scores are
+    n = 20
+    sc = np.arange(n, dtype=np.float64)
+    sc[:2] = sc[-3:] = -np.inf
+    got = O.topk_pages_forced(sc, n, 8, 2, 3)
+    assert list(got) == [0, 1, 14, 15, 16, 17, 18, 19]   # 16, 15, 14 compete best
+    # the whole budget forced: sinks and window only
+    assert list(O.topk_pages_forced(sc, n, 5, 2, 3)) == [0, 1, 17, 18, 19]
+    # the window follows the sequence's end, not the row's capacity
+    assert list(O.topk_pages_forced(np.zeros(40), 30, 4, 1, 2)) == [0, 1, 28, 29]
+    # a budget smaller than the forced pages is refused
+    try:
+        O.topk_pages_forced(sc, n, 4, 2, 3)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("n_sink + n_local > k must be refused")
+
+
 # ---------------------------------------------------------------- attention
 
 def check_attention_golden(O):
@@ -581,6 +647,7 @@ ALL_CHECKS = [
     check_homogeneity, check_padding_and_indirection, check_gqa_group_sum,
     check_topk_golden, check_topk_bruteforce, check_topk_special_cases,
     check_topk_library,
+    check_forced_golden, check_forced_bruteforce, check_forced_special_cases,
     check_attention_golden, check_sparse_all_equals_dense, check_dense_vs_sdpa,
     check_attention_special_cases, check_attention_restricts_to_selection,
     check_gqa_head_mapping, check_empty_sequence,

@@ -77,6 +77,35 @@ def topk_ignores_short_rule(scores, n, k):
     return out
 
 
+def forced_window_shifted(scores, n, k, ns, nl):
+    """local window one page too early"""
+    if n <= k or nl == 0:
+        return O.topk_pages_forced(scores, n, k, ns, nl)
+    s = np.array(scores[:n], dtype=np.float64)
+    s[n - nl - 1:n - 1] = np.inf
+    s[:ns] = np.inf
+    return O.topk_pages(s, n, k)
+
+
+def forced_full_competition(scores, n, k, ns, nl):
+    """forced pages added on top of a full k-page competition"""
+    out = O.topk_pages_forced(scores, n, k, 0, 0)
+    if n <= k:
+        return out
+    kept = set(int(x) for x in out if x >= 0) | set(range(ns)) | set(range(n - nl, n))
+    kept = sorted(kept)[:k]
+    return np.array(kept + [-1] * (k - len(kept)))
+
+
+def forced_roles_swapped(scores, n, k, ns, nl):
+    """n_sink pages taken from the end and n_local from the start"""
+    return O.topk_pages_forced(scores, n, k, nl, ns)
+
+
+def forced_ignored(scores, n, k, ns, nl):
+    return O.topk_pages(scores, n, k)
+
+
 def meta_all_slots(k_pool, pt, lens, S):
     full = np.array([-(-int(L) // S) * S for L in lens])
     return O.page_meta(k_pool, pt, full, S)
@@ -139,6 +168,10 @@ MUTANTS = {
     "topk_descending": dict(topk_pages=topk_descending_output),
     "topk_off_by_one": dict(topk_pages=topk_off_by_one),
     "topk_no_short_rule": dict(topk_pages=topk_ignores_short_rule),
+    "forced_window_shifted": dict(topk_pages_forced=forced_window_shifted),
+    "forced_full_competition": dict(topk_pages_forced=forced_full_competition),
+    "forced_roles_swapped": dict(topk_pages_forced=forced_roles_swapped),
+    "forced_ignored": dict(topk_pages_forced=forced_ignored),
     "meta_reads_invalid_slots": dict(page_meta=meta_all_slots),
     "meta_unsigned_zero": dict(page_meta=meta_plain_minmax),
     "append_never_resets": dict(append_token=append_no_reset),
