@@ -1,27 +1,50 @@
 """Benchmark of the Quest sparse decode step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload longchat]
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
 
-A "step" is one pass of the whole hot path -- quest_estimate ->
-quest_topk_sparse_decode_attn (Top-K + sparse attention + split merge) --
-replayed as a HIP graph, over one LongChat-7B-shaped
-layer (32 heads, 32K context, 2048-token budget, fp16).  Inputs are seeded
-synthetic caches drawn on the GPU and resident in HBM before timing starts.
-Consecutive steps rotate over several independent caches whose touched bytes
-(metadata + selected pages) together exceed the 256 MB Infinity Cache, so
-every step reads its bytes from HBM.
+Workloads (each prints ONE JSON line):
 
-Prints ONE JSON line: the step time (the metric), effective GB/s on the
-algorithmic bytes, the dense-baseline time and speedup, a roofline object for
-the dominant kernel (HIP-event time on the launch stream), and a CPU-oracle
-baseline timed on a bounded sample of the same workload.
+* ``longchat`` (default, the headline): one LongChat-7B-shaped layer -- 32
+  heads, 32K context, 2048-token budget, fp16.  A "step" is one pass of the
+  whole hot path: quest_estimate -> quest_topk_sparse_decode_attn (Top-K +
+  sparse attention + split merge), issued eagerly or replayed as a HIP graph
+  (the faster counts; both are reported).  Consecutive steps rotate over
+  several independent caches whose touched bytes (metadata + selected
+  pages) together exceed the 256 MB Infinity Cache, so every step reads its
+  bytes from HBM.
+* ``gqa_multistep``: 32 layers of 32 q-heads / 8 kv-heads; every step
+  appends one token per layer (quest_update_page_meta, append mode), runs
+  dense attention on layers 0-1 and the sparse step on layers 2-31.  A step
+  is all 32 layers; the timed steps walk the 128 appends in order.
+* ``ragged``: 32 requests x 32 heads, contexts uniform in [8K, 32K], bf16,
+  pages scattered through a shared pool.
+* ``sweep``: the longchat layer over contexts 4K..128K x budgets 256..4096
+  tokens (one line holding every point).
+
+Inputs are seeded synthetic tensors drawn on the GPU and resident in HBM
+before timing starts.  The line carries the step time (the metric),
+effective GB/s on the algorithmic bytes, the dense-baseline time and
+speedup, the measured stream-read ceiling, a roofline object for the
+dominant call (HIP-event time on the launch stream) and, for the headline,
+a CPU-oracle baseline timed on a bounded sample of the same workload.
+
+    python bench.py --pmc-summary DIR
+
+turns the CSV output of rocprofv3 FETCH_SIZE / WRITE_SIZE runs (DIR/fetch,
+DIR/write, and DIR/cfetch, DIR/cwrite over ``--copy-probe``) into the
+per-call HBM traffic summary kept under profiles/.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import re
+import statistics
 import sys
 import time
 
@@ -32,6 +55,20 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 METRIC = ("µs/decode step + effective HBM GB/s, 32 heads, 32K ctx, "
           "2048-token budget")
+CSRC = os.path.join(ROOT, "query_aware_kv_amd", "csrc")
+
+# The kernels each timed call launches, and the sources they compile from
+# (a change to any of them invalidates the recorded HBM traffic).
+CALLS = {
+    "quest_estimate": {
+        "kernels": ["estimate_kernel"],
+        "sources": ["estimate.hip", "dev_estimate.h", "common.h", "launch.h"]},
+    "quest_topk_sparse_decode_attn": {
+        "kernels": ["topk_attn_kernel", "attn_merge_kernel"],
+        "sources": ["topk_attn.hip", "attention.hip", "dev_topk.h",
+                    "dev_attn.h", "common.h", "launch.h"]},
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_longchat32k.md")
 
 
 # ------------------------------------------------------------- byte model
@@ -69,63 +106,148 @@ def dense_bytes(seq_lens, n_kv_heads, n_q_heads, page_size=16, d=128, s=2):
                                                   for L in seq_lens)
 
 
+def append_bytes(batch, n_kv_heads, d=128, s=2):
+    """One appended token per request: the K and V rows written, and the
+    page's min/max read and written back."""
+    return batch * n_kv_heads * d * s * (2 + 4)
+
+
 def kv_cache_bytes(layers, heads, d, ctx, s=2):
     """K and V of every layer and head for ctx tokens."""
     return layers * 2 * heads * d * ctx * s
 
 
-# ------------------------------------------------------------- GPU timing
+def sources_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(n.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
-class KernelTimer:
-    """Events recorded on the stream the kernels run on."""
 
-    def __init__(self, torch, stream):
-        self.torch, self.stream, self.pairs = torch, stream, []
+def recorded_traffic(call):
+    """HBM bytes per launch of `call` from the committed rocprofv3 counter
+    summary, or None if there is none or the call's sources changed since."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"^\| %s \| (\d+) \| ([0-9a-f]+) \|" % re.escape(call), text, re.M)
+    if not m or m.group(2) != sources_digest(CALLS[call]["sources"]):
+        return None
+    return int(m.group(1))
 
-    def around(self, fn):
-        e0 = self.torch.cuda.Event(enable_timing=True)
-        e1 = self.torch.cuda.Event(enable_timing=True)
-        e0.record(self.stream)
+
+# ------------------------------------------------------------- GPU helpers
+
+def pct(xs, p):
+    xs = sorted(xs)
+    i = min(len(xs) - 1, max(0, int(round(p / 100 * (len(xs) - 1)))))
+    return xs[i]
+
+
+class Timer:
+    """Wall-clock mean per step (synchronised at both ends) and per-step
+    HIP-event durations on the launch stream for percentiles."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, n, w, rot, events=True):
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        for i in range(w):
+            fn(i % rot)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i % rot)
+        torch.cuda.synchronize()
+        mean = (time.perf_counter() - t0) / n * 1e6
+        if not events:
+            return dict(mean=mean)
+        pairs = []
+        for i in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(i % rot)
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        return dict(mean=mean, p10=pct(ts, 10), p50=pct(ts, 50), p90=pct(ts, 90))
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
         fn()
-        e1.record(self.stream)
-        self.pairs.append((e0, e1))
-
-    def mean_us(self):
-        self.torch.cuda.synchronize()
-        ts = [a.elapsed_time(b) * 1e3 for a, b in self.pairs]
-        return sum(ts) / len(ts) if ts else float("nan")
+    return g
 
 
-def run_gpu(args):
-    import numpy as np
-    import torch
+def call_us(torch, call, rot, reps):
+    """Device time of one call: HIP events on the launch stream around
+    replays of a graph holding one launch per cache, back to back."""
+    stream = torch.cuda.current_stream()
+    g = capture(torch, lambda: [call(i) for i in range(rot)])
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * rot)
 
-    import query_aware_kv_amd as qa
-    import synth
 
-    dev = "cuda"
-    if args.workload != "longchat":
-        raise SystemExit(f"unknown workload {args.workload}")
-    base = synth.longchat_layer_workload()
-    rot = args.rotate
-    insts = []
-    for i in range(rot):
-        wl = synth.longchat_layer_workload(seed=base.base_seed + 1000 * i)
-        c = synth.draw_layer(wl, 0, dev)
-        kv = qa.paged_kv(wl.batch, wl.num_q_heads, wl.num_kv_heads,
-                         wl.pool_pages(), wl.max_pages, wl.torch_dtype)
-        kmin, kmax = qa.alloc_meta(kv)
-        qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], kmin, kmax,
-                                  c["page_table"], c["seq_lens"])
-        c.update(kmin=kmin, kmax=kmax, kv=kv)
-        insts.append(c)
+def stream_read_ceiling(torch, qa, gib=4, reps=10):
+    """GB/s of quest_stream_read_probe over a buffer far larger than the
+    Infinity Cache."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qa.quest_stream_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        qa.quest_stream_read_probe(buf, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbps = (gib << 30) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return round(gbps, 1)
+
+
+def make_layer(qa, synth, wl, layer=0, dev="cuda"):
+    c = synth.draw_layer(wl, layer, dev)
+    kv = qa.paged_kv(wl.batch, wl.num_q_heads, wl.num_kv_heads,
+                     wl.pool_pages(), wl.max_pages, wl.torch_dtype)
+    kmin, kmax = qa.alloc_meta(kv)
+    qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], kmin, kmax,
+                              c["page_table"], c["seq_lens"])
+    c.update(kmin=kmin, kmax=kmax, kv=kv)
+    return c
+
+
+def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=True):
+    """Sparse step (and dense baseline) over rotating instances of one layer
+    geometry; per-call device times; algorithmic bytes from the selections
+    actually made."""
+    rot = len(wls)
+    insts = [make_layer(qa, synth, wl) for wl in wls]
     torch.cuda.synchronize()
     kv = insts[0]["kv"]
-    k = base.k_pages
+    k = wls[0].k_pages
     sm = 1.0 / math.sqrt(128)
     steps = [qa.SparseDecodeStep(kv, k, sm) for _ in range(rot)]
-    denses = [qa.DenseDecode(kv, sm) for _ in range(rot)]
-    stream = torch.cuda.current_stream()
+    denses = [qa.DenseDecode(kv, sm) for _ in range(rot)] if with_dense else []
 
     def step_call(i):
         c = insts[i]
@@ -136,49 +258,21 @@ def run_gpu(args):
         c = insts[i]
         denses[i](c["q"], c["k_pool"], c["v_pool"], c["page_table"], c["seq_lens"])
 
-    def capture(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        return g
-
     for i in range(rot):                 # eager warm-up before capture
         step_call(i)
-        dense_call(i)
+        if with_dense:
+            dense_call(i)
     torch.cuda.synchronize()
-    step_graphs = [capture(lambda i=i: step_call(i)) for i in range(rot)]
-    dense_graphs = [capture(lambda i=i: dense_call(i)) for i in range(rot)]
-
-    def timed(fn, n, w):
-        for i in range(w):
-            fn(i % rot)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(n):
-            fn(i % rot)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / n * 1e6
-
-    us_step = timed(lambda i: step_graphs[i].replay(), args.steps, args.warmup)
-    us_eager = timed(step_call, args.steps, args.warmup)
-    us_dense = (float("nan") if args.no_dense else
-                timed(lambda i: dense_graphs[i].replay(), max(20, args.steps // 4),
-                      args.warmup))
-
-    # Per-call device time: HIP events on the launch stream around replays of
-    # a graph holding one launch of the call per cache (8 back to back).
-    def call_us(call, reps=max(10, args.steps // rot)):
-        g = capture(lambda: [call(i) for i in range(rot)])
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (reps * rot)
+    step_graphs = [capture(torch, lambda i=i: step_call(i)) for i in range(rot)]
+    tm = Timer(torch)
+    t_graph = tm.run(lambda i: step_graphs[i].replay(), args.steps, args.warmup,
+                     rot, events=percentiles)
+    t_eager = tm.run(step_call, args.steps, args.warmup, rot, events=False)
+    t_dense = None
+    if with_dense:
+        dense_graphs = [capture(torch, lambda i=i: dense_call(i)) for i in range(rot)]
+        t_dense = tm.run(lambda i: dense_graphs[i].replay(),
+                         max(20, args.steps // 4), args.warmup, rot, events=False)
 
     def est(i):
         c, st = insts[i], steps[i]
@@ -191,37 +285,249 @@ def run_gpu(args):
             kv, c["q"], c["k_pool"], c["v_pool"], c["page_table"],
             c["seq_lens"], st.scores, k, sm, st.sel, st.out, st.workspace)
 
-    us_est = call_us(est)
-    us_ta = call_us(topk_attn)
+    reps = max(10, args.steps // rot)
+    us_est = call_us(torch, est, rot, reps)
+    us_ta = call_us(torch, topk_attn, rot, reps) if steps[0].fused_topk else None
 
-    # algorithmic bytes from the selections actually made
     sels = [st.sel.cpu().numpy() for st in steps]
-    lens = [int(x) for x in insts[0]["seq_lens"].cpu()]
-    bstep = [step_bytes(lens, kv.num_kv_heads, kv.num_q_heads, k, sel=s)
-             for s in sels]
-    avg = {key: sum(b[key] for b in bstep) / len(bstep) for key in bstep[0]}
-    B = len(lens)
+    lens_all = [[int(x) for x in c["seq_lens"].cpu()] for c in insts]
+    bstep = [step_bytes(lens_all[i], kv.num_kv_heads, kv.num_q_heads, k, sel=sels[i])
+             for i in range(rot)]
+    avg = {key: sum(b[key] for b in bstep) / rot for key in bstep[0]}
+    B = kv.batch
     est_bytes = avg["meta"] + avg["q"] + avg["table"] + \
         kv.num_kv_heads * kv.max_pages_per_seq * 4 * B
     ta_bytes = avg["kv"] + avg["q"] + avg["out"] + \
         kv.num_kv_heads * (kv.max_pages_per_seq + k) * 4 * B
-    calls = {"quest_estimate [estimate_kernel]": (us_est, est_bytes),
-             "quest_topk_sparse_decode_attn [topk_attn_kernel + attn_merge_kernel]":
-                 (us_ta, ta_bytes)}
+    calls = {"quest_estimate": (us_est, est_bytes)}
+    if us_ta is not None:
+        calls["quest_topk_sparse_decode_attn"] = (us_ta, ta_bytes)
+    dbytes = sum(dense_bytes(l, kv.num_kv_heads, kv.num_q_heads) for l in lens_all) / rot
+    return dict(t_graph=t_graph, t_eager=t_eager, t_dense=t_dense, bytes=avg,
+                calls=calls, dense_bytes=dbytes, insts=insts, kv=kv, k_pages=k,
+                sm=sm)
+
+
+def roofline(calls, traffic_recorded=False):
+    """Roofline of the slowest call.  `traffic` is the recorded rocprofv3
+    HBM traffic (longchat layer only) while its sources are unchanged."""
     dom = max(calls, key=lambda c: calls[c][0])
     d_us, d_bytes = calls[dom]
     achieved = d_bytes / (d_us * 1e-6) / 1e9
-    return dict(
-        us_step=us_step, us_eager=us_eager, us_dense=us_dense, bytes=avg,
-        calls={c: round(v[0], 3) for c, v in calls.items()},
-        roofline={"bound": "hbm", "achieved": round(achieved, 1),
-                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                  "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                  "kernel": dom, "kernel_us": round(d_us, 3),
-                  "bytes_per_launch": int(d_bytes)},
-        dense_bytes=dense_bytes(lens, kv.num_kv_heads, kv.num_q_heads),
-        gpu=torch.cuda.get_device_name(0), insts=insts, kv=kv,
-        k_pages=k, sm=sm)
+    traffic = recorded_traffic(dom) if traffic_recorded else None
+    return {"bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": f"{dom} [{' + '.join(CALLS[dom]['kernels'])}]",
+            "kernel_us": round(d_us, 3), "bytes_per_launch": int(d_bytes)}
+
+
+# ------------------------------------------------------------- workloads
+
+def bench_longchat(args, torch, qa, synth):
+    base = synth.longchat_layer_workload()
+    wls = [synth.longchat_layer_workload(seed=base.base_seed + 1000 * i)
+           for i in range(args.rotate)]
+    r = time_single_layer(args, torch, qa, synth, wls, with_dense=not args.no_dense)
+    tg, te = r["t_graph"], r["t_eager"]
+    us = min(tg["mean"], te["mean"])
+    gbps = r["bytes"]["total"] / (us * 1e-6) / 1e9
+    us_dense = r["t_dense"]["mean"] if r["t_dense"] else float("nan")
+    ceiling = None if args.no_ceiling else stream_read_ceiling(torch, qa)
+    line = {
+        "metric": METRIC, "value": round(us, 3), "unit": "us/step",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) fp16 K/V/q, 4 outlier channels x8, "
+                "5 planted pages per head; identity page table)",
+        "config": {"workload": "longchat7b_layer_decode", "batch": 1,
+                   "q_heads": 32, "kv_heads": 32, "head_dim": 128,
+                   "page_size": 16, "ctx": 32768, "budget_tokens": 2048,
+                   "rotating_caches": args.rotate},
+        "effective_GBps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "stream_read_GBps": ceiling,
+        "ceiling_frac": round(gbps / ceiling, 4) if ceiling else None,
+        "bytes_per_step": int(r["bytes"]["total"]),
+        "dense_us_per_step": round(us_dense, 3),
+        "speedup_vs_dense": round(us_dense / us, 3),
+        "dense_effective_GBps": round(r["dense_bytes"] / (us_dense * 1e-6) / 1e9, 1),
+        "timing": "value = the faster of eager issue (the calls from Python "
+                  "through ctypes) and HIP-graph replay (one graph per cache); "
+                  f"{args.rotate} caches rotated; percentiles from HIP events "
+                  "around each graph replay",
+        "eager_us_per_step": round(te["mean"], 3),
+        "graph_us_per_step": round(tg["mean"], 3),
+        "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
+        "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
+        "roofline": roofline(r["calls"], traffic_recorded=True),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds)
+    return line
+
+
+def bench_ragged(args, torch, qa, synth):
+    wl = synth.ragged_batch_workload()
+    r = time_single_layer(args, torch, qa, synth, [wl], with_dense=not args.no_dense)
+    tg, te = r["t_graph"], r["t_eager"]
+    us = min(tg["mean"], te["mean"])
+    gbps = r["bytes"]["total"] / (us * 1e-6) / 1e9
+    us_dense = r["t_dense"]["mean"] if r["t_dense"] else float("nan")
+    return {
+        "metric": "µs/decode step + effective HBM GB/s, batched ragged",
+        "value": round(us, 3), "unit": "us/step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/q; pool pages permuted)",
+        "config": {"workload": "ragged_batch_decode", "batch": wl.batch,
+                   "q_heads": 32, "kv_heads": 32, "ctx_min": min(wl.seq_lens),
+                   "ctx_max": max(wl.seq_lens), "budget_tokens": 2048},
+        "effective_GBps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": int(r["bytes"]["total"]),
+        "dense_us_per_step": round(us_dense, 3),
+        "speedup_vs_dense": round(us_dense / us, 3),
+        "dense_effective_GBps": round(r["dense_bytes"] / (us_dense * 1e-6) / 1e9, 1),
+        "eager_us_per_step": round(te["mean"], 3),
+        "graph_us_per_step": round(tg["mean"], 3),
+        "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
+        "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
+        "roofline": roofline(r["calls"]),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+
+
+def bench_sweep(args, torch, qa, synth):
+    points = []
+    for ctx in synth.SWEEP_CTX:
+        for budget in synth.SWEEP_BUDGET:
+            # enough independent caches that the bytes one pass over them
+            # touches (metadata + selected pages) exceed the Infinity Cache
+            touched_mib = ctx / 1024 + min(budget, ctx) / 64
+            rot = min(64, max(2, math.ceil(768 / touched_mib)))
+            wls = [synth.sweep_workload(ctx, budget, seed=2 + 1000 * i)
+                   for i in range(rot)]
+            r = time_single_layer(args, torch, qa, synth, wls,
+                                  with_dense=not args.no_dense, percentiles=False)
+            us = min(r["t_graph"]["mean"], r["t_eager"]["mean"])
+            us_dense = r["t_dense"]["mean"] if r["t_dense"] else float("nan")
+            points.append({
+                "ctx": ctx, "budget": budget, "us_per_step": round(us, 3),
+                "effective_GBps": round(r["bytes"]["total"] / (us * 1e-6) / 1e9, 1),
+                "dense_us": round(us_dense, 3),
+                "speedup_vs_dense": round(us_dense / us, 3),
+                "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()}})
+            print(json.dumps({"progress": points[-1]}), file=sys.stderr, flush=True)
+            del r
+            torch.cuda.empty_cache()
+    at = [p for p in points if p["ctx"] == 32768 and p["budget"] == 2048][0]
+    return {
+        "metric": "µs/decode step over context x budget, 32 heads",
+        "value": at["us_per_step"], "unit": "us/step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(at["us_per_step"] / 1e3, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic (as longchat, per point)",
+        "config": {"workload": "ctx_budget_sweep", "ctx": list(synth.SWEEP_CTX),
+                   "budget_tokens": list(synth.SWEEP_BUDGET),
+                   "value_at": "ctx 32768, budget 2048"},
+        "points": points, "gpu": torch.cuda.get_device_name(0)}
+
+
+def bench_gqa_multistep(args, torch, qa, synth):
+    wl = synth.gqa_multistep_workload()
+    dev = "cuda"
+    sm = 1.0 / math.sqrt(128)
+    k = wl.k_pages
+    nsteps = wl.steps
+    layers = []
+    for layer in range(wl.layers):
+        c = make_layer(qa, synth, wl, layer)
+        st = dict(c=c, kv=c["kv"])
+        if layer < wl.dense_layers:
+            st["dense"] = qa.DenseDecode(c["kv"], sm)
+        else:
+            st["step"] = qa.SparseDecodeStep(c["kv"], k, sm)
+        st["q"] = torch.stack([synth.draw_query(wl, layer, dev, step=s)
+                               for s in range(nsteps)])
+        kn, vn = zip(*[synth.draw_append_token(wl, layer, s, dev)
+                       for s in range(nsteps)])
+        st["k_new"], st["v_new"] = torch.stack(kn), torch.stack(vn)
+        layers.append(st)
+    L0 = wl.seq_lens[0]
+    lens = [torch.tensor([L0 + s + 1], dtype=torch.int32, device=dev)
+            for s in range(nsteps)]
+    torch.cuda.synchronize()
+
+    def one_step(s):
+        for layer, st in enumerate(layers):
+            c, kv = st["c"], st["kv"]
+            qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], c["kmin"],
+                                      c["kmax"], c["page_table"], lens[s],
+                                      k_new=st["k_new"][s], v_new=st["v_new"][s])
+            if layer < wl.dense_layers:
+                st["dense"](st["q"][s], c["k_pool"], c["v_pool"],
+                            c["page_table"], lens[s])
+            else:
+                st["step"](st["q"][s], c["k_pool"], c["v_pool"], c["kmin"],
+                           c["kmax"], c["page_table"], lens[s])
+
+    # Warm-up steps re-append the same tokens at the same positions; they
+    # leave every page box a superset of the timed run's, which changes no
+    # byte count and no launch.
+    for s in range(min(args.warmup, nsteps)):
+        one_step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(nsteps):
+        one_step(s)
+    torch.cuda.synchronize()
+    us_eager = (time.perf_counter() - t0) / nsteps * 1e6
+    graphs = [capture(torch, lambda s=s: one_step(s)) for s in range(nsteps)]
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tg = tm.run(lambda s: graphs[s].replay(), nsteps, min(args.warmup, nsteps),
+                nsteps)
+    us = min(us_eager, tg["mean"])
+
+    # bytes per step (final lengths, selections of the last replayed step)
+    B = 1
+    sparse_b = 0
+    for st in layers[wl.dense_layers:]:
+        sel = st["step"].sel.cpu().numpy()
+        sparse_b += step_bytes([L0 + nsteps], 8, 32, k, sel=sel)["total"]
+    dense_b = wl.dense_layers * dense_bytes([L0 + nsteps], 8, 32)
+    app_b = wl.layers * append_bytes(B, 8)
+    total = sparse_b + dense_b + app_b
+    all_dense = wl.layers * dense_bytes([L0 + nsteps], 8, 32) + app_b
+    return {
+        "metric": "µs per 32-layer decode step, GQA 32/8, 32K ctx, "
+                  "2048-token budget, layers 0-1 dense",
+        "value": round(us, 3), "unit": "us/step", "n_gpus": 1,
+        "steps": nsteps, "warmup": min(args.warmup, nsteps),
+        "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) fp16, 4 outlier channels x8 per "
+                "(layer, kv-head); one appended token per layer per step)",
+        "config": {"workload": "gqa_multistep_decode", "layers": wl.layers,
+                   "q_heads": 32, "kv_heads": 8, "ctx_start": L0,
+                   "appended_steps": nsteps, "budget_tokens": wl.budget_tokens,
+                   "dense_layers": wl.dense_layers},
+        "effective_GBps": round(total / (us * 1e-6) / 1e9, 1),
+        "hbm_frac": round(total / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": int(total),
+        "all_dense_bytes_per_step": int(all_dense),
+        "eager_us_per_step": round(us_eager, 3),
+        "graph_us_per_step": round(tg["mean"], 3),
+        "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
+        "launches_per_step": wl.dense_layers * 3 + (wl.layers - wl.dense_layers) * 4,
+        "gpu": torch.cuda.get_device_name(0),
+    }
 
 
 # ------------------------------------------------------------- CPU oracle
@@ -263,21 +569,76 @@ def cpu_baseline(gpu, budget_s):
                        f"{gpu['kv'].num_q_heads // len(heads)} to 32 heads")}
 
 
+# ------------------------------------------------------------- counters
+
+def _counter_medians(path):
+    """Median counter value per kernel (short name) over its dispatches."""
+    vals = {}
+    for f in glob.glob(os.path.join(path, "*counter_collection.csv")):
+        for row in csv.DictReader(open(f)):
+            n = row["Kernel_Name"]
+            m = re.search(r"quest::\(anonymous namespace\)::(\w+)", n)
+            key = m.group(1) if m else ("copy" if "copy" in n.lower() else None)
+            if key:
+                vals.setdefault(key, []).append(float(row["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}, \
+        {k: len(v) for k, v in vals.items()}
+
+
+def pmc_summary(d, copy_mib):
+    """Markdown: calibrated FETCH_SIZE + WRITE_SIZE bytes per launch."""
+    fetch, nf = _counter_medians(os.path.join(d, "fetch"))
+    write, _ = _counter_medians(os.path.join(d, "write"))
+    cfetch, _ = _counter_medians(os.path.join(d, "cfetch"))
+    cwrite, _ = _counter_medians(os.path.join(d, "cwrite"))
+    copy_kib = copy_mib * 1024
+    f_scale = copy_kib / cfetch["copy"]
+    w_scale = copy_kib / cwrite["copy"]
+    out = ["| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | "
+           "calibrated bytes |", "|---|---|---|---|---|"]
+    per_kernel = {}
+    for k in sorted(fetch):
+        if k == "copy" or k not in write:
+            continue
+        b = (fetch[k] * f_scale + write[k] * w_scale) * 1024
+        per_kernel[k] = b
+        out.append(f"| {k} | {nf[k]} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.0f} |")
+    calls = ["", "| call | HBM bytes per launch | sources digest |", "|---|---|---|"]
+    for call, spec in CALLS.items():
+        if all(k in per_kernel for k in spec["kernels"]):
+            b = sum(per_kernel[k] for k in spec["kernels"])
+            calls.append(f"| {call} | {b:.0f} | {sources_digest(spec['sources'])} |")
+    head = [f"Copy calibration ({copy_mib} MiB read + {copy_mib} MiB written "
+            f"by one device copy): FETCH_SIZE reads {cfetch['copy']:.1f} KiB "
+            f"(scale x{f_scale:.4f}), WRITE_SIZE {cwrite['copy']:.1f} KiB "
+            f"(scale x{w_scale:.4f}).", ""]
+    return "\n".join(head + out + calls) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="longchat")
+    ap.add_argument("--workload", default="longchat",
+                    choices=["longchat", "gqa_multistep", "ragged", "sweep"])
     ap.add_argument("--rotate", type=int, default=8,
                     help="independent caches the steps cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times "
                          "(calibrates the FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="only summarise rocprofv3 counter CSVs under DIR")
+    ap.add_argument("--copy-mib", type=int, default=512,
+                    help="size the --copy-probe runs used (for --pmc-summary)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        sys.stdout.write(pmc_summary(args.pmc_summary, args.copy_mib))
+        return
     if args.copy_probe:
         import torch
         a = torch.empty(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
@@ -294,36 +655,14 @@ def main():
               "with no exchange; see the design notes).", file=sys.stderr)
         sys.exit(2)
 
-    g = run_gpu(args)
-    us = g["us_step"]
-    gbps = g["bytes"]["total"] / (us * 1e-6) / 1e9
-    line = {
-        "metric": METRIC, "value": round(us, 3), "unit": "us/step",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-        "data": "synthetic (seeded N(0,1) fp16 K/V/q, 4 outlier channels x8, "
-                "5 planted pages per head; identity page table)",
-        "config": {"workload": "longchat7b_layer_decode", "batch": 1,
-                   "q_heads": 32, "kv_heads": 32, "head_dim": 128,
-                   "page_size": 16, "ctx": 32768, "budget_tokens": 2048,
-                   "rotating_caches": args.rotate},
-        "effective_GBps": round(gbps, 1),
-        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "bytes_per_step": int(g["bytes"]["total"]),
-        "dense_us_per_step": round(g["us_dense"], 3),
-        "speedup_vs_dense": round(g["us_dense"] / us, 3),
-        "dense_effective_GBps": round(g["dense_bytes"] / (g["us_dense"] * 1e-6) / 1e9, 1),
-        "timing": "HIP-graph replay of the step (one graph per cache, 8 caches "
-                  "rotated); eager = the same calls issued from Python",
-        "eager_us_per_step": round(g["us_eager"], 3),
-        "call_us": g["calls"],
-        "roofline": g["roofline"],
-        "gpu": g["gpu"],
-    }
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(g, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    import torch
+
+    import query_aware_kv_amd as qa
+    import synth
+
+    fn = {"longchat": bench_longchat, "gqa_multistep": bench_gqa_multistep,
+          "ragged": bench_ragged, "sweep": bench_sweep}[args.workload]
+    print(json.dumps(fn(args, torch, qa, synth)), flush=True)
 
 
 if __name__ == "__main__":

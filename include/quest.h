@@ -221,6 +221,17 @@ QUEST_API quest_status quest_step_workspace_size(const quest_paged_kv* kv,
 QUEST_API quest_status quest_workspace_size(const quest_paged_kv* kv,
                                             int32_t k_pages, size_t* bytes);
 
+/*
+ * Diagnostic, not part of the method: reads `bytes` (a positive multiple of
+ * 16) of device memory at `buf` (16-byte aligned) once, as a plain streaming
+ * read with 16-byte loads over the whole GPU.  Its time gives the HBM read
+ * ceiling that the read-bound calls above are compared against.  `sink`
+ * (device, 4-byte aligned, one uint32) is written only if the xor of all
+ * loaded words equals 0x9e3779b9; its value means nothing.
+ */
+QUEST_API quest_status quest_stream_read_probe(const void* buf, size_t bytes,
+                                               uint32_t* sink, void* stream);
+
 /* Host only: static description of a status code. */
 QUEST_API const char* quest_status_string(quest_status status);
 

@@ -17,7 +17,8 @@ from ._abi import (  # noqa: F401
     QUEST_ERR_HIP, QUEST_ERR_INVALID_ARGUMENT, QUEST_ERR_UNSUPPORTED,
     QUEST_ERR_WORKSPACE_TOO_SMALL, paged_kv, paged_kv_like,
     quest_decode_attn, quest_estimate, quest_sparse_decode_attn,
-    quest_sparse_decode_step, quest_step_workspace_size, quest_topk_pages,
+    quest_sparse_decode_step, quest_step_workspace_size,
+    quest_stream_read_probe, quest_topk_pages,
     quest_topk_sparse_decode_attn, quest_update_page_meta,
     quest_workspace_size,
 )

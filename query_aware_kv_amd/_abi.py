@@ -81,6 +81,7 @@ def _load():
         "quest_step_workspace_size": [KV, I, ctypes.POINTER(ctypes.c_size_t)],
         "quest_topk_sparse_decode_attn": [KV, P, P, P, P, P, P, I, ctypes.c_float,
                                           P, P, P, ctypes.c_size_t, P],
+        "quest_stream_read_probe": [P, ctypes.c_size_t, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -301,3 +302,11 @@ def quest_topk_sparse_decode_attn(kv: PagedKV, q, k_pool, v_pool, page_table,
         _ptr(out, "out", torch.float32, (kv.batch, kv.num_q_heads, kv.head_dim)),
         _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes),
         _stream(stream)))
+
+
+def quest_stream_read_probe(buf, sink, stream=None) -> None:
+    """Diagnostic: one streaming read of the whole of `buf` (any dtype,
+    16-byte multiple); `sink` is a one-element int32/uint32 device tensor."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(LIB.quest_stream_read_probe(_ptr(buf, "buf"), ctypes.c_size_t(nbytes),
+                                       _ptr(sink, "sink"), _stream(stream)))

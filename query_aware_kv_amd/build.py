@@ -33,7 +33,7 @@ COMMON_FLAGS = [
 ]
 
 SOURCES = ["api.cpp", "meta.hip", "estimate.hip", "topk.hip", "attention.hip",
-           "topk_attn.hip", "step.hip"]
+           "topk_attn.hip", "step.hip", "probe.hip"]
 
 
 def _compile(src: str) -> str:

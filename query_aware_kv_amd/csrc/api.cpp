@@ -341,6 +341,19 @@ QUEST_API quest_status quest_workspace_size(const quest_paged_kv* kv,
   return ok();
 }
 
+QUEST_API quest_status quest_stream_read_probe(const void* buf, size_t bytes,
+                                               uint32_t* sink, void* stream) {
+  const char* fn = "quest_stream_read_probe";
+  REQUIRE_PTR(buf, aligned16(buf));
+  REQUIRE_PTR(sink, aligned4(sink));
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(QUEST_ERR_INVALID_ARGUMENT,
+                "%s: bytes (%zu) must be a positive multiple of 16", fn, bytes);
+  return hip_status(
+      quest::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)),
+      fn);
+}
+
 QUEST_API const char* quest_status_string(quest_status status) {
   switch (status) {
     case QUEST_OK: return "ok";

@@ -187,14 +187,14 @@ struct MergeSmem {
 // Merge nsplit partials of one (request, query head) into out_row[128] with
 // a 256-thread workgroup: partial s is (o[s*128 .. +128], ml[2s] = M,
 // ml[2s+1] = den).  Thread (half, ch) folds channel ch of the splits of its
-// parity with a running max (online softmax), 8 splits per chunk whose
-// loads are all issued together -- one memory round trip per chunk; the
-// two halves then meet in LDS.
+// parity with a running max (online softmax), 16 splits per chunk whose
+// loads are all issued together -- one memory round trip per chunk, so one
+// in all for up to 32 splits; the two halves then meet in LDS.
 __device__ __forceinline__ void merge_splits(const float* __restrict__ o,
                                              const float* __restrict__ ml,
                                              int nsplit, float* __restrict__ out_row,
                                              MergeSmem& sm) {
-  constexpr int kChunk = 8;
+  constexpr int kChunk = 16;
   const int tid = threadIdx.x;
   const int ch = tid & (kHeadDim - 1), half = tid >> 7;
   float mr = -INFINITY, num = 0.f, den = 0.f;

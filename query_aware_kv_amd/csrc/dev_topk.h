@@ -51,11 +51,6 @@ __device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t x) {
   return op(op(r0, r1), op(r2, r3));
 }
 
-// Select for one row.  The whole block (BLOCK threads) must call it.
-//   v      : this thread's scores from topk_load (the row has n <= BLOCK*KPT)
-//   out    : k slots; kept logical page indices ascending, then -1
-//   pt_row : if non-null, phys[slot] = pt_row[page] for each kept page and
-//            -1 for the padding (the physical page list used by attention)
 // Load a thread's KPT consecutive scores; entries below `limit` are in
 // bounds (limit = the row's length in the buffer), so callers can issue this
 // before they know n.
@@ -67,18 +62,44 @@ __device__ __forceinline__ void topk_load(const float* __restrict__ s, int limit
   for (int i = 0; i < KPT; ++i) v[i] = base + i < limit ? s[base + i] : 0.f;
 }
 
+// The page-table entries of the same KPT pages, so that the kept pages' pool
+// ids come out of the selection with no dependent load after it.
+template <int BLOCK, int KPT>
+__device__ __forceinline__ void topk_load_table(const int32_t* __restrict__ pt_row,
+                                                int limit, int32_t (&e)[KPT]) {
+  const int base = threadIdx.x * KPT;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) e[i] = base + i < limit ? pt_row[base + i] : -1;
+}
+
+// Select for one row.  The whole block (BLOCK threads) must call it.
+//   v    : this thread's scores from topk_load (the row has n <= BLOCK*KPT)
+//   out  : the k output slots are kept logical page indices ascending, then
+//          -1; only slots lo <= slot < hi are written, slot s to out[s - lo]
+//   ent  : if non-null, this thread's page-table entries (topk_load_table);
+//          then phys[s - lo] = the kept page's entry, -1 for the padding (the
+//          pool page list used by attention), for the same slots
 template <int BLOCK, int KPT>
 __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
                          int32_t* __restrict__ out,
-                         const int32_t* __restrict__ pt_row,
-                         int32_t* __restrict__ phys, TopkSmem<BLOCK>& sm) {
+                         const int32_t (*ent)[KPT],
+                         int32_t* __restrict__ phys, TopkSmem<BLOCK>& sm,
+                         int lo = 0, int hi = 0x7fffffff) {
   constexpr int NW = BLOCK / kWave;
   static_assert(NW >= 2, "one wave scans while the others clear");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  hi = min(hi, k);
   if (n <= k) {  // everything fits: keep every page
-    for (int i = tid; i < k; i += BLOCK) {
-      out[i] = i < n ? i : -1;
-      if (phys) phys[i] = i < n ? pt_row[i] : -1;
+    for (int i = lo + tid; i < hi; i += BLOCK) {
+      out[i - lo] = i < n ? i : -1;
+      if (phys && i >= n) phys[i - lo] = -1;
+    }
+    if (phys) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int p = tid * KPT + i;
+        if (p < n && p >= lo && p < hi) phys[p - lo] = (*ent)[i];
+      }
     }
     return;
   }
@@ -191,9 +212,9 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
       if (eq_before < need) slot = gt_before + eq_before;
       ++eq_before;
     }
-    if (slot < (uint32_t)k) {  // always < k when selected
-      out[slot] = base + i;
-      if (phys) phys[slot] = pt_row[base + i];
+    if (slot - (uint32_t)lo < (uint32_t)(hi - lo)) {  // selected, in the window
+      out[slot - lo] = base + i;
+      if (phys) phys[slot - lo] = (*ent)[i];
     }
   }
 }

@@ -54,6 +54,10 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
 
 // Top-K + sparse attention in one launch (each workgroup selects its row).
 constexpr int kTopkAttnMaxPages = 8192;
+// probe.hip: streaming read of `bytes` (a multiple of 16) at `buf`.
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink,
+                             hipStream_t stream);
+
 hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
                                  const void* k_pool, const void* v_pool,
                                  const int32_t* page_table,

@@ -34,33 +34,35 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
     TopkSmem<256> topk;
     AttnSmem<G> attn;
   } sm;
-  extern __shared__ int32_t kept[];  // k entries: the row's selection
+  // This workgroup's slice of the row's selection.
+  __shared__ int32_t kept[kAttnWaves * PPW];
   const int unit = blockIdx.y;       // b * Hkv + g
   const int b = unit / Hkv, g = unit - (unit / Hkv) * Hkv;
   const int split = blockIdx.x, nsplit = gridDim.x;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int c = lane & 15, r = lane >> 4;
 
+  // Scores, the length and q are independent loads.
   float v[KPT];
   topk_load<256, KPT>(scores + (int64_t)unit * max_pages, max_pages, v);
   const int L = seq_lens[b];
   float qf[G][8];
   attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
   const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
-  topk_row<256, KPT>(v, n, k, kept, nullptr, nullptr, sm.topk);
+  const int s0 = split * kAttnWaves * PPW;
+  topk_row<256, KPT>(v, n, k, kept, nullptr, nullptr, sm.topk, s0,
+                     s0 + kAttnWaves * PPW);
   __syncthreads();
 
   // This workgroup's slice of the list: publish it, then attend over it.
-  const int s0 = split * kAttnWaves * PPW;
   for (int i = tid; i < kAttnWaves * PPW && s0 + i < k; i += 256)
-    sel[(int64_t)unit * k + s0 + i] = kept[s0 + i];
-  const int i0 = s0 + wid * PPW;
+    sel[(int64_t)unit * k + s0 + i] = kept[i];
   int pj[PPW];
   int64_t pp[PPW];
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi) {
-    const int i = i0 + pi;
-    const int j = i < k ? kept[i] : -1;
+    const int i = wid * PPW + pi;
+    const int j = s0 + i < k ? kept[i] : -1;
     pp[pi] = (j >= 0 && j < n) ? page_table[(int64_t)b * max_pages + j] : -1;
     pj[pi] = (pp[pi] >= 0 && pp[pi] < num_pool_pages) ? j : -1;
   }
@@ -105,7 +107,7 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* k_pool,
               int32_t* sel, float* out, float* ws_o, float* ws_ml, int nsplit,
               hipStream_t stream) {
   dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
-  topk_attn_kernel<T, G, KPT, PPW><<<grid, 256, (size_t)k * sizeof(int32_t), stream>>>(
+  topk_attn_kernel<T, G, KPT, PPW><<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), page_table, seq_lens, scores, k,
       kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages, qscale, sel, out,

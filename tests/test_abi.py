@@ -177,3 +177,14 @@ def test_fused_step_is_switched_off():
         P(FAKE), P(FAKE), 1 << 30, None)
     assert st == _abi.QUEST_ERR_UNSUPPORTED
     assert "switched off" in qa.LIB.quest_last_error().decode()
+
+
+def test_stream_read_probe_validation():
+    P = ctypes.c_void_p
+    f = qa.LIB.quest_stream_read_probe
+    assert f(None, 1024, P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert f(P(FAKE), 1024, None, None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert f(P(FAKE + 8), 1024, P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert f(P(FAKE), 1000, P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert "multiple of 16" in qa.LIB.quest_last_error().decode()
+    assert f(P(FAKE), 0, P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
