@@ -139,6 +139,25 @@ QUEST_API quest_status quest_topk_pages(
     int32_t k_pages, int32_t* sel_pages, void* stream);
 
 /*
+ * Top-K with forced pages.  [G] §3 and Implementation Step 2: the first
+ * pages (attention sinks) and the most recent pages (the local window) are
+ * kept unconditionally and the rest of the budget goes to the highest
+ * bounds among the other pages.  For a row with n_b > k_pages the kept set
+ * is pages j < n_sink, pages j >= n_b - n_local, and the first
+ * k_pages - n_sink - n_local of the remaining pages in the order (score
+ * descending, page index ascending); a row with n_b <= k_pages keeps all of
+ * its pages.  Output as for quest_topk_pages (ascending, -1 padded).
+ * Requires 0 <= n_sink, 0 <= n_local and n_sink + n_local <= k_pages
+ * (QUEST_ERR_INVALID_ARGUMENT otherwise), so every row keeps exactly
+ * min(k_pages, n_b) pages; n_local = 0 means no window.  n_sink = n_local =
+ * 0 is quest_topk_pages.  Scores of forced pages are not read as values.
+ */
+QUEST_API quest_status quest_topk_pages_ex(
+    const quest_paged_kv* kv, const float* scores, const int32_t* seq_lens,
+    int32_t k_pages, int32_t n_sink, int32_t n_local, int32_t* sel_pages,
+    void* stream);
+
+/*
  * Sparse exact decode attention over the selected pages.  [Q] Summary and
  * [G] §3: attention runs only over the kept pages' tokens.  For query head
  * h (kv-head g = h / G) of request b, over the tokens t < v_j of every page
@@ -172,6 +191,18 @@ QUEST_API quest_status quest_topk_sparse_decode_attn(
     const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
     const float* scores, int32_t k_pages, float sm_scale, int32_t* sel_pages,
     float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * quest_topk_pages_ex followed by quest_sparse_decode_attn in one launch
+ * (plus the split merge); otherwise as quest_topk_sparse_decode_attn, whose
+ * n_sink = n_local = 0 case it is.
+ */
+QUEST_API quest_status quest_topk_sparse_decode_attn_ex(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const float* scores, int32_t k_pages, int32_t n_sink, int32_t n_local,
+    float sm_scale, int32_t* sel_pages, float* out, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 /*
  * Dense decode attention over all L_b tokens (the in-library baseline).

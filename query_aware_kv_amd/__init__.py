@@ -18,8 +18,9 @@ from ._abi import (  # noqa: F401
     QUEST_ERR_WORKSPACE_TOO_SMALL, paged_kv, paged_kv_like,
     quest_decode_attn, quest_estimate, quest_sparse_decode_attn,
     quest_sparse_decode_step, quest_step_workspace_size,
-    quest_stream_read_probe, quest_topk_pages,
-    quest_topk_sparse_decode_attn, quest_update_page_meta,
+    quest_stream_read_probe, quest_topk_pages, quest_topk_pages_ex,
+    quest_topk_sparse_decode_attn, quest_topk_sparse_decode_attn_ex,
+    quest_update_page_meta,
     quest_workspace_size,
 )
 
@@ -48,15 +49,19 @@ TOPK_ATTN_MAX_PAGES = 8192
 
 class SparseDecodeStep:
     """Buffers and call sequence of one sparse decode step for a fixed
-    geometry: quest_estimate, then quest_topk_sparse_decode_attn (Top-K and
-    attention in one launch) -- or, with ``fused_topk=False`` or beyond its
-    size limit, quest_topk_pages then quest_sparse_decode_attn.
+    geometry: quest_estimate, then quest_topk_sparse_decode_attn_ex (Top-K
+    and attention in one launch) -- or, with ``fused_topk=False`` or beyond
+    its size limit, quest_topk_pages_ex then quest_sparse_decode_attn.
+    ``n_sink`` / ``n_local`` force the first / last pages of every row into
+    the selection (0, 0: plain Top-K).
     """
 
     def __init__(self, kv: PagedKV, k_pages: int, sm_scale: float | None = None,
-                 device="cuda", fused_topk: bool = True):
+                 device="cuda", fused_topk: bool = True, n_sink: int = 0,
+                 n_local: int = 0):
         self.kv = kv
         self.k_pages = int(k_pages)
+        self.n_sink, self.n_local = int(n_sink), int(n_local)
         self.sm_scale = default_sm_scale(kv.head_dim) if sm_scale is None else sm_scale
         B, Hq, Hkv = kv.batch, kv.num_q_heads, kv.num_kv_heads
         self.scores = torch.empty(B, Hkv, kv.max_pages_per_seq,
@@ -75,13 +80,13 @@ class SparseDecodeStep:
         quest_estimate(self.kv, q, kmin, kmax, page_table, seq_lens,
                        self.scores, stream)
         if self.fused_topk:
-            quest_topk_sparse_decode_attn(
+            quest_topk_sparse_decode_attn_ex(
                 self.kv, q, k_pool, v_pool, page_table, seq_lens, self.scores,
-                self.k_pages, self.sm_scale, self.sel, self.out,
-                self.workspace, stream)
+                self.k_pages, self.n_sink, self.n_local, self.sm_scale,
+                self.sel, self.out, self.workspace, stream)
             return self.out
-        quest_topk_pages(self.kv, self.scores, seq_lens, self.k_pages,
-                         self.sel, stream)
+        quest_topk_pages_ex(self.kv, self.scores, seq_lens, self.k_pages,
+                            self.n_sink, self.n_local, self.sel, stream)
         quest_sparse_decode_attn(self.kv, q, k_pool, v_pool, page_table,
                                  seq_lens, self.sel, self.k_pages,
                                  self.sm_scale, self.out, self.workspace,

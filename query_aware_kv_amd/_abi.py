@@ -82,6 +82,10 @@ def _load():
         "quest_topk_sparse_decode_attn": [KV, P, P, P, P, P, P, I, ctypes.c_float,
                                           P, P, P, ctypes.c_size_t, P],
         "quest_stream_read_probe": [P, ctypes.c_size_t, P, P],
+        "quest_topk_pages_ex": [KV, P, P, I, I, I, P, P],
+        "quest_topk_sparse_decode_attn_ex": [KV, P, P, P, P, P, P, I, I, I,
+                                             ctypes.c_float, P, P, P,
+                                             ctypes.c_size_t, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -203,6 +207,20 @@ def quest_topk_pages(kv: PagedKV, scores, seq_lens, k_pages: int, sel_pages,
         _stream(stream)))
 
 
+def quest_topk_pages_ex(kv: PagedKV, scores, seq_lens, k_pages: int,
+                        n_sink: int, n_local: int, sel_pages,
+                        stream=None) -> None:
+    _check(LIB.quest_topk_pages_ex(
+        ctypes.byref(kv),
+        _ptr(scores, "scores", torch.float32,
+             (kv.batch, kv.num_kv_heads, kv.max_pages_per_seq)),
+        _ptr(seq_lens, "seq_lens", torch.int32, (kv.batch,)),
+        int(k_pages), int(n_sink), int(n_local),
+        _ptr(sel_pages, "sel_pages", torch.int32,
+             (kv.batch, kv.num_kv_heads, k_pages)),
+        _stream(stream)))
+
+
 def quest_sparse_decode_attn(kv: PagedKV, q, k_pool, v_pool, page_table,
                              seq_lens, sel_pages, k_pages: int,
                              sm_scale: float, out, workspace,
@@ -310,3 +328,27 @@ def quest_stream_read_probe(buf, sink, stream=None) -> None:
     nbytes = buf.numel() * buf.element_size()
     _check(LIB.quest_stream_read_probe(_ptr(buf, "buf"), ctypes.c_size_t(nbytes),
                                        _ptr(sink, "sink"), _stream(stream)))
+
+
+def quest_topk_sparse_decode_attn_ex(kv: PagedKV, q, k_pool, v_pool,
+                                     page_table, seq_lens, scores,
+                                     k_pages: int, n_sink: int, n_local: int,
+                                     sm_scale: float, sel_pages, out,
+                                     workspace, stream=None) -> None:
+    dt = kv.torch_dtype
+    i32 = torch.int32
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.quest_topk_sparse_decode_attn_ex(
+        ctypes.byref(kv),
+        _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv)),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv)),
+        _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
+        _ptr(seq_lens, "seq_lens", i32, (kv.batch,)),
+        _ptr(scores, "scores", torch.float32,
+             (kv.batch, kv.num_kv_heads, kv.max_pages_per_seq)),
+        int(k_pages), int(n_sink), int(n_local), float(sm_scale),
+        _ptr(sel_pages, "sel_pages", i32, (kv.batch, kv.num_kv_heads, k_pages)),
+        _ptr(out, "out", torch.float32, (kv.batch, kv.num_q_heads, kv.head_dim)),
+        _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes),
+        _stream(stream)))

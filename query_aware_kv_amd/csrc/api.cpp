@@ -77,6 +77,27 @@ quest_status check_kv(const quest_paged_kv* kv, const char* fn) {
   return QUEST_OK;
 }
 
+quest_status check_topk_counts(int32_t k_pages, int32_t n_sink, int32_t n_local,
+                               const char* fn) {
+  if (k_pages < 1)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  if (n_sink < 0 || n_local < 0 || (int64_t)n_sink + n_local > k_pages)
+    return fail(QUEST_ERR_INVALID_ARGUMENT,
+                "%s: need 0 <= n_sink, 0 <= n_local, n_sink + n_local <= k_pages "
+                "(got %d, %d, k_pages %d)", fn, n_sink, n_local, k_pages);
+  return QUEST_OK;
+}
+
+// The plain entry points forward to the _ex ones; their messages then name
+// the entry point the caller used.
+void retag(char* msg, const char* from, const char* to) {
+  const size_t nf = strlen(from);
+  if (strncmp(msg, from, nf) != 0) return;
+  char tmp[sizeof(g_last_error)];
+  snprintf(tmp, sizeof(tmp), "%s%s", to, msg + nf);
+  snprintf(msg, sizeof(g_last_error), "%s", tmp);
+}
+
 quest_status check_group(const quest_paged_kv* kv, const char* fn) {
   const int G = kv->num_q_heads / kv->num_kv_heads;
   if (!quest::estimate_supported(G) || !quest::attention_supported(G))
@@ -188,26 +209,37 @@ QUEST_API quest_status quest_estimate(const quest_paged_kv* kv, const void* q,
                     fn);
 }
 
-QUEST_API quest_status quest_topk_pages(const quest_paged_kv* kv,
-                                        const float* scores,
-                                        const int32_t* seq_lens,
-                                        int32_t k_pages, int32_t* sel_pages,
-                                        void* stream) {
-  const char* fn = "quest_topk_pages";
+QUEST_API quest_status quest_topk_pages_ex(const quest_paged_kv* kv,
+                                           const float* scores,
+                                           const int32_t* seq_lens,
+                                           int32_t k_pages, int32_t n_sink,
+                                           int32_t n_local, int32_t* sel_pages,
+                                           void* stream) {
+  const char* fn = "quest_topk_pages_ex";
   quest_status s = check_kv(kv, fn);
   if (s != QUEST_OK) return s;
   REQUIRE_PTR(scores, aligned4(scores));
   REQUIRE_PTR(seq_lens, aligned4(seq_lens));
   REQUIRE_PTR(sel_pages, aligned4(sel_pages));
-  if (k_pages < 1)
-    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  if ((s = check_topk_counts(k_pages, n_sink, n_local, fn)) != QUEST_OK) return s;
   if (kv->max_pages_per_seq > quest::kTopkMaxPages)
     return fail(QUEST_ERR_UNSUPPORTED, "%s: max_pages_per_seq %d > %d", fn,
                 kv->max_pages_per_seq, quest::kTopkMaxPages);
-  return hip_status(quest::launch_topk(*kv, scores, seq_lens, k_pages,
-                                       sel_pages,
+  return hip_status(quest::launch_topk(*kv, scores, seq_lens, k_pages, n_sink,
+                                       n_local, sel_pages,
                                        static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+QUEST_API quest_status quest_topk_pages(const quest_paged_kv* kv,
+                                        const float* scores,
+                                        const int32_t* seq_lens,
+                                        int32_t k_pages, int32_t* sel_pages,
+                                        void* stream) {
+  const quest_status s =
+      quest_topk_pages_ex(kv, scores, seq_lens, k_pages, 0, 0, sel_pages, stream);
+  if (s != QUEST_OK) retag(g_last_error, "quest_topk_pages_ex", "quest_topk_pages");
+  return s;
 }
 
 QUEST_API quest_status quest_sparse_decode_attn(
@@ -227,19 +259,19 @@ QUEST_API quest_status quest_sparse_decode_attn(
                        stream, fn);
 }
 
-QUEST_API quest_status quest_topk_sparse_decode_attn(
+QUEST_API quest_status quest_topk_sparse_decode_attn_ex(
     const quest_paged_kv* kv, const void* q, const void* k_pool,
     const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
-    const float* scores, int32_t k_pages, float sm_scale, int32_t* sel_pages,
-    float* out, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "quest_topk_sparse_decode_attn";
+    const float* scores, int32_t k_pages, int32_t n_sink, int32_t n_local,
+    float sm_scale, int32_t* sel_pages, float* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const char* fn = "quest_topk_sparse_decode_attn_ex";
   quest_status s = check_attention_common(kv, q, k_pool, v_pool, page_table,
                                           seq_lens, sm_scale, out, fn);
   if (s != QUEST_OK) return s;
   REQUIRE_PTR(scores, aligned4(scores));
   REQUIRE_PTR(sel_pages, aligned4(sel_pages));
-  if (k_pages < 1)
-    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  if ((s = check_topk_counts(k_pages, n_sink, n_local, fn)) != QUEST_OK) return s;
   if (kv->max_pages_per_seq > quest::kTopkAttnMaxPages || k_pages > quest::kTopkAttnMaxPages)
     return fail(QUEST_ERR_UNSUPPORTED, "%s: max_pages_per_seq and k_pages must be <= %d",
                 fn, quest::kTopkAttnMaxPages);
@@ -253,9 +285,23 @@ QUEST_API quest_status quest_topk_sparse_decode_attn(
   }
   return hip_status(quest::launch_topk_attention(
                         *kv, q, k_pool, v_pool, page_table, seq_lens, scores,
-                        k_pages, sm_scale, sel_pages, out, workspace,
-                        static_cast<hipStream_t>(stream)),
+                        k_pages, n_sink, n_local, sm_scale, sel_pages, out,
+                        workspace, static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+QUEST_API quest_status quest_topk_sparse_decode_attn(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const float* scores, int32_t k_pages, float sm_scale, int32_t* sel_pages,
+    float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const quest_status s = quest_topk_sparse_decode_attn_ex(
+      kv, q, k_pool, v_pool, page_table, seq_lens, scores, k_pages, 0, 0,
+      sm_scale, sel_pages, out, workspace, workspace_bytes, stream);
+  if (s != QUEST_OK)
+    retag(g_last_error, "quest_topk_sparse_decode_attn_ex",
+          "quest_topk_sparse_decode_attn");
+  return s;
 }
 
 QUEST_API quest_status quest_decode_attn(const quest_paged_kv* kv,

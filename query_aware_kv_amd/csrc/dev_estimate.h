@@ -87,15 +87,26 @@ __device__ __forceinline__ void est_score(const float (&qf)[G][8],
   }
 }
 
-// Lanes 0..3 of the row store the 4 scores (-inf where there is no page).
+// Store the 4 scores (-inf where there is no page): one 16-byte store by
+// lane 0 of the row when the 4 slots are in the row and 16-byte aligned,
+// else lanes 0..3 store one each.
 __device__ __forceinline__ void est_store(float* __restrict__ srow, int j0,
                                           int max_pages, int c,
                                           const int (&pid)[kEstPages],
                                           const float (&s)[kEstPages]) {
-  // one predicated store per page, constant register indices only
+  static_assert(kEstPages == 4, "one float4 per block");
+  float w[kEstPages];
 #pragma unroll
-  for (int u = 0; u < kEstPages; ++u)
-    if (c == u && j0 + u < max_pages) srow[j0 + u] = pid[u] >= 0 ? s[u] : -INFINITY;
+  for (int u = 0; u < kEstPages; ++u) w[u] = pid[u] >= 0 ? s[u] : -INFINITY;
+  float* dst = srow + j0;
+  if (j0 + kEstPages <= max_pages && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+    if (c == 0) *reinterpret_cast<float4*>(dst) = make_float4(w[0], w[1], w[2], w[3]);
+  } else {
+    // one predicated store per page, constant register indices only
+#pragma unroll
+    for (int u = 0; u < kEstPages; ++u)
+      if (c == u && j0 + u < max_pages) dst[u] = w[u];
+  }
 }
 
 }  // namespace quest

@@ -53,13 +53,27 @@ __device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t x) {
 
 // Load a thread's KPT consecutive scores; entries below `limit` are in
 // bounds (limit = the row's length in the buffer), so callers can issue this
-// before they know n.
+// before they know n.  A 16-byte-aligned row is read with 16-byte loads (KPT
+// is a multiple of 4): KPT/4 load instructions per thread instead of KPT.
 template <int BLOCK, int KPT>
 __device__ __forceinline__ void topk_load(const float* __restrict__ s, int limit,
                                           float (&v)[KPT]) {
+  static_assert(KPT % 4 == 0, "16-byte pieces");
   const int base = threadIdx.x * KPT;
+  const bool vec = (reinterpret_cast<uintptr_t>(s) & 15u) == 0;  // row-uniform
+  if (vec && base + KPT <= limit) {
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) v[i] = base + i < limit ? s[base + i] : 0.f;
+    for (int i = 0; i < KPT; i += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(s + base + i);
+      v[i] = x.x;
+      v[i + 1] = x.y;
+      v[i + 2] = x.z;
+      v[i + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) v[i] = base + i < limit ? s[base + i] : 0.f;
+  }
 }
 
 // The page-table entries of the same KPT pages, so that the kept pages' pool
@@ -74,43 +88,58 @@ __device__ __forceinline__ void topk_load_table(const int32_t* __restrict__ pt_r
 
 // Select for one row.  The whole block (BLOCK threads) must call it.
 //   v    : this thread's scores from topk_load (the row has n <= BLOCK*KPT)
+//   n_sink, n_local : when n > k, pages j < n_sink and j >= n - n_local are
+//          kept whatever their scores ("Guide to Quest" §3: attention sinks
+//          and the local window) and the other k - n_sink - n_local slots
+//          go to the best remaining pages; needs n_sink + n_local <= k
 //   out  : the k output slots are kept logical page indices ascending, then
-//          -1; only slots lo <= slot < hi are written, slot s to out[s - lo]
+//          -1; only slots w_lo <= slot < w_hi are written, slot s to
+//          out[s - w_lo]
 //   ent  : if non-null, this thread's page-table entries (topk_load_table);
-//          then phys[s - lo] = the kept page's entry, -1 for the padding (the
-//          pool page list used by attention), for the same slots
+//          then phys[s - w_lo] = the kept page's entry, -1 for the padding
+//          (the pool page list used by attention), for the same slots
+// Forced pages take no part in the radix select: it picks k - n_sink -
+// n_local among the others, and the placement scan counts forced pages as
+// kept, so the list stays ascending.
 template <int BLOCK, int KPT>
 __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
+                         int n_sink, int n_local,
                          int32_t* __restrict__ out,
                          const int32_t (*ent)[KPT],
                          int32_t* __restrict__ phys, TopkSmem<BLOCK>& sm,
-                         int lo = 0, int hi = 0x7fffffff) {
+                         int w_lo = 0, int w_hi = 0x7fffffff) {
   constexpr int NW = BLOCK / kWave;
   static_assert(NW >= 2, "one wave scans while the others clear");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  hi = min(hi, k);
+  w_hi = min(w_hi, k);
   if (n <= k) {  // everything fits: keep every page
-    for (int i = lo + tid; i < hi; i += BLOCK) {
-      out[i - lo] = i < n ? i : -1;
-      if (phys && i >= n) phys[i - lo] = -1;
+    for (int i = w_lo + tid; i < w_hi; i += BLOCK) {
+      out[i - w_lo] = i < n ? i : -1;
+      if (phys && i >= n) phys[i - w_lo] = -1;
     }
     if (phys) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int p = tid * KPT + i;
-        if (p < n && p >= lo && p < hi) phys[p - lo] = (*ent)[i];
+        if (p < n && p >= w_lo && p < w_hi) phys[p - w_lo] = (*ent)[i];
       }
     }
     return;
   }
+  // n > k >= n_sink + n_local: the forced ranges are disjoint and at least
+  // one page competes.
   const int base = tid * KPT;
+  const int local0 = n - n_local;
   uint32_t key[KPT];
+  bool forced[KPT], cand[KPT];
   uint32_t kmn = 0xffffffffu, kmx = 0u;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const bool ok = base + i < n;
-    key[i] = ok ? score_key(v[i]) : 0u;
-    if (ok) {
+    const int p = base + i;
+    forced[i] = p < n && (p < n_sink || p >= local0);
+    cand[i] = p < n && !forced[i];
+    key[i] = cand[i] ? score_key(v[i]) : 0u;
+    if (cand[i]) {
       kmn = min(kmn, key[i]);
       kmx = max(kmx, key[i]);
     }
@@ -132,9 +161,10 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
   for (int i = 0; i < KPT; ++i) key[i] -= kmn;  // rel key; invalid ones wrap, never read
   const uint32_t range = kmx - kmn;
 
-  uint32_t prefix = 0, need = (uint32_t)k;
+  uint32_t prefix = 0, need = (uint32_t)(k - n_sink - n_local);
+  const bool pick = need > 0;  // any competing slot at all
   int shift = 0;  // bits >= shift of the threshold are decided
-  if (range != 0) {
+  if (pick && range != 0) {
     const int bits = 32 - __clz(range);
     int hi = 32;                      // bits >= hi already decided
     shift = bits > 8 ? bits - 8 : 0;  // first digit: top 8 differing bits
@@ -144,9 +174,8 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
       // candidates: keys whose decided bits equal the prefix's
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
-        const bool cand = base + i < n &&
-                          (hi >= 32 || (key[i] >> hi) == (prefix >> hi));
-        if (cand) atomicAdd(&sm.hist[buf][(key[i] >> shift) & 255u], 1u);
+        const bool live = cand[i] && (hi >= 32 || (key[i] >> hi) == (prefix >> hi));
+        if (live) atomicAdd(&sm.hist[buf][(key[i] >> shift) & 255u], 1u);
       }
       __syncthreads();
       if (wid == 0) {
@@ -179,17 +208,16 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
       buf ^= 1;
     }
   }
-  // Kept: keys whose decided bits exceed the threshold's, plus the first
-  // `need` (in page order) whose decided bits equal them.
+  // Kept: forced pages, competing keys whose decided bits exceed the
+  // threshold's, and the first `need` (in page order) whose decided bits
+  // equal them.  "gt" counts the first two kinds.
   const uint32_t thr = shift >= 32 ? 0u : (prefix >> shift);
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    if (base + i < n) {
-      const uint32_t v = key[i] >> shift;
-      gt += v > thr;
-      eq += v == thr;
-    }
+    const uint32_t v = key[i] >> shift;
+    gt += forced[i] || (pick && cand[i] && v > thr);
+    eq += pick && cand[i] && v == thr;
   }
   const uint32_t packed = (gt << 16) | eq;  // both < 65536 (n <= 65535)
   const uint32_t incl = wave_scan_incl(packed);
@@ -205,16 +233,16 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
     if (base + i >= n) break;
     const uint32_t v = key[i] >> shift;
     uint32_t slot = 0xffffffffu;
-    if (v > thr) {
+    if (forced[i] || (pick && cand[i] && v > thr)) {
       slot = gt_before + min(eq_before, need);
       ++gt_before;
-    } else if (v == thr) {
+    } else if (pick && cand[i] && v == thr) {
       if (eq_before < need) slot = gt_before + eq_before;
       ++eq_before;
     }
-    if (slot - (uint32_t)lo < (uint32_t)(hi - lo)) {  // selected, in the window
-      out[slot - lo] = base + i;
-      if (phys) phys[slot - lo] = (*ent)[i];
+    if (slot - (uint32_t)w_lo < (uint32_t)(w_hi - w_lo)) {  // kept, in the window
+      out[slot - w_lo] = base + i;
+      if (phys) phys[slot - w_lo] = (*ent)[i];
     }
   }
 }

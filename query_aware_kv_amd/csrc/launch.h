@@ -30,9 +30,11 @@ hipError_t launch_estimate(const quest_paged_kv& kv, const void* q,
 
 // Largest max_pages_per_seq the Top-K kernel handles.
 constexpr int kTopkMaxPages = 32768;
+// n_sink / n_local: forced pages (0, 0 = plain Top-K); the caller checks
+// n_sink + n_local <= k_pages.
 hipError_t launch_topk(const quest_paged_kv& kv, const float* scores,
-                       const int32_t* seq_lens, int k_pages, int32_t* sel,
-                       hipStream_t stream);
+                       const int32_t* seq_lens, int k_pages, int n_sink,
+                       int n_local, int32_t* sel, hipStream_t stream);
 
 // Attention (sparse when sel != nullptr, else dense over all pages).
 struct AttnPlan {
@@ -62,8 +64,9 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
                                  const void* k_pool, const void* v_pool,
                                  const int32_t* page_table,
                                  const int32_t* seq_lens, const float* scores,
-                                 int k_pages, float sm_scale, int32_t* sel,
-                                 float* out, void* workspace, hipStream_t stream);
+                                 int k_pages, int n_sink, int n_local,
+                                 float sm_scale, int32_t* sel, float* out,
+                                 void* workspace, hipStream_t stream);
 
 // Fused step (estimate -> Top-K -> attention in one launch).
 constexpr int kStepMaxPages = 8192;

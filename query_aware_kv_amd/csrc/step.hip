@@ -129,7 +129,7 @@ __device__ __forceinline__ void est_item(const StepArgs& a, uint32_t t, StepSmem
   int32_t ent[KPT];
   topk_load<kStepThreads, KPT>(srow, n, v);
   topk_load_table<kStepThreads, KPT>(pt_row, n, ent);
-  topk_row<kStepThreads, KPT>(v, n, a.k, a.sel + (int64_t)row * a.k, &ent,
+  topk_row<kStepThreads, KPT>(v, n, a.k, 0, 0, a.sel + (int64_t)row * a.k, &ent,
                               a.phys + (int64_t)row * a.k, sm.topk);
   fence_release();
   __syncthreads();

@@ -1,5 +1,6 @@
-// quest_topk_pages: one workgroup per (request, kv-head) row runs the radix
-// selection of dev_topk.h ("Guide to Quest", §3 and Implementation Step 2).
+// quest_topk_pages(_ex): one workgroup per (request, kv-head) row runs the
+// radix selection of dev_topk.h ("Guide to Quest", §3 and Implementation
+// Step 2), with optional forced sink and local-window pages.
 #include "dev_topk.h"
 #include "launch.h"
 
@@ -10,7 +11,7 @@ template <int BLOCK, int KPT>
 __global__ void __launch_bounds__(BLOCK)
 topk_kernel(const float* __restrict__ scores,
             const int32_t* __restrict__ seq_lens, int Hkv, int max_pages,
-            int k, int32_t* __restrict__ sel) {
+            int k, int n_sink, int n_local, int32_t* __restrict__ sel) {
   __shared__ TopkSmem<BLOCK> sm;
   const int rowid = blockIdx.x;  // b * Hkv + g
   const int b = rowid / Hkv;
@@ -18,29 +19,31 @@ topk_kernel(const float* __restrict__ scores,
   topk_load<BLOCK, KPT>(scores + (int64_t)rowid * max_pages, max_pages, v);
   const int L = seq_lens[b];
   const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
-  topk_row<BLOCK, KPT>(v, n, k, sel + (int64_t)rowid * k, nullptr, nullptr, sm);
+  topk_row<BLOCK, KPT>(v, n, k, n_sink, n_local, sel + (int64_t)rowid * k, nullptr,
+                       nullptr, sm);
 }
 
 template <int BLOCK, int KPT>
 void launch_t(const quest_paged_kv& kv, const float* scores,
-              const int32_t* seq_lens, int k, int32_t* sel,
-              hipStream_t stream) {
+              const int32_t* seq_lens, int k, int n_sink, int n_local,
+              int32_t* sel, hipStream_t stream) {
   topk_kernel<BLOCK, KPT><<<kv.batch * kv.num_kv_heads, BLOCK, 0, stream>>>(
-      scores, seq_lens, kv.num_kv_heads, kv.max_pages_per_seq, k, sel);
+      scores, seq_lens, kv.num_kv_heads, kv.max_pages_per_seq, k, n_sink, n_local,
+      sel);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const quest_paged_kv& kv, const float* scores,
-                       const int32_t* seq_lens, int k_pages, int32_t* sel,
-                       hipStream_t stream) {
+                       const int32_t* seq_lens, int k_pages, int n_sink,
+                       int n_local, int32_t* sel, hipStream_t stream) {
   const int mp = kv.max_pages_per_seq;
-  if (mp <= 1024)       launch_t<256, 4>(kv, scores, seq_lens, k_pages, sel, stream);
-  else if (mp <= 2048)  launch_t<256, 8>(kv, scores, seq_lens, k_pages, sel, stream);
-  else if (mp <= 4096)  launch_t<512, 8>(kv, scores, seq_lens, k_pages, sel, stream);
-  else if (mp <= 8192)  launch_t<1024, 8>(kv, scores, seq_lens, k_pages, sel, stream);
-  else if (mp <= 16384) launch_t<1024, 16>(kv, scores, seq_lens, k_pages, sel, stream);
-  else                  launch_t<1024, 32>(kv, scores, seq_lens, k_pages, sel, stream);
+  if (mp <= 1024)       launch_t<256, 4>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
+  else if (mp <= 2048)  launch_t<256, 8>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
+  else if (mp <= 4096)  launch_t<512, 8>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
+  else if (mp <= 8192)  launch_t<1024, 8>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
+  else if (mp <= 16384) launch_t<1024, 16>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
+  else                  launch_t<1024, 32>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
   return hipGetLastError();
 }
 

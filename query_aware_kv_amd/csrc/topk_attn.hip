@@ -26,7 +26,8 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
                  const uint16_t* __restrict__ v_pool,
                  const int32_t* __restrict__ page_table,
                  const int32_t* __restrict__ seq_lens,
-                 const float* __restrict__ scores, int k, int Hkv,
+                 const float* __restrict__ scores, int k, int n_sink,
+                 int n_local, int Hkv,
                  int max_pages, int num_pool_pages, float qscale,
                  int32_t* __restrict__ sel, float* __restrict__ out,
                  float* __restrict__ ws_o, float* __restrict__ ws_ml) {
@@ -50,7 +51,7 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
   attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
   const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
   const int s0 = split * kAttnWaves * PPW;
-  topk_row<256, KPT>(v, n, k, kept, nullptr, nullptr, sm.topk, s0,
+  topk_row<256, KPT>(v, n, k, n_sink, n_local, kept, nullptr, nullptr, sm.topk, s0,
                      s0 + kAttnWaves * PPW);
   __syncthreads();
 
@@ -103,26 +104,27 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
 template <DType T, int G, int KPT, int PPW>
 void launch_t(const quest_paged_kv& kv, const void* q, const void* k_pool,
               const void* v_pool, const int32_t* page_table,
-              const int32_t* seq_lens, const float* scores, int k, float qscale,
-              int32_t* sel, float* out, float* ws_o, float* ws_ml, int nsplit,
-              hipStream_t stream) {
+              const int32_t* seq_lens, const float* scores, int k, int n_sink,
+              int n_local, float qscale, int32_t* sel, float* out, float* ws_o,
+              float* ws_ml, int nsplit, hipStream_t stream) {
   dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
   topk_attn_kernel<T, G, KPT, PPW><<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), page_table, seq_lens, scores, k,
-      kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages, qscale, sel, out,
+      n_sink, n_local, kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages, qscale, sel, out,
       ws_o, ws_ml);
 }
 
 template <DType T, int KPT>
 void dispatch_g(int G, int ppw, const quest_paged_kv& kv, const void* q,
                 const void* k_pool, const void* v_pool, const int32_t* page_table,
-                const int32_t* seq_lens, const float* scores, int k, float qscale,
-                int32_t* sel, float* out, float* ws_o, float* ws_ml, int nsplit,
-                hipStream_t s) {
+                const int32_t* seq_lens, const float* scores, int k, int n_sink,
+                int n_local, float qscale, int32_t* sel, float* out, float* ws_o,
+                float* ws_ml, int nsplit, hipStream_t s) {
 #define QUEST_TA(GG, PP)                                                         \
   launch_t<T, GG, KPT, PP>(kv, q, k_pool, v_pool, page_table, seq_lens, scores, \
-                           k, qscale, sel, out, ws_o, ws_ml, nsplit, s)
+                           k, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,    \
+                           nsplit, s)
   if (G == 1) {
     if (ppw == 4) QUEST_TA(1, 4);
     else if (ppw == 2) QUEST_TA(1, 2);
@@ -145,8 +147,9 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
                                  const void* k_pool, const void* v_pool,
                                  const int32_t* page_table,
                                  const int32_t* seq_lens, const float* scores,
-                                 int k_pages, float sm_scale, int32_t* sel,
-                                 float* out, void* workspace, hipStream_t stream) {
+                                 int k_pages, int n_sink, int n_local,
+                                 float sm_scale, int32_t* sel, float* out,
+                                 void* workspace, hipStream_t stream) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
   const AttnPlan pl = attention_plan(kv, k_pages);
   const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
@@ -157,17 +160,21 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
   if (kv.dtype == QUEST_F16) {
     if (mp <= 2048)
       dispatch_g<DType::F16, 8>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                                scores, k_pages, qscale, sel, out, ws_o, ws_ml, pl.nsplit, stream);
+                                scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,
+                                pl.nsplit, stream);
     else
       dispatch_g<DType::F16, 32>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                                 scores, k_pages, qscale, sel, out, ws_o, ws_ml, pl.nsplit, stream);
+                                 scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,
+                                pl.nsplit, stream);
   } else {
     if (mp <= 2048)
       dispatch_g<DType::BF16, 8>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                                 scores, k_pages, qscale, sel, out, ws_o, ws_ml, pl.nsplit, stream);
+                                 scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,
+                                pl.nsplit, stream);
     else
       dispatch_g<DType::BF16, 32>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                                  scores, k_pages, qscale, sel, out, ws_o, ws_ml, pl.nsplit, stream);
+                                  scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,
+                                pl.nsplit, stream);
   }
   if (pl.nsplit > 1) launch_merge(kv, ws_o, ws_ml, pl.nsplit, out, stream);
   return hipGetLastError();

@@ -88,17 +88,22 @@ def assert_valid_selection(sel_row: np.ndarray, n: int, k: int):
     assert np.all(np.diff(kept) > 0), "must be strictly ascending"
 
 
-def assert_sets_match(sel_gpu: np.ndarray, s_ora: np.ndarray, lens, k, S=16):
-    """Identical to the oracle's Top-K (on its float64 scores) except for
-    swaps x in G-O, y in O-G with s_y - s_x <= 1e-4 max(|s_x|, |s_y|).
-    Returns the number of swapped pages."""
+def assert_sets_match(sel_gpu: np.ndarray, s_ora: np.ndarray, lens, k, S=16,
+                      n_sink=0, n_local=0):
+    """Identical to the oracle's Top-K (on its float64 scores; with forced
+    sink / local pages if given) except for swaps x in G-O, y in O-G with
+    s_y - s_x <= 1e-4 max(|s_x|, |s_y|).  Returns the number of swapped
+    pages."""
     swaps = 0
     B, H = sel_gpu.shape[:2]
     for b in range(B):
         n = -(-int(lens[b]) // S)
         for g in range(H):
             assert_valid_selection(sel_gpu[b, g], n, k)
-            o = O.topk_pages(s_ora[b, g], n, k)
+            if n_sink or n_local:
+                o = O.topk_pages_forced(s_ora[b, g], n, k, n_sink, n_local)
+            else:
+                o = O.topk_pages(s_ora[b, g], n, k)
             G_ = set(int(x) for x in sel_gpu[b, g] if x >= 0)
             O_ = set(int(x) for x in o if x >= 0)
             only_g, only_o = G_ - O_, O_ - G_
@@ -129,8 +134,10 @@ def oracle_inputs(c, heads=None):
                 seq_lens=c["seq_lens"].cpu().numpy().astype(np.int64))
 
 
-def run_gpu_step(c, k_pages, kmin, kmax, sm_scale, fused_topk=True):
-    step = qa.SparseDecodeStep(c["kv"], k_pages, sm_scale, fused_topk=fused_topk)
+def run_gpu_step(c, k_pages, kmin, kmax, sm_scale, fused_topk=True, n_sink=0,
+                 n_local=0):
+    step = qa.SparseDecodeStep(c["kv"], k_pages, sm_scale, fused_topk=fused_topk,
+                               n_sink=n_sink, n_local=n_local)
     out = step(c["q"], c["k_pool"], c["v_pool"], kmin, kmax,
                c["page_table"], c["seq_lens"])
     torch.cuda.synchronize()

@@ -188,3 +188,26 @@ def test_stream_read_probe_validation():
     assert f(P(FAKE), 1000, P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
     assert "multiple of 16" in qa.LIB.quest_last_error().decode()
     assert f(P(FAKE), 0, P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+
+
+def test_topk_ex_forced_count_validation():
+    k = kv()
+    P = ctypes.c_void_p
+    f = qa.LIB.quest_topk_pages_ex
+    for ns, nl in ((-1, 0), (0, -1), (5, 4), (8, 1)):
+        assert f(ctypes.byref(k), P(FAKE), P(FAKE), 8, ns, nl, P(FAKE), None) == \
+            _abi.QUEST_ERR_INVALID_ARGUMENT
+        assert "n_sink" in qa.LIB.quest_last_error().decode()
+    st, need = ws_size(k, 8)
+    common = [P(FAKE)] * 6                 # q, k_pool, v_pool, pt, lens, scores
+    assert qa.LIB.quest_topk_sparse_decode_attn_ex(
+        ctypes.byref(k), *common, 8, 6, 3, 0.088, P(FAKE), P(FAKE), P(FAKE),
+        need, None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+
+
+def test_plain_calls_name_themselves_in_errors():
+    k = kv()
+    P = ctypes.c_void_p
+    assert qa.LIB.quest_topk_pages(ctypes.byref(k), P(FAKE), P(FAKE), 0,
+                                   P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert qa.LIB.quest_last_error().decode().startswith("quest_topk_pages:")

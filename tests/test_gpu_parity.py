@@ -192,7 +192,7 @@ def _topk_case(rows, n_list, mp, k, seed):
     return s
 
 
-@pytest.mark.parametrize("mp,k", [(64, 8), (1024, 100), (2048, 128),
+@pytest.mark.parametrize("mp,k", [(64, 8), (1024, 100), (1027, 100), (2048, 128),
                                   (4100, 256), (8192, 512), (16384, 1000),
                                   (32768, 4096)])
 def test_topk_kernel_bitexact(mp, k):
