@@ -28,6 +28,10 @@ with its reason in the design notes):
   * the estimate is the unscaled max-form sum (no 1/sqrt(d));
   * a GQA group's page score is the sum of its query heads' estimates;
     query head h belongs to kv-head h // G;
+  * the alternative group rule ("Best Practices" 2: per-head bounds, then the
+    union of the heads' Top-K pages) is ``estimate_heads`` + a per-head
+    selection + ``union_pages``: every query head of the group attends the
+    union, which holds between min(k, n) and G * min(k, n) pages;
   * ties in the Top-K go to the lower page index, and scores compare as
     numbers (-0 == +0); the selection is returned in ascending page order,
     padded with -1;
@@ -52,8 +56,8 @@ import numpy as np
 
 __all__ = [
     "page_valid_tokens", "page_meta", "append_token", "estimate",
-    "topk_pages", "topk_pages_forced", "sparse_attention", "dense_attention",
-    "decode_step", "layer_step",
+    "estimate_heads", "topk_pages", "topk_pages_forced", "union_pages",
+    "sparse_attention", "dense_attention", "decode_step", "layer_step",
 ]
 
 
@@ -156,6 +160,56 @@ def estimate(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray,
                 total += np.maximum(qh * lo, qh * hi).sum(axis=1)
             s[b, g, :n] = total
     return s
+
+
+def estimate_heads(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray,
+                   page_table: np.ndarray, seq_lens: np.ndarray,
+                   page_size: int, max_pages: Optional[int] = None) -> np.ndarray:
+    """The same upper bound for every QUERY head separately.
+
+    [G] §2 upper-bound inequality for query head h against the box of its
+    kv-head h // G; [G] Best Practices 2 computes these per-head bounds
+    before taking the union of the heads' Top-K pages.
+
+    q: [B, Hq, d].  Returns float64 [B, Hq, max_pages], -inf past n_b.
+    """
+    B, Hq, d = q.shape
+    H = kmin.shape[1]
+    G = Hq // H
+    mp = page_table.shape[1] if max_pages is None else max_pages
+    s = np.full((B, Hq, mp), -np.inf)
+    for b in range(B):
+        n = -(-int(seq_lens[b]) // page_size)
+        if n == 0:
+            continue
+        pages = page_table[b, :n].astype(np.int64)
+        for h in range(Hq):
+            lo = kmin[pages, h // G, :]            # [n, d]
+            hi = kmax[pages, h // G, :]
+            qh = q[b, h, :]
+            s[b, h, :n] = np.maximum(qh * lo, qh * hi).sum(axis=1)
+    return s
+
+
+def union_pages(sel_heads: np.ndarray, group: int) -> np.ndarray:
+    """Union of the query heads' page selections, per kv-head.
+
+    [G] Best Practices 2: the group loads the union of its heads' Top-K
+    pages once, and every head of the group attends all of them.
+    sel_heads: [B, Hq, k] per-head lists (-1 = unused), Hq = Hkv * group.
+    Returns int64 [B, Hkv, group * k]: the union ascending, then -1s.
+    """
+    B, Hq, k = sel_heads.shape
+    H = Hq // group
+    out = np.full((B, H, group * k), -1, dtype=np.int64)
+    for b in range(B):
+        for g in range(H):
+            pages = set()
+            for h in range(g * group, (g + 1) * group):
+                pages.update(int(x) for x in sel_heads[b, h] if x >= 0)
+            u = sorted(pages)
+            out[b, g, :len(u)] = u
+    return out
 
 
 def topk_pages(scores: np.ndarray, n_pages: int, k: int) -> np.ndarray:

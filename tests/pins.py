@@ -434,6 +434,80 @@ def check_forced_special_cases(O, seed=22):
         raise AssertionError("n_sink + n_local > k must be refused")
 
 
+# ---------------------------------------------------------------- GQA union
+
+def check_union_golden(O):
+    g = load_golden("union_worked.json")
+    box = np.array(g["kmin"], dtype=np.float64)[:, None, :]      # [P=4, H=1, d=2]
+    pt = np.arange(4)[None, :]
+    lens = np.array([4])
+    k = g["k"]
+
+    def run(qh):
+        q = np.array(qh, dtype=np.float64)[None]                 # [1, 2, 2]
+        s = O.estimate_heads(q, box, box, pt, lens, 1)
+        sel = np.stack([O.topk_pages(s[0, h], 4, k) for h in range(2)])[None]
+        return s, O.union_pages(sel, 2), q
+
+    s, u, q = run(g["q_heads"])
+    assert np.array_equal(s[0], np.array(g["expect_bounds"], dtype=np.float64))
+    assert list(u[0, 0]) == g["expect_union"]
+    s_sum = O.estimate(q, box, box, pt, lens, 1)
+    assert list(O.topk_pages(s_sum[0, 0], 4, k)) == g["expect_sum_rule"]
+    _, u2, _ = run(g["q_heads_agree"])
+    assert list(u2[0, 0]) == g["expect_union_agree"]
+
+
+def check_estimate_heads_sum_and_bound(O, seed=23):
+    """The heads' bounds add up to the group bound (the sum rule), and each
+    head's bound is at least its true max q_h . k over the page's tokens."""
+    rng = np.random.default_rng(seed)
+    for G in (1, 2, 4):
+        c = small_cache(rng, B=2, Hq=2 * G, H=2, d=16, S=4, lens=(13, 9))
+        kmin, kmax = _meta(O, c)
+        sh = O.estimate_heads(c["q"], kmin, kmax, c["page_table"], c["seq_lens"], c["S"])
+        sg = O.estimate(c["q"], kmin, kmax, c["page_table"], c["seq_lens"], c["S"])
+        for b in range(2):
+            n = -(-int(c["seq_lens"][b]) // c["S"])
+            for g in range(2):
+                tot = sh[b, g * G:(g + 1) * G, :n].sum(axis=0)
+                assert np.allclose(tot, sg[b, g, :n], rtol=0, atol=1e-9)
+                for h in range(g * G, (g + 1) * G):
+                    for j in range(n):
+                        keys = _valid_tokens(c, b, j, g)
+                        assert sh[b, h, j] >= (keys @ c["q"][b, h]).max() - 1e-9
+            assert np.all(np.isneginf(sh[b, :, n:]))
+
+
+def check_union_properties(O, seed=24):
+    rng = np.random.default_rng(seed)
+    for trial in range(40):
+        G = int(rng.choice([1, 2, 4, 8]))
+        H, B = 2, 2
+        k = int(rng.integers(1, 9))
+        n = int(rng.integers(1, 20))
+        sel = np.stack([np.stack([O.topk_pages(rng.integers(-3, 4, n).astype(float), n, k)
+                                  for _ in range(H * G)]) for _ in range(B)])
+        u = O.union_pages(sel, G)
+        assert u.shape == (B, H, G * k)
+        for b in range(B):
+            for g in range(H):
+                row = [int(x) for x in u[b, g]]
+                kept = [x for x in row if x >= 0]
+                m = len(kept)
+                assert row[m:] == [-1] * (G * k - m)          # padding at the end
+                assert kept == sorted(set(kept))              # ascending, no repeats
+                heads = [set(int(x) for x in sel[b, h] if x >= 0)
+                         for h in range(g * G, (g + 1) * G)]
+                for hs in heads:
+                    assert hs <= set(kept)                    # holds every head's pages
+                for x in kept:
+                    assert any(x in hs for hs in heads)       # and nothing else
+                assert max(len(hs) for hs in heads) <= m <= min(n, G * min(k, n))
+                if G == 1:
+                    assert row[:k] == [int(x) for x in sel[b, g]]
+
+
 # ---------------------------------------------------------------- attention
 
 def check_attention_golden(O):
@@ -648,6 +722,7 @@ ALL_CHECKS = [
     check_topk_golden, check_topk_bruteforce, check_topk_special_cases,
     check_topk_library,
     check_forced_golden, check_forced_bruteforce, check_forced_special_cases,
+    check_union_golden, check_estimate_heads_sum_and_bound, check_union_properties,
     check_attention_golden, check_sparse_all_equals_dense, check_dense_vs_sdpa,
     check_attention_special_cases, check_attention_restricts_to_selection,
     check_gqa_head_mapping, check_empty_sequence,

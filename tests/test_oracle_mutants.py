@@ -106,6 +106,55 @@ def forced_ignored(scores, n, k, ns, nl):
     return O.topk_pages(scores, n, k)
 
 
+def heads_wrong_map(q, kmin, kmax, pt, lens, S, max_pages=None):
+    """query head h read against kv-head h % Hkv instead of h // G"""
+    B, Hq, d = q.shape
+    H = kmin.shape[1]
+    G = Hq // H
+    perm = np.array([(h % H) * G + h // H for h in range(Hq)])
+    out = O.estimate_heads(q[:, perm], kmin, kmax, pt, lens, S, max_pages)
+    inv = np.argsort(perm)
+    return out[:, inv]
+
+
+def heads_group_sum(q, kmin, kmax, pt, lens, S, max_pages=None):
+    """every head gets its group's summed bound"""
+    B, Hq, d = q.shape
+    G = Hq // kmin.shape[1]
+    s = O.estimate(q, kmin, kmax, pt, lens, S, max_pages)
+    return np.repeat(s, G, axis=1)
+
+
+def union_drops_last_head(sel, G):
+    if G == 1:
+        return O.union_pages(sel, G)
+    B, Hq, k = sel.shape
+    s2 = sel.copy()
+    s2[:, G - 1::G] = -1
+    return O.union_pages(s2, G)
+
+
+def union_unsorted(sel, G):
+    u = O.union_pages(sel, G)
+    for b in range(u.shape[0]):
+        for g in range(u.shape[1]):
+            m = int((u[b, g] >= 0).sum())
+            u[b, g, :m] = u[b, g, :m][::-1]
+    return u
+
+
+def union_with_repeats(sel, G):
+    B, Hq, k = sel.shape
+    H = Hq // G
+    out = np.full((B, H, G * k), -1, dtype=np.int64)
+    for b in range(B):
+        for g in range(H):
+            allp = sorted(int(x) for h in range(g * G, (g + 1) * G)
+                          for x in sel[b, h] if x >= 0)
+            out[b, g, :len(allp)] = allp
+    return out
+
+
 def meta_all_slots(k_pool, pt, lens, S):
     full = np.array([-(-int(L) // S) * S for L in lens])
     return O.page_meta(k_pool, pt, full, S)
@@ -172,6 +221,11 @@ MUTANTS = {
     "forced_full_competition": dict(topk_pages_forced=forced_full_competition),
     "forced_roles_swapped": dict(topk_pages_forced=forced_roles_swapped),
     "forced_ignored": dict(topk_pages_forced=forced_ignored),
+    "heads_wrong_map": dict(estimate_heads=heads_wrong_map),
+    "heads_group_sum": dict(estimate_heads=heads_group_sum),
+    "union_drops_last_head": dict(union_pages=union_drops_last_head),
+    "union_unsorted": dict(union_pages=union_unsorted),
+    "union_with_repeats": dict(union_pages=union_with_repeats),
     "meta_reads_invalid_slots": dict(page_meta=meta_all_slots),
     "meta_unsigned_zero": dict(page_meta=meta_plain_minmax),
     "append_never_resets": dict(append_token=append_no_reset),
