@@ -20,6 +20,9 @@ Workloads (each prints ONE JSON line):
   pages scattered through a shared pool.
 * ``sweep``: the longchat layer over contexts 4K..128K x budgets 256..4096
   tokens (one line holding every point).
+* ``gqa_union``: one 32/8-head GQA layer at 32K, the group-sum selection
+  against per-head selection + union ("Guide to Quest", Best Practices 2):
+  time, bytes and pages kept per kv-head for each rule.
 
 Inputs are seeded synthetic tensors drawn on the GPU and resident in HBM
 before timing starts.  The line carries the step time (the metric),
@@ -293,8 +296,30 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
             kv, c["q"], c["k_pool"], c["v_pool"], c["page_table"],
             c["seq_lens"], st.scores, k, sm, st.sel, st.out, st.workspace)
 
+    def topk_attn_forced(i):   # the pages' default: 2 sink + 2 local pages
+        c, st = insts[i], steps[i]
+        qa.quest_topk_sparse_decode_attn_ex(
+            kv, c["q"], c["k_pool"], c["v_pool"], c["page_table"],
+            c["seq_lens"], st.scores, k, 2, 2, sm, st.sel, st.out, st.workspace)
+
+    def topk_sep(i):
+        c, st = insts[i], steps[i]
+        qa.quest_topk_pages(kv, st.scores, c["seq_lens"], k, st.sel)
+
+    def attn_sep(i):
+        c, st = insts[i], steps[i]
+        qa.quest_sparse_decode_attn(kv, c["q"], c["k_pool"], c["v_pool"],
+                                    c["page_table"], c["seq_lens"], st.sel, k,
+                                    sm, st.out, st.workspace)
+
     reps = max(10, args.steps // rot)
     us_est = call_us(torch, est, rot, reps)
+    other = {}
+    if steps[0].fused_topk:
+        other["quest_topk_sparse_decode_attn_ex (2 sink + 2 local pages)"] = \
+            round(call_us(torch, topk_attn_forced, rot, reps), 3)
+    other["quest_topk_pages"] = round(call_us(torch, topk_sep, rot, reps), 3)
+    other["quest_sparse_decode_attn"] = round(call_us(torch, attn_sep, rot, reps), 3)
     us_ta = call_us(torch, topk_attn, rot, reps) if steps[0].fused_topk else None
 
     sels = [st.sel.cpu().numpy() for st in steps]
@@ -312,7 +337,7 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
         calls["quest_topk_sparse_decode_attn"] = (us_ta, ta_bytes)
     dbytes = sum(dense_bytes(l, kv.num_kv_heads, kv.num_q_heads) for l in lens_all) / rot
     return dict(t_graph=t_graph, t_eager=t_eager, t_batch=t_batch,
-                t_dense=t_dense, bytes=avg,
+                t_dense=t_dense, bytes=avg, other_calls=other,
                 calls=calls, dense_bytes=dbytes, insts=insts, kv=kv, k_pages=k,
                 sm=sm)
 
@@ -374,6 +399,7 @@ def bench_longchat(args, torch, qa, synth):
         "graph_batch_us_per_step": round(tb["mean"], 3),
         "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
         "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
+        "other_call_us": r["other_calls"],
         "roofline": roofline(r["calls"], traffic_recorded=True),
         "gpu": torch.cuda.get_device_name(0),
     }
@@ -434,7 +460,8 @@ def bench_sweep(args, torch, qa, synth):
                 "effective_GBps": round(r["bytes"]["total"] / (us * 1e-6) / 1e9, 1),
                 "dense_us": round(us_dense, 3),
                 "speedup_vs_dense": round(us_dense / us, 3),
-                "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()}})
+                "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
+                "other_call_us": r["other_calls"]})
             print(json.dumps({"progress": points[-1]}), file=sys.stderr, flush=True)
             del r
             torch.cuda.empty_cache()
@@ -543,6 +570,64 @@ def bench_gqa_multistep(args, torch, qa, synth):
     }
 
 
+def bench_gqa_union(args, torch, qa, synth):
+    """One GQA layer (32 q-heads / 8 kv-heads, 32K, 2048-token budget): the
+    group-sum rule against the per-head + union rule, same caches."""
+    rot = args.rotate
+    wls = [synth.gqa_multistep_workload(seed=4 + 1000 * i, layers=1, steps=0)
+           for i in range(rot)]
+    insts = [make_layer(qa, synth, wl) for wl in wls]
+    torch.cuda.synchronize()
+    kv = insts[0]["kv"]
+    k = wls[0].k_pages
+    sm = 1.0 / math.sqrt(128)
+    G = kv.num_q_heads // kv.num_kv_heads
+    sums = [qa.SparseDecodeStep(kv, k, sm) for _ in range(rot)]
+    unions = [qa.UnionDecodeStep(kv, k, sm) for _ in range(rot)]
+
+    def call(steps, i):
+        c = insts[i]
+        steps[i](c["q"], c["k_pool"], c["v_pool"], c["kmin"], c["kmax"],
+                 c["page_table"], c["seq_lens"])
+
+    res = {}
+    for name, steps in (("sum", sums), ("union", unions)):
+        for i in range(rot):
+            call(steps, i)
+        torch.cuda.synchronize()
+        g = capture(torch, lambda steps=steps: [call(steps, i) for i in range(rot)])
+        t = Timer(torch).run(lambda i: g.replay(), max(2, args.steps // rot), 2, 1,
+                             events=False)
+        lens = [int(x) for x in insts[0]["seq_lens"].cpu()]
+        b = [step_bytes(lens, kv.num_kv_heads, kv.num_q_heads, k,
+                        sel=steps[i].sel.cpu().numpy())["total"] for i in range(rot)]
+        kept = [float((steps[i].sel >= 0).sum()) / (kv.batch * kv.num_kv_heads)
+                for i in range(rot)]
+        res[name] = dict(us=t["mean"] / rot, bytes=sum(b) / rot,
+                         pages=sum(kept) / rot)
+    u, sm_ = res["union"], res["sum"]
+    return {
+        "metric": "µs/decode step, GQA 32/8 layer, per-head Top-K + union vs "
+                  "group-sum Top-K",
+        "value": round(u["us"], 3), "unit": "us/step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(u["us"] / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) fp16, 4 outlier channels x8 per kv-head)",
+        "config": {"workload": "gqa_layer_union_rule", "batch": 1, "q_heads": 32,
+                   "kv_heads": 8, "ctx": 32768, "budget_tokens": 2048,
+                   "rotating_caches": rot},
+        "union": {"us_per_step": round(u["us"], 3), "bytes_per_step": int(u["bytes"]),
+                  "effective_GBps": round(u["bytes"] / (u["us"] * 1e-6) / 1e9, 1),
+                  "pages_per_kv_head": round(u["pages"], 1)},
+        "group_sum": {"us_per_step": round(sm_["us"], 3),
+                      "bytes_per_step": int(sm_["bytes"]),
+                      "effective_GBps": round(sm_["bytes"] / (sm_["us"] * 1e-6) / 1e9, 1),
+                      "pages_per_kv_head": round(sm_["pages"], 1)},
+        "union_pages_over_k": round(u["pages"] / k, 3),
+        "group": G, "gpu": torch.cuda.get_device_name(0)}
+
+
 # ------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(gpu, budget_s):
@@ -634,7 +719,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="longchat",
-                    choices=["longchat", "gqa_multistep", "ragged", "sweep"])
+                    choices=["longchat", "gqa_multistep", "ragged", "sweep",
+                             "gqa_union"])
     ap.add_argument("--rotate", type=int, default=8,
                     help="independent caches the steps cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -674,7 +760,8 @@ def main():
     import synth
 
     fn = {"longchat": bench_longchat, "gqa_multistep": bench_gqa_multistep,
-          "ragged": bench_ragged, "sweep": bench_sweep}[args.workload]
+          "ragged": bench_ragged, "sweep": bench_sweep,
+          "gqa_union": bench_gqa_union}[args.workload]
     print(json.dumps(fn(args, torch, qa, synth)), flush=True)
 
 

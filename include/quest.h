@@ -126,6 +126,39 @@ QUEST_API quest_status quest_estimate(
     float* scores, void* stream);
 
 /*
+ * Per-query-head estimate.  [G] §2 upper-bound inequality for each query
+ * head h against the boxes of its kv-head g = h / G, as [G] Best Practices 2
+ * asks for before the union of the heads' selections:
+ *   scores[b][h][j] = sum_i max(q[b][h][i] * kmin[p][g][i],
+ *                               q[b][h][i] * kmax[p][g][i]),
+ * p = page_table[b][j], j < n_b; -inf for n_b <= j < max_pages_per_seq.
+ * `scores` is float32 [batch][Hq][max_pages_per_seq]; each box is read once
+ * for the G heads.  Arithmetic as quest_estimate (whose group sum these
+ * rows add up to, up to float32 rounding).
+ */
+QUEST_API quest_status quest_estimate_heads(
+    const quest_paged_kv* kv, const void* q, const void* kmin,
+    const void* kmax, const int32_t* page_table, const int32_t* seq_lens,
+    float* scores, void* stream);
+
+/*
+ * Union of a GQA group's per-head selections.  [G] Best Practices 2: the
+ * kv-head loads the union of its query heads' Top-K pages once and every
+ * head of the group attends all of them.  sel_heads is int32
+ * [batch][Hq][k_pages] (each query head's list, as written by
+ * quest_topk_pages(_ex) run on quest_estimate_heads' scores with a
+ * descriptor whose num_kv_heads = num_q_heads); sel_union is int32
+ * [batch][Hkv][G * k_pages]: for each (b, g) the distinct pages listed by
+ * heads g*G .. g*G+G-1, ascending, then -1.  Entries outside
+ * [0, max_pages_per_seq) are ignored.  Pass sel_union to
+ * quest_sparse_decode_attn with k_pages' = G * k_pages.  Requires
+ * max_pages_per_seq <= 32768.
+ */
+QUEST_API quest_status quest_union_pages(
+    const quest_paged_kv* kv, const int32_t* sel_heads, int32_t k_pages,
+    int32_t* sel_union, void* stream);
+
+/*
  * Top-K page selection.  [G] §3: keep the k_pages pages with the highest
  * scores; Implementation Step 2: a request with n_b <= k_pages keeps all of
  * its pages.  For each (b, g) row the kept set is the first min(k_pages, n_b)

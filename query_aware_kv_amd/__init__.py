@@ -18,6 +18,7 @@ from ._abi import (  # noqa: F401
     QUEST_ERR_WORKSPACE_TOO_SMALL, paged_kv, paged_kv_like,
     quest_decode_attn, quest_estimate, quest_sparse_decode_attn,
     quest_sparse_decode_step, quest_step_workspace_size,
+    quest_estimate_heads, quest_union_pages,
     quest_stream_read_probe, quest_topk_pages, quest_topk_pages_ex,
     quest_topk_sparse_decode_attn, quest_topk_sparse_decode_attn_ex,
     quest_update_page_meta,
@@ -89,6 +90,49 @@ class SparseDecodeStep:
                             self.n_sink, self.n_local, self.sel, stream)
         quest_sparse_decode_attn(self.kv, q, k_pool, v_pool, page_table,
                                  seq_lens, self.sel, self.k_pages,
+                                 self.sm_scale, self.out, self.workspace,
+                                 stream)
+        return self.out
+
+
+class UnionDecodeStep:
+    """The GQA group rule of per-head selection + union ("Guide to Quest",
+    Best Practices 2): quest_estimate_heads, quest_topk_pages_ex per query
+    head, quest_union_pages, then quest_sparse_decode_attn over the union
+    (up to G * k_pages pages per kv-head, shared by the group's heads)."""
+
+    def __init__(self, kv: PagedKV, k_pages: int, sm_scale: float | None = None,
+                 device="cuda", n_sink: int = 0, n_local: int = 0):
+        self.kv = kv
+        self.k_pages = int(k_pages)
+        self.n_sink, self.n_local = int(n_sink), int(n_local)
+        self.sm_scale = default_sm_scale(kv.head_dim) if sm_scale is None else sm_scale
+        B, Hq, Hkv = kv.batch, kv.num_q_heads, kv.num_kv_heads
+        self.group = Hq // Hkv
+        # per-head rows: the same geometry seen with one row per query head
+        self.kv_heads = paged_kv(B, Hq, Hq, kv.num_pool_pages,
+                                 kv.max_pages_per_seq, kv.torch_dtype,
+                                 kv.head_dim, kv.page_size)
+        self.scores = torch.empty(B, Hq, kv.max_pages_per_seq,
+                                  dtype=torch.float32, device=device)
+        self.sel_heads = torch.empty(B, Hq, self.k_pages, dtype=torch.int32,
+                                     device=device)
+        self.sel = torch.empty(B, Hkv, self.group * self.k_pages,
+                               dtype=torch.int32, device=device)
+        self.out = torch.empty(B, Hq, kv.head_dim, dtype=torch.float32,
+                               device=device)
+        self.workspace = alloc_workspace(kv, self.group * self.k_pages, device)
+
+    def __call__(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_lens,
+                 stream=None) -> torch.Tensor:
+        quest_estimate_heads(self.kv, q, kmin, kmax, page_table, seq_lens,
+                             self.scores, stream)
+        quest_topk_pages_ex(self.kv_heads, self.scores, seq_lens, self.k_pages,
+                            self.n_sink, self.n_local, self.sel_heads, stream)
+        quest_union_pages(self.kv, self.sel_heads, self.k_pages, self.sel,
+                          stream)
+        quest_sparse_decode_attn(self.kv, q, k_pool, v_pool, page_table,
+                                 seq_lens, self.sel, self.group * self.k_pages,
                                  self.sm_scale, self.out, self.workspace,
                                  stream)
         return self.out

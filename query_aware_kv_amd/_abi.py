@@ -83,6 +83,8 @@ def _load():
                                           P, P, P, ctypes.c_size_t, P],
         "quest_stream_read_probe": [P, ctypes.c_size_t, P, P],
         "quest_topk_pages_ex": [KV, P, P, I, I, I, P, P],
+        "quest_estimate_heads": [KV, P, P, P, P, P, P, P],
+        "quest_union_pages": [KV, P, I, P, P],
         "quest_topk_sparse_decode_attn_ex": [KV, P, P, P, P, P, P, I, I, I,
                                              ctypes.c_float, P, P, P,
                                              ctypes.c_size_t, P],
@@ -351,4 +353,32 @@ def quest_topk_sparse_decode_attn_ex(kv: PagedKV, q, k_pool, v_pool,
         _ptr(sel_pages, "sel_pages", i32, (kv.batch, kv.num_kv_heads, k_pages)),
         _ptr(out, "out", torch.float32, (kv.batch, kv.num_q_heads, kv.head_dim)),
         _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes),
+        _stream(stream)))
+
+
+def quest_estimate_heads(kv: PagedKV, q, kmin, kmax, page_table, seq_lens,
+                         scores, stream=None) -> None:
+    dt = kv.torch_dtype
+    _check(LIB.quest_estimate_heads(
+        ctypes.byref(kv),
+        _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
+        _ptr(kmin, "kmin", dt, _meta_shape(kv)),
+        _ptr(kmax, "kmax", dt, _meta_shape(kv)),
+        _ptr(page_table, "page_table", torch.int32, (kv.batch, kv.max_pages_per_seq)),
+        _ptr(seq_lens, "seq_lens", torch.int32, (kv.batch,)),
+        _ptr(scores, "scores", torch.float32,
+             (kv.batch, kv.num_q_heads, kv.max_pages_per_seq)),
+        _stream(stream)))
+
+
+def quest_union_pages(kv: PagedKV, sel_heads, k_pages: int, sel_union,
+                      stream=None) -> None:
+    G = kv.num_q_heads // kv.num_kv_heads
+    _check(LIB.quest_union_pages(
+        ctypes.byref(kv),
+        _ptr(sel_heads, "sel_heads", torch.int32,
+             (kv.batch, kv.num_q_heads, k_pages)),
+        int(k_pages),
+        _ptr(sel_union, "sel_union", torch.int32,
+             (kv.batch, kv.num_kv_heads, G * k_pages)),
         _stream(stream)))

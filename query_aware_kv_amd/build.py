@@ -33,7 +33,8 @@ COMMON_FLAGS = [
 ]
 
 SOURCES = ["api.cpp", "meta.hip", "estimate.hip", "topk.hip", "attention.hip",
-           "topk_attn.hip", "step.hip", "probe.hip"]
+           "topk_attn.hip", "step.hip", "probe.hip",
+           "union.hip"]
 
 
 def _compile(src: str) -> str:

@@ -188,12 +188,11 @@ QUEST_API quest_status quest_update_page_meta(
                     fn);
 }
 
-QUEST_API quest_status quest_estimate(const quest_paged_kv* kv, const void* q,
-                                      const void* kmin, const void* kmax,
-                                      const int32_t* page_table,
-                                      const int32_t* seq_lens, float* scores,
-                                      void* stream) {
-  const char* fn = "quest_estimate";
+static quest_status run_estimate(const quest_paged_kv* kv, const void* q,
+                          const void* kmin, const void* kmax,
+                          const int32_t* page_table, const int32_t* seq_lens,
+                          float* scores, bool per_head, void* stream,
+                          const char* fn) {
   quest_status s = check_kv(kv, fn);
   if (s != QUEST_OK) return s;
   if ((s = check_group(kv, fn)) != QUEST_OK) return s;
@@ -204,8 +203,49 @@ QUEST_API quest_status quest_estimate(const quest_paged_kv* kv, const void* q,
   REQUIRE_PTR(seq_lens, aligned4(seq_lens));
   REQUIRE_PTR(scores, aligned4(scores));
   return hip_status(quest::launch_estimate(*kv, q, kmin, kmax, page_table,
-                                           seq_lens, scores,
+                                           seq_lens, scores, per_head,
                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+QUEST_API quest_status quest_estimate(const quest_paged_kv* kv, const void* q,
+                                      const void* kmin, const void* kmax,
+                                      const int32_t* page_table,
+                                      const int32_t* seq_lens, float* scores,
+                                      void* stream) {
+  return run_estimate(kv, q, kmin, kmax, page_table, seq_lens, scores, false,
+                      stream, "quest_estimate");
+}
+
+QUEST_API quest_status quest_estimate_heads(const quest_paged_kv* kv,
+                                            const void* q, const void* kmin,
+                                            const void* kmax,
+                                            const int32_t* page_table,
+                                            const int32_t* seq_lens,
+                                            float* scores, void* stream) {
+  return run_estimate(kv, q, kmin, kmax, page_table, seq_lens, scores, true,
+                      stream, "quest_estimate_heads");
+}
+
+QUEST_API quest_status quest_union_pages(const quest_paged_kv* kv,
+                                         const int32_t* sel_heads,
+                                         int32_t k_pages, int32_t* sel_union,
+                                         void* stream) {
+  const char* fn = "quest_union_pages";
+  quest_status s = check_kv(kv, fn);
+  if (s != QUEST_OK) return s;
+  REQUIRE_PTR(sel_heads, aligned4(sel_heads));
+  REQUIRE_PTR(sel_union, aligned4(sel_union));
+  if (k_pages < 1)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  const int64_t G = kv->num_q_heads / kv->num_kv_heads;
+  if (G * k_pages > (int64_t)1 << 30)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: G * k_pages too large", fn);
+  if (kv->max_pages_per_seq > quest::kTopkMaxPages)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: max_pages_per_seq %d > %d", fn,
+                kv->max_pages_per_seq, quest::kTopkMaxPages);
+  return hip_status(quest::launch_union(*kv, sel_heads, k_pages, sel_union,
+                                        static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -87,6 +87,31 @@ __device__ __forceinline__ void est_score(const float (&qf)[G][8],
   }
 }
 
+// Per-query-head bounds of the 4 pages: s[h][u] for the G heads of the
+// group, from one read of each box ("Guide to Quest", Best Practices 2).
+template <DType T, int G>
+__device__ __forceinline__ void est_score_heads(const float (&qf)[G][8],
+                                                const int (&pid)[kEstPages],
+                                                const uint4 (&lo)[kEstPages],
+                                                const uint4 (&hi)[kEstPages],
+                                                float (&s)[G][kEstPages]) {
+#pragma unroll
+  for (int u = 0; u < kEstPages; ++u) {
+    float a[8], z[8];
+    widen8<T>(lo[u], a);
+    widen8<T>(hi[u], z);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.f;
+      if (pid[u] >= 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += fmaxf(qf[h][e] * a[e], qf[h][e] * z[e]);
+      }
+      s[h][u] = row16_sum(acc);
+    }
+  }
+}
+
 // Store the 4 scores (-inf where there is no page): one 16-byte store by
 // lane 0 of the row when the 4 slots are in the row and 16-byte aligned,
 // else lanes 0..3 store one each.

@@ -1,6 +1,7 @@
-// quest_estimate: the query-aware upper bound of every page of every
-// (request, kv-head) row ("Guide to Quest", §2 upper-bound inequality; the
-// arithmetic lives in dev_estimate.h).
+// quest_estimate / quest_estimate_heads: the query-aware upper bound of every
+// page of every (request, kv-head) row -- or of every query head
+// ("Guide to Quest", §2 upper-bound inequality; Best Practices 2 for the
+// per-head form; the arithmetic lives in dev_estimate.h).
 //
 // Work mapping: a 16-lane DPP row owns one kv-head g of one request and walks
 // blocks of 4 consecutive pages, prefetching the next block's page ids while
@@ -14,7 +15,9 @@ namespace {
 
 constexpr int kRowsPerBlock = 16;  // 256 threads
 
-template <DType T, int G>
+// PER_HEAD: scores hold one row per query head ([B][Hq][max_pages], head
+// g * G + h) instead of one per kv-head with the group's sum.
+template <DType T, int G, bool PER_HEAD>
 __global__ void __launch_bounds__(256)
 estimate_kernel(const uint16_t* __restrict__ q,
                 const uint16_t* __restrict__ kmin,
@@ -30,7 +33,7 @@ estimate_kernel(const uint16_t* __restrict__ q,
   const int g = row % Hkv;
   const int jb0 = row / Hkv;
   const int32_t* pt_row = page_table + (int64_t)b * max_pages;
-  float* srow = scores + ((int64_t)b * Hkv + g) * max_pages;
+  float* srow = scores + ((int64_t)b * Hkv + g) * (PER_HEAD ? G : 1) * max_pages;
   // The length, the first table entries and q are independent loads.
   int ent[kEstPages];
   est_table(pt_row, max_pages, jb0 * kEstPages, ent);
@@ -45,13 +48,21 @@ estimate_kernel(const uint16_t* __restrict__ q,
     uint4 lo[kEstPages], hi[kEstPages];
     est_load_meta(kmin, kmax, pid, Hkv, g, c, lo, hi);
     est_table(pt_row, max_pages, (jb + rows_per_head) * kEstPages, ent);  // prefetch
-    float s[kEstPages];
-    est_score<T, G>(qf, pid, lo, hi, s);
-    est_store(srow, jb * kEstPages, max_pages, c, pid, s);
+    if constexpr (PER_HEAD) {
+      float s[G][kEstPages];
+      est_score_heads<T, G>(qf, pid, lo, hi, s);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        est_store(srow + (int64_t)h * max_pages, jb * kEstPages, max_pages, c, pid, s[h]);
+    } else {
+      float s[kEstPages];
+      est_score<T, G>(qf, pid, lo, hi, s);
+      est_store(srow, jb * kEstPages, max_pages, c, pid, s);
+    }
   }
 }
 
-template <DType T, int G>
+template <DType T, int G, bool PER_HEAD>
 void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
               const void* kmax, const int32_t* page_table,
               const int32_t* seq_lens, float* scores, hipStream_t stream) {
@@ -66,22 +77,22 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
   const int64_t rows = rph * Hkv;
   dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock),
             (unsigned)kv.batch);
-  estimate_kernel<T, G><<<grid, 256, 0, stream>>>(
+  estimate_kernel<T, G, PER_HEAD><<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kmin),
       static_cast<const uint16_t*>(kmax), page_table, seq_lens, scores, Hkv,
       kv.max_pages_per_seq, (int)rph, kv.num_pool_pages);
 }
 
-template <DType T>
+template <DType T, bool PER_HEAD>
 void dispatch_group(int G, const quest_paged_kv& kv, const void* q,
                     const void* kmin, const void* kmax,
                     const int32_t* page_table, const int32_t* seq_lens,
                     float* scores, hipStream_t stream) {
   switch (G) {
-    case 1: launch_t<T, 1>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
-    case 2: launch_t<T, 2>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
-    case 4: launch_t<T, 4>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
-    default: launch_t<T, 8>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
+    case 1: launch_t<T, 1, PER_HEAD>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
+    case 2: launch_t<T, 2, PER_HEAD>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
+    case 4: launch_t<T, 4, PER_HEAD>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
+    default: launch_t<T, 8, PER_HEAD>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
   }
 }
 
@@ -94,12 +105,19 @@ bool estimate_supported(int group) {
 hipError_t launch_estimate(const quest_paged_kv& kv, const void* q,
                            const void* kmin, const void* kmax,
                            const int32_t* page_table, const int32_t* seq_lens,
-                           float* scores, hipStream_t stream) {
+                           float* scores, bool per_head, hipStream_t stream) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
-  if (kv.dtype == QUEST_F16)
-    dispatch_group<DType::F16>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, stream);
-  else
-    dispatch_group<DType::BF16>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, stream);
+  if (per_head) {
+    if (kv.dtype == QUEST_F16)
+      dispatch_group<DType::F16, true>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, stream);
+    else
+      dispatch_group<DType::BF16, true>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, stream);
+  } else {
+    if (kv.dtype == QUEST_F16)
+      dispatch_group<DType::F16, false>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, stream);
+    else
+      dispatch_group<DType::BF16, false>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, stream);
+  }
   return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "common.h"
 #include "quest.h"
 
 namespace quest {
@@ -23,10 +24,17 @@ hipError_t launch_meta_append(const quest_paged_kv& kv, void* k_pool,
 
 // True when an estimate kernel exists for this group size.
 bool estimate_supported(int group);
+// per_head: one score row per query head ([B][Hq][max_pages]) instead of
+// one per kv-head holding the group's sum.
 hipError_t launch_estimate(const quest_paged_kv& kv, const void* q,
                            const void* kmin, const void* kmax,
                            const int32_t* page_table, const int32_t* seq_lens,
-                           float* scores, hipStream_t stream);
+                           float* scores, bool per_head, hipStream_t stream);
+
+// union.hip: per (request, kv-head), the ascending union of the G query
+// heads' k-entry lists, -1 padded to G*k; max_pages <= kTopkMaxPages.
+hipError_t launch_union(const quest_paged_kv& kv, const int32_t* sel_heads,
+                        int k_pages, int32_t* sel_union, hipStream_t stream);
 
 // Largest max_pages_per_seq the Top-K kernel handles.
 constexpr int kTopkMaxPages = 32768;

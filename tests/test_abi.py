@@ -211,3 +211,18 @@ def test_plain_calls_name_themselves_in_errors():
     assert qa.LIB.quest_topk_pages(ctypes.byref(k), P(FAKE), P(FAKE), 0,
                                    P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
     assert qa.LIB.quest_last_error().decode().startswith("quest_topk_pages:")
+
+
+def test_union_and_heads_validation():
+    k = kv(num_q_heads=32, num_kv_heads=8)
+    P = ctypes.c_void_p
+    assert qa.LIB.quest_union_pages(ctypes.byref(k), P(FAKE), 0, P(FAKE), None) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert qa.LIB.quest_union_pages(ctypes.byref(k), None, 8, P(FAKE), None) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+    big = kv(max_pages_per_seq=40000)
+    assert qa.LIB.quest_union_pages(ctypes.byref(big), P(FAKE), 8, P(FAKE), None) == \
+        _abi.QUEST_ERR_UNSUPPORTED
+    assert qa.LIB.quest_estimate_heads(ctypes.byref(k), *([P(FAKE)] * 5), None,
+                                       None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert "scores" in qa.LIB.quest_last_error().decode()
