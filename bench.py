@@ -23,6 +23,8 @@ Workloads (each prints ONE JSON line):
 * ``gqa_union``: one 32/8-head GQA layer at 32K, the group-sum selection
   against per-head selection + union ("Guide to Quest", Best Practices 2):
   time, bytes and pages kept per kv-head for each rule.
+* ``page32``: 16- against 32-token pages at 32K and 128K (same token
+  budget), and the one-shot prefill metadata build against writing K.
 
 Inputs are seeded synthetic tensors drawn on the GPU and resident in HBM
 before timing starts.  The line carries the step time (the metric),
@@ -231,7 +233,8 @@ def stream_read_ceiling(torch, qa, gib=4, reps=10):
 def make_layer(qa, synth, wl, layer=0, dev="cuda"):
     c = synth.draw_layer(wl, layer, dev)
     kv = qa.paged_kv(wl.batch, wl.num_q_heads, wl.num_kv_heads,
-                     wl.pool_pages(), wl.max_pages, wl.torch_dtype)
+                     wl.pool_pages(), wl.max_pages, wl.torch_dtype,
+                     page_size=wl.page_size)
     kmin, kmax = qa.alloc_meta(kv)
     qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], kmin, kmax,
                               c["page_table"], c["seq_lens"])
@@ -324,7 +327,8 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
 
     sels = [st.sel.cpu().numpy() for st in steps]
     lens_all = [[int(x) for x in c["seq_lens"].cpu()] for c in insts]
-    bstep = [step_bytes(lens_all[i], kv.num_kv_heads, kv.num_q_heads, k, sel=sels[i])
+    bstep = [step_bytes(lens_all[i], kv.num_kv_heads, kv.num_q_heads, k, sel=sels[i],
+                        page_size=kv.page_size)
              for i in range(rot)]
     avg = {key: sum(b[key] for b in bstep) / rot for key in bstep[0]}
     B = kv.batch
@@ -335,7 +339,8 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
     calls = {"quest_estimate": (us_est, est_bytes)}
     if us_ta is not None:
         calls["quest_topk_sparse_decode_attn"] = (us_ta, ta_bytes)
-    dbytes = sum(dense_bytes(l, kv.num_kv_heads, kv.num_q_heads) for l in lens_all) / rot
+    dbytes = sum(dense_bytes(l, kv.num_kv_heads, kv.num_q_heads, page_size=kv.page_size)
+                 for l in lens_all) / rot
     return dict(t_graph=t_graph, t_eager=t_eager, t_batch=t_batch,
                 t_dense=t_dense, bytes=avg, other_calls=other,
                 calls=calls, dense_bytes=dbytes, insts=insts, kv=kv, k_pages=k,
@@ -628,6 +633,77 @@ def bench_gqa_union(args, torch, qa, synth):
         "group": G, "gpu": torch.cuda.get_device_name(0)}
 
 
+def bench_page32(args, torch, qa, synth):
+    """Page size 16 against 32 ("Guide to Quest", Best Practices 1) on the
+    LongChat layer at 32K and 128K with the same 2048-token budget, and the
+    one-shot prefill metadata build against writing the prompt's K."""
+    import dataclasses
+    rows = []
+    for ctx in (32768, 131072):
+        for S in (16, 32):
+            touched_mib = ctx / 1024 * 16 / S + 2048 / 64
+            rot = min(args.rotate, max(2, math.ceil(768 / touched_mib)))
+            wls = [dataclasses.replace(synth.longchat_layer_workload(ctx, 2048,
+                                                                     seed=1 + 1000 * i),
+                                       page_size=S, name=f"p{S}_ctx{ctx}")
+                   for i in range(rot)]
+            r = time_single_layer(args, torch, qa, synth, wls,
+                                  with_dense=not args.no_dense, percentiles=False)
+            us = min(r["t_graph"]["mean"], r["t_eager"]["mean"], r["t_batch"]["mean"])
+            c, kv = r["insts"][0], r["kv"]
+            # prefill: rebuild every box of the prompt vs writing its K once
+            kmin, kmax = qa.alloc_meta(kv)
+            k_bytes = c["k_pool"].numel() * c["k_pool"].element_size()
+            dst = torch.empty_like(c["k_pool"])
+            stream = torch.cuda.current_stream()
+
+            def ev(fn, reps=10):
+                fn()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / reps
+
+            meta_us = ev(lambda: qa.quest_update_page_meta(
+                kv, c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"],
+                c["seq_lens"]))
+            kwrite_us = ev(lambda: dst.fill_(1.0))
+            meta_bytes = k_bytes + 2 * kv.num_pool_pages * kv.num_kv_heads * 128 * 2
+            rows.append({
+                "ctx": ctx, "page_size": S, "k_pages": wls[0].k_pages,
+                "us_per_step": round(us, 3),
+                "bytes_per_step": int(r["bytes"]["total"]),
+                "effective_GBps": round(r["bytes"]["total"] / (us * 1e-6) / 1e9, 1),
+                "meta_bytes_per_step": int(r["bytes"]["meta"]),
+                "dense_us": round(r["t_dense"]["mean"], 3) if r["t_dense"] else None,
+                "call_us": {k_: round(v[0], 3) for k_, v in r["calls"].items()},
+                "prefill_meta_build_us": round(meta_us, 2),
+                "prefill_meta_GBps": round(meta_bytes / (meta_us * 1e-6) / 1e9, 1),
+                "prefill_k_write_us": round(kwrite_us, 2),
+                "meta_build_over_k_write": round(meta_us / kwrite_us, 3)})
+            print(json.dumps({"progress": rows[-1]}), file=sys.stderr, flush=True)
+            del r, c, dst, kmin, kmax
+            torch.cuda.empty_cache()
+    at = [x for x in rows if x["ctx"] == 131072 and x["page_size"] == 32][0]
+    return {
+        "metric": "µs/decode step with 32-token pages, 32 heads, 128K ctx, "
+                  "2048-token budget (16-token pages alongside)",
+        "value": at["us_per_step"], "unit": "us/step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(at["us_per_step"] / 1e3, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic (as longchat, per point)",
+        "config": {"workload": "page_size_16_vs_32", "ctx": [32768, 131072],
+                   "page_size": [16, 32], "budget_tokens": 2048,
+                   "value_at": "ctx 131072, page size 32"},
+        "points": rows, "gpu": torch.cuda.get_device_name(0)}
+
+
 # ------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(gpu, budget_s):
@@ -720,7 +796,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="longchat",
                     choices=["longchat", "gqa_multistep", "ragged", "sweep",
-                             "gqa_union"])
+                             "gqa_union", "page32"])
     ap.add_argument("--rotate", type=int, default=8,
                     help="independent caches the steps cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -761,7 +837,7 @@ def main():
 
     fn = {"longchat": bench_longchat, "gqa_multistep": bench_gqa_multistep,
           "ragged": bench_ragged, "sweep": bench_sweep,
-          "gqa_union": bench_gqa_union}[args.workload]
+          "gqa_union": bench_gqa_union, "page32": bench_page32}[args.workload]
     print(json.dumps(fn(args, torch, qa, synth)), flush=True)
 
 

@@ -66,8 +66,8 @@ quest_status check_kv(const quest_paged_kv* kv, const char* fn) {
   if (kv->head_dim != quest::kHeadDim)
     return fail(QUEST_ERR_UNSUPPORTED, "%s: head_dim %d (only 128)", fn,
                 kv->head_dim);
-  if (kv->page_size != quest::kPageSize)
-    return fail(QUEST_ERR_UNSUPPORTED, "%s: page_size %d (only 16)", fn,
+  if (!quest::page_size_supported(kv->page_size))
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: page_size %d (16 or 32)", fn,
                 kv->page_size);
   if (kv->dtype != QUEST_F16 && kv->dtype != QUEST_BF16)
     return fail(QUEST_ERR_UNSUPPORTED, "%s: dtype %d", fn, kv->dtype);
@@ -386,6 +386,8 @@ QUEST_API quest_status quest_sparse_decode_step(
   if (kv->max_pages_per_seq > quest::kStepMaxPages)
     return fail(QUEST_ERR_UNSUPPORTED, "%s: max_pages_per_seq %d > %d", fn,
                 kv->max_pages_per_seq, quest::kStepMaxPages);
+  if (kv->page_size != quest::kTileRows)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: 16-token pages only", fn);
   const size_t need = quest::step_workspace_bytes(*kv, k_pages);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(QUEST_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu",

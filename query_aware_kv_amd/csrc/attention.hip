@@ -13,7 +13,7 @@
 namespace quest {
 namespace {
 
-template <DType T, int G, int PPW>
+template <DType T, int G, int PPW, int SUB>
 __global__ void __launch_bounds__(256)
 attn_split_kernel(const uint16_t* __restrict__ q,
                   const uint16_t* __restrict__ k_pool,
@@ -49,23 +49,31 @@ attn_split_kernel(const uint16_t* __restrict__ q,
   const int L = seq_lens[b];
   float qf[G][8];
   attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
-  const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
+  constexpr int S = SUB * kTileRows;
+  const int n = pages_of(L, S, max_pages);
   int pj[PPW];
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi)
     pj[pi] = (jr[pi] >= 0 && jr[pi] < n && pp[pi] >= 0 && pp[pi] < num_pool_pages)
                  ? jr[pi] : -1;
-  uint4 kx[PPW][4], vx[PPW][4];
+  uint4 kx[PPW][SUB][4], vx[PPW][SUB][4];
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi)
-    if (pj[pi] >= 0) attn_load_tile(k_pool, v_pool, pp[pi], Hkv, g, r, c, kx[pi], vx[pi]);
+#pragma unroll
+    for (int s = 0; s < SUB; ++s)
+      if (pj[pi] >= 0 && L - pj[pi] * S - s * kTileRows > 0)
+        attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
+                       kx[pi][s], vx[pi][s]);
 
   AttnState<G> st;
   attn_init(st);
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi)
-    if (pj[pi] >= 0)
-      attn_page<T, G>(st, qf, kx[pi], vx[pi], min(kPageSize, L - pj[pi] * kPageSize), r);
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      const int v = pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
+      if (v > 0) attn_page<T, G>(st, qf, kx[pi][s], vx[pi][s], v, r);
+    }
   attn_combine_rows(st);
   attn_stage_wave(st, sm, wid, r, c);
   __syncthreads();
@@ -102,7 +110,12 @@ attn_merge_kernel(const float* __restrict__ ws_o,
                out + qh * kHeadDim, sm);
 }
 
-int max_ppw(int G) { return G == 1 ? 4 : G <= 4 ? 2 : 1; }
+// Pages per wave the registers allow: 16-token tiles per wave at most 4
+// (G = 1), 2 (G <= 4) or 1 (G = 8).
+int max_ppw(int G, int sub) {
+  const int tiles = G == 1 ? 4 : G <= 4 ? 2 : 1;
+  return tiles / sub > 0 ? tiles / sub : 1;
+}
 
 using Plan = AttnPlan;
 
@@ -114,7 +127,7 @@ AttnPlan attention_plan(const quest_paged_kv& kv, int list_len) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
   const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
   int ppw = 1;
-  for (int cand = max_ppw(G); cand > 1; cand /= 2) {
+  for (int cand = max_ppw(G, kv.page_size / kTileRows); cand > 1; cand /= 2) {
     const int64_t ns = (list_len + kAttnWaves * cand - 1) / (kAttnWaves * cand);
     if (units * ns >= 1024) { ppw = cand; break; }
   }
@@ -137,39 +150,46 @@ void launch_merge(const quest_paged_kv& kv, const float* ws_o,
 
 namespace {
 
-template <DType T, int G, int PPW>
+template <DType T, int G, int PPW, int SUB>
 void launch_split(const quest_paged_kv& kv, const void* q, const void* k_pool,
                   const void* v_pool, const int32_t* page_table,
                   const int32_t* seq_lens, const int32_t* sel, int list_len,
                   float qscale, float* out, float* ws_o, float* ws_ml,
                   int nsplit, hipStream_t stream) {
   dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
-  attn_split_kernel<T, G, PPW><<<grid, 256, 0, stream>>>(
+  attn_split_kernel<T, G, PPW, SUB><<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), page_table, seq_lens, sel,
       list_len, kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages,
       qscale, out, ws_o, ws_ml);
 }
 
-template <DType T>
+template <DType T, int SUB>
 void dispatch(int G, int ppw, const quest_paged_kv& kv, const void* q,
               const void* k_pool, const void* v_pool,
               const int32_t* page_table, const int32_t* seq_lens,
               const int32_t* sel, int list_len, float qscale, float* out,
               float* ws_o, float* ws_ml, int nsplit, hipStream_t stream) {
-#define QUEST_SPLIT(GG, PP)                                                   \
-  launch_split<T, GG, PP>(kv, q, k_pool, v_pool, page_table, seq_lens, sel,  \
-                          list_len, qscale, out, ws_o, ws_ml, nsplit, stream)
+#define QUEST_SPLIT(GG, PP)                                                        \
+  launch_split<T, GG, PP, SUB>(kv, q, k_pool, v_pool, page_table, seq_lens, sel,  \
+                               list_len, qscale, out, ws_o, ws_ml, nsplit, stream)
+  // ppw never exceeds max_ppw(G, SUB): only those variants are built
   if (G == 1) {
-    if (ppw == 4) QUEST_SPLIT(1, 4);
-    else if (ppw == 2) QUEST_SPLIT(1, 2);
+    if constexpr (SUB == 1) {
+      if (ppw == 4) { QUEST_SPLIT(1, 4); return; }
+    }
+    if (ppw == 2) QUEST_SPLIT(1, 2);
     else QUEST_SPLIT(1, 1);
   } else if (G == 2) {
-    if (ppw == 2) QUEST_SPLIT(2, 2);
-    else QUEST_SPLIT(2, 1);
+    if constexpr (SUB == 1) {
+      if (ppw == 2) { QUEST_SPLIT(2, 2); return; }
+    }
+    QUEST_SPLIT(2, 1);
   } else if (G == 4) {
-    if (ppw == 2) QUEST_SPLIT(4, 2);
-    else QUEST_SPLIT(4, 1);
+    if constexpr (SUB == 1) {
+      if (ppw == 2) { QUEST_SPLIT(4, 2); return; }
+    }
+    QUEST_SPLIT(4, 1);
   } else {
     QUEST_SPLIT(8, 1);
   }
@@ -200,14 +220,18 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = ws_o ? ws_o + attention_ml_offset(slots) : nullptr;
   const float qscale = sm_scale * kLog2e;
-  if (kv.dtype == QUEST_F16)
-    dispatch<DType::F16>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                         sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit,
-                         stream);
-  else
-    dispatch<DType::BF16>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                          sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit,
-                          stream);
+#define QUEST_DISPATCH(TT, SS)                                                    \
+  dispatch<TT, SS>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens, sel,   \
+                   list_len, qscale, out, ws_o, ws_ml, pl.nsplit, stream)
+  const bool s32 = kv.page_size == 32;
+  if (kv.dtype == QUEST_F16) {
+    if (s32) QUEST_DISPATCH(DType::F16, 2);
+    else QUEST_DISPATCH(DType::F16, 1);
+  } else {
+    if (s32) QUEST_DISPATCH(DType::BF16, 2);
+    else QUEST_DISPATCH(DType::BF16, 1);
+  }
+#undef QUEST_DISPATCH
   if (pl.nsplit > 1) launch_merge(kv, ws_o, ws_ml, pl.nsplit, out, stream);
   return hipGetLastError();
 }

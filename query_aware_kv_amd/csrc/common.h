@@ -7,8 +7,17 @@
 namespace quest {
 
 constexpr int kHeadDim = 128;
-constexpr int kPageSize = 16;
+// Kernels read pages as 16-token tiles: a page of S tokens (S = 16 or 32,
+// the page sizes of "Guide to Quest", Best Practices 1) is S / 16 tiles.
+constexpr int kTileRows = 16;
 constexpr int kWave = 64;
+
+__host__ __device__ constexpr bool page_size_supported(int S) { return S == 16 || S == 32; }
+
+// Pages of a request of L tokens, clamped to the row's capacity.
+__device__ __forceinline__ int pages_of(int L, int S, int max_pages) {
+  return L > 0 ? min((L + S - 1) / S, max_pages) : 0;
+}
 
 enum class DType : int { F16 = 0, BF16 = 1 };
 

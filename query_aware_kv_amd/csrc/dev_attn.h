@@ -52,12 +52,20 @@ __device__ __forceinline__ void attn_load_q(const uint16_t* __restrict__ q,
   }
 }
 
-// 16-byte pieces of one (page, kv-head) tile for lane (r, c).
+// Element offset of 16-token tile s of pool page p, kv-head g, for pages of
+// SUB * 16 tokens ([P][Hkv][SUB*16][128]).
+template <int SUB>
+__device__ __forceinline__ int64_t attn_tile_offset(int64_t p, int Hkv, int g, int s) {
+  return ((p * Hkv + g) * SUB + s) * (int64_t)(kTileRows * kHeadDim);
+}
+
+// 16-byte pieces of one 16-token tile (at element offset `tile`) for lane
+// (r, c): rows r, r+4, r+8, r+12, channels 8c..8c+7.
 __device__ __forceinline__ void attn_load_tile(const uint16_t* __restrict__ k_pool,
                                                const uint16_t* __restrict__ v_pool,
-                                               int64_t p, int Hkv, int g, int r, int c,
+                                               int64_t tile, int r, int c,
                                                uint4 (&kx)[4], uint4 (&vx)[4]) {
-  const int64_t tile = (p * Hkv + g) * (kPageSize * kHeadDim) + c * 8;
+  tile += c * 8;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     kx[i] = *reinterpret_cast<const uint4*>(k_pool + tile + (r + 4 * i) * kHeadDim);
@@ -65,7 +73,8 @@ __device__ __forceinline__ void attn_load_tile(const uint16_t* __restrict__ k_po
   }
 }
 
-// Fold one page (v valid tokens) into the row group's state.
+// Fold one 16-token tile (its first v tokens valid; v <= 0 changes nothing)
+// into the row group's state.
 template <DType T, int G>
 __device__ __forceinline__ void attn_page(AttnState<G>& st, const float (&qf)[G][8],
                                           const uint4 (&kx)[4], const uint4 (&vx)[4],

@@ -25,7 +25,7 @@ estimate_kernel(const uint16_t* __restrict__ q,
                 const int32_t* __restrict__ page_table,
                 const int32_t* __restrict__ seq_lens,
                 float* __restrict__ scores, int Hkv, int max_pages,
-                int rows_per_head, int num_pool_pages) {
+                int rows_per_head, int num_pool_pages, int page_size) {
   const int b = blockIdx.y;
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
@@ -40,7 +40,7 @@ estimate_kernel(const uint16_t* __restrict__ q,
   const int L = seq_lens[b];
   float qf[G][8];
   est_load_q<T, G>(q, ((int64_t)b * Hkv + g) * G, c, qf);
-  const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
+  const int n = pages_of(L, page_size, max_pages);
 
   for (int jb = jb0; jb * kEstPages < max_pages; jb += rows_per_head) {
     int pid[kEstPages];
@@ -80,7 +80,7 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
   estimate_kernel<T, G, PER_HEAD><<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kmin),
       static_cast<const uint16_t*>(kmax), page_table, seq_lens, scores, Hkv,
-      kv.max_pages_per_seq, (int)rph, kv.num_pool_pages);
+      kv.max_pages_per_seq, (int)rph, kv.num_pool_pages, kv.page_size);
 }
 
 template <DType T, bool PER_HEAD>

@@ -47,21 +47,21 @@ meta_rebuild_kernel(const uint16_t* __restrict__ k_pool,
                     const int32_t* __restrict__ page_table,
                     const int32_t* __restrict__ seq_lens,
                     const int32_t* __restrict__ first_token, int Hkv,
-                    int max_pages, int num_pool_pages) {
+                    int max_pages, int num_pool_pages, int S) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (unit >= max_pages * Hkv) return;
   const int j = unit / Hkv, g = unit - (unit / Hkv) * Hkv;
   const int L = seq_lens[b];
-  const int v = min(kPageSize, L - j * kPageSize);  // valid tokens in page j
+  const int v = min(S, L - j * S);  // valid tokens in page j
   if (v <= 0) return;
   const int f = first_token ? first_token[b] : 0;
-  const int t0 = max(0, f - j * kPageSize);          // first token to fold
+  const int t0 = max(0, f - j * S);  // first token to fold
   if (t0 >= v) return;
   const int64_t p = page_table[(int64_t)b * max_pages + j];
   if (p < 0 || p >= num_pool_pages) return;  // not a pool page: nothing to read
-  const int64_t tile = (p * Hkv + g) * (kPageSize * kHeadDim);
+  const int64_t tile = (p * Hkv + g) * ((int64_t)S * kHeadDim);
   const uint4* src = reinterpret_cast<const uint4*>(k_pool + tile);
   const int c = lane & 15, r = lane >> 4;
 
@@ -69,7 +69,7 @@ meta_rebuild_kernel(const uint16_t* __restrict__ k_pool,
 #pragma unroll
   for (int e = 0; e < 8; ++e) { mn[e] = INT_MAX; mx[e] = INT_MIN; }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {  // rows r + 4i of up to 32; v <= S bounds them
     const int t = r + 4 * i;
     if (t >= t0 && t < v) fold8(src[t * 16 + c], mn, mx);
   }
@@ -99,7 +99,7 @@ meta_append_kernel(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
                    const int32_t* __restrict__ seq_lens,
                    const uint16_t* __restrict__ k_new,
                    const uint16_t* __restrict__ v_new, int Hkv, int max_pages,
-                   int num_pool_pages) {
+                   int num_pool_pages, int S) {
   const int b = blockIdx.y;
   const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -107,12 +107,12 @@ meta_append_kernel(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
   const int L = seq_lens[b];
   if (L <= 0) return;
   const int pos = L - 1;
-  const int j = pos / kPageSize, slot = pos - j * kPageSize;
+  const int j = pos / S, slot = pos - j * S;
   if (j >= max_pages) return;
   const int64_t p = page_table[(int64_t)b * max_pages + j];
   if (p < 0 || p >= num_pool_pages) return;
   const int c = lane & 15;
-  const int64_t row = ((p * Hkv + g) * kPageSize + slot) * kHeadDim + c * 8;
+  const int64_t row = ((p * Hkv + g) * S + slot) * kHeadDim + c * 8;
   const int64_t src = ((int64_t)b * Hkv + g) * kHeadDim + c * 8;
   if (lane >= 16) {
     *reinterpret_cast<uint4*>(v_pool + row) =
@@ -151,7 +151,7 @@ hipError_t launch_meta_rebuild(const quest_paged_kv& kv, const void* k_pool,
   meta_rebuild_kernel<<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(k_pool), static_cast<uint16_t*>(kmin),
       static_cast<uint16_t*>(kmax), page_table, seq_lens, first_token,
-      kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages);
+      kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages, kv.page_size);
   return hipGetLastError();
 }
 
@@ -166,7 +166,7 @@ hipError_t launch_meta_append(const quest_paged_kv& kv, void* k_pool,
       static_cast<uint16_t*>(kmin), static_cast<uint16_t*>(kmax), page_table,
       seq_lens, static_cast<const uint16_t*>(k_new),
       static_cast<const uint16_t*>(v_new), kv.num_kv_heads,
-      kv.max_pages_per_seq, kv.num_pool_pages);
+      kv.max_pages_per_seq, kv.num_pool_pages, kv.page_size);
   return hipGetLastError();
 }
 

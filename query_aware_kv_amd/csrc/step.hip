@@ -83,7 +83,7 @@ __device__ __forceinline__ uint32_t fetch_add_acq_rel(uint32_t* p, uint32_t v) {
 
 __device__ __forceinline__ int row_pages(const StepArgs& a, int b) {
   const int L = a.seq_lens[b];
-  return L > 0 ? min((L + kPageSize - 1) / kPageSize, a.max_pages) : 0;
+  return pages_of(L, kTileRows, a.max_pages);  // 16-token pages only
 }
 
 template <int G>
@@ -187,13 +187,15 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, uint32_t t, StepSme
   uint4 kx[PPW][4], vx[PPW][4];
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi)
-    if (pj[pi] >= 0) attn_load_tile(a.k_pool, a.v_pool, pp[pi], a.Hkv, g, r, c, kx[pi], vx[pi]);
+    if (pj[pi] >= 0)
+      attn_load_tile(a.k_pool, a.v_pool, attn_tile_offset<1>(pp[pi], a.Hkv, g, 0), r, c,
+                     kx[pi], vx[pi]);
   AttnState<G> st;
   attn_init(st);
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi)
     if (pj[pi] >= 0)
-      attn_page<T, G>(st, qf, kx[pi], vx[pi], min(kPageSize, L - pj[pi] * kPageSize), r);
+      attn_page<T, G>(st, qf, kx[pi], vx[pi], min(kTileRows, L - pj[pi] * kTileRows), r);
   attn_combine_rows(st);
   attn_stage_wave(st, sm.attn, wid, r, c);
   __syncthreads();

@@ -11,14 +11,15 @@ template <int BLOCK, int KPT>
 __global__ void __launch_bounds__(BLOCK)
 topk_kernel(const float* __restrict__ scores,
             const int32_t* __restrict__ seq_lens, int Hkv, int max_pages,
-            int k, int n_sink, int n_local, int32_t* __restrict__ sel) {
+            int k, int n_sink, int n_local, int page_size,
+            int32_t* __restrict__ sel) {
   __shared__ TopkSmem<BLOCK> sm;
   const int rowid = blockIdx.x;  // b * Hkv + g
   const int b = rowid / Hkv;
   float v[KPT];  // issued together with the length load
   topk_load<BLOCK, KPT>(scores + (int64_t)rowid * max_pages, max_pages, v);
   const int L = seq_lens[b];
-  const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
+  const int n = pages_of(L, page_size, max_pages);
   topk_row<BLOCK, KPT>(v, n, k, n_sink, n_local, sel + (int64_t)rowid * k, nullptr,
                        nullptr, sm);
 }
@@ -29,7 +30,7 @@ void launch_t(const quest_paged_kv& kv, const float* scores,
               int32_t* sel, hipStream_t stream) {
   topk_kernel<BLOCK, KPT><<<kv.batch * kv.num_kv_heads, BLOCK, 0, stream>>>(
       scores, seq_lens, kv.num_kv_heads, kv.max_pages_per_seq, k, n_sink, n_local,
-      sel);
+      kv.page_size, sel);
 }
 
 }  // namespace

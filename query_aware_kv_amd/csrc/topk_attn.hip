@@ -19,7 +19,7 @@
 namespace quest {
 namespace {
 
-template <DType T, int G, int KPT, int PPW>
+template <DType T, int G, int KPT, int PPW, int SUB>
 __global__ void __launch_bounds__(256)
 topk_attn_kernel(const uint16_t* __restrict__ q,
                  const uint16_t* __restrict__ k_pool,
@@ -49,7 +49,8 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
   const int L = seq_lens[b];
   float qf[G][8];
   attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
-  const int n = L > 0 ? min((L + kPageSize - 1) / kPageSize, max_pages) : 0;
+  constexpr int S = SUB * kTileRows;
+  const int n = pages_of(L, S, max_pages);
   const int s0 = split * kAttnWaves * PPW;
   topk_row<256, KPT>(v, n, k, n_sink, n_local, kept, nullptr, nullptr, sm.topk, s0,
                      s0 + kAttnWaves * PPW);
@@ -67,16 +68,23 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
     pp[pi] = (j >= 0 && j < n) ? page_table[(int64_t)b * max_pages + j] : -1;
     pj[pi] = (pp[pi] >= 0 && pp[pi] < num_pool_pages) ? j : -1;
   }
-  uint4 kx[PPW][4], vx[PPW][4];
+  uint4 kx[PPW][SUB][4], vx[PPW][SUB][4];
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi)
-    if (pj[pi] >= 0) attn_load_tile(k_pool, v_pool, pp[pi], Hkv, g, r, c, kx[pi], vx[pi]);
+#pragma unroll
+    for (int s = 0; s < SUB; ++s)
+      if (pj[pi] >= 0 && L - pj[pi] * S - s * kTileRows > 0)
+        attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
+                       kx[pi][s], vx[pi][s]);
   AttnState<G> st;
   attn_init(st);
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi)
-    if (pj[pi] >= 0)
-      attn_page<T, G>(st, qf, kx[pi], vx[pi], min(kPageSize, L - pj[pi] * kPageSize), r);
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      const int v = pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
+      if (v > 0) attn_page<T, G>(st, qf, kx[pi][s], vx[pi][s], v, r);
+    }
   attn_combine_rows(st);
   __syncthreads();  // the Top-K scratch becomes the attention scratch
   attn_stage_wave(st, sm.attn, wid, r, c);
@@ -101,40 +109,47 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
   }
 }
 
-template <DType T, int G, int KPT, int PPW>
+template <DType T, int G, int KPT, int PPW, int SUB>
 void launch_t(const quest_paged_kv& kv, const void* q, const void* k_pool,
               const void* v_pool, const int32_t* page_table,
               const int32_t* seq_lens, const float* scores, int k, int n_sink,
               int n_local, float qscale, int32_t* sel, float* out, float* ws_o,
               float* ws_ml, int nsplit, hipStream_t stream) {
   dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
-  topk_attn_kernel<T, G, KPT, PPW><<<grid, 256, 0, stream>>>(
+  topk_attn_kernel<T, G, KPT, PPW, SUB><<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), page_table, seq_lens, scores, k,
       n_sink, n_local, kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages, qscale, sel, out,
       ws_o, ws_ml);
 }
 
-template <DType T, int KPT>
+template <DType T, int KPT, int SUB>
 void dispatch_g(int G, int ppw, const quest_paged_kv& kv, const void* q,
                 const void* k_pool, const void* v_pool, const int32_t* page_table,
                 const int32_t* seq_lens, const float* scores, int k, int n_sink,
                 int n_local, float qscale, int32_t* sel, float* out, float* ws_o,
                 float* ws_ml, int nsplit, hipStream_t s) {
 #define QUEST_TA(GG, PP)                                                         \
-  launch_t<T, GG, KPT, PP>(kv, q, k_pool, v_pool, page_table, seq_lens, scores, \
+  launch_t<T, GG, KPT, PP, SUB>(kv, q, k_pool, v_pool, page_table, seq_lens, scores, \
                            k, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,    \
                            nsplit, s)
+  // ppw never exceeds the plan's limit for SUB: only those variants are built
   if (G == 1) {
-    if (ppw == 4) QUEST_TA(1, 4);
-    else if (ppw == 2) QUEST_TA(1, 2);
+    if constexpr (SUB == 1) {
+      if (ppw == 4) { QUEST_TA(1, 4); return; }
+    }
+    if (ppw == 2) QUEST_TA(1, 2);
     else QUEST_TA(1, 1);
   } else if (G == 2) {
-    if (ppw == 2) QUEST_TA(2, 2);
-    else QUEST_TA(2, 1);
+    if constexpr (SUB == 1) {
+      if (ppw == 2) { QUEST_TA(2, 2); return; }
+    }
+    QUEST_TA(2, 1);
   } else if (G == 4) {
-    if (ppw == 2) QUEST_TA(4, 2);
-    else QUEST_TA(4, 1);
+    if constexpr (SUB == 1) {
+      if (ppw == 2) { QUEST_TA(4, 2); return; }
+    }
+    QUEST_TA(4, 1);
   } else {
     QUEST_TA(8, 1);
   }
@@ -157,25 +172,19 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
   float* ws_ml = ws_o ? ws_o + attention_ml_offset(slots) : nullptr;
   const float qscale = sm_scale * kLog2e;
   const int mp = kv.max_pages_per_seq;
+#define QUEST_TA_D(TT, KK, SS)                                                       \
+  dispatch_g<TT, KK, SS>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,    \
+                         scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o,  \
+                         ws_ml, pl.nsplit, stream)
+  const bool s32 = kv.page_size == 32;
   if (kv.dtype == QUEST_F16) {
-    if (mp <= 2048)
-      dispatch_g<DType::F16, 8>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                                scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,
-                                pl.nsplit, stream);
-    else
-      dispatch_g<DType::F16, 32>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                                 scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,
-                                pl.nsplit, stream);
+    if (mp <= 2048) { if (s32) QUEST_TA_D(DType::F16, 8, 2); else QUEST_TA_D(DType::F16, 8, 1); }
+    else { if (s32) QUEST_TA_D(DType::F16, 32, 2); else QUEST_TA_D(DType::F16, 32, 1); }
   } else {
-    if (mp <= 2048)
-      dispatch_g<DType::BF16, 8>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                                 scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,
-                                pl.nsplit, stream);
-    else
-      dispatch_g<DType::BF16, 32>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,
-                                  scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,
-                                pl.nsplit, stream);
+    if (mp <= 2048) { if (s32) QUEST_TA_D(DType::BF16, 8, 2); else QUEST_TA_D(DType::BF16, 8, 1); }
+    else { if (s32) QUEST_TA_D(DType::BF16, 32, 2); else QUEST_TA_D(DType::BF16, 32, 1); }
   }
+#undef QUEST_TA_D
   if (pl.nsplit > 1) launch_merge(kv, ws_o, ws_ml, pl.nsplit, out, stream);
   return hipGetLastError();
 }

@@ -28,16 +28,17 @@ def to64(t: torch.Tensor) -> np.ndarray:
 
 
 def workload(B=1, Hq=1, Hkv=1, lens=(1024,), budget=128, dtype="f16", seed=0,
-             permute=False, outliers=0, planted=0, name="case"):
+             permute=False, outliers=0, planted=0, name="case", page_size=16):
     return synth.Workload(name, B, Hq, Hkv, tuple(lens), budget, dtype,
-                          outliers=outliers, planted=planted,
-                          permute_pool=permute, base_seed=seed)
+                          page_size=page_size, outliers=outliers,
+                          planted=planted, permute_pool=permute, base_seed=seed)
 
 
 def draw(wl, layer=0, heads=None):
     c = synth.draw_layer(wl, layer, "cuda", heads=heads)
     c["kv"] = qa.paged_kv(wl.batch, wl.num_q_heads, wl.num_kv_heads,
-                          wl.pool_pages(), wl.max_pages, wl.torch_dtype)
+                          wl.pool_pages(), wl.max_pages, wl.torch_dtype,
+                          page_size=wl.page_size)
     return c
 
 

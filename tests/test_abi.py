@@ -54,7 +54,8 @@ def test_status_strings():
 
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 64, _abi.QUEST_ERR_UNSUPPORTED),
-    ("page_size", 32, _abi.QUEST_ERR_UNSUPPORTED),
+    ("page_size", 64, _abi.QUEST_ERR_UNSUPPORTED),
+    ("page_size", 8, _abi.QUEST_ERR_UNSUPPORTED),
     ("dtype", 7, _abi.QUEST_ERR_UNSUPPORTED),
     ("num_kv_heads", 5, _abi.QUEST_ERR_INVALID_ARGUMENT),   # 32 % 5 != 0
     ("num_q_heads", 96, _abi.QUEST_ERR_UNSUPPORTED),        # G = 3
