@@ -25,6 +25,9 @@ Workloads (each prints ONE JSON line):
   time, bytes and pages kept per kv-head for each rule.
 * ``page32``: 16- against 32-token pages at 32K and 128K (same token
   budget), and the one-shot prefill metadata build against writing K.
+* ``host_kv``: the longchat layer with K/V in pinned host memory (metadata
+  in HBM): only the kept pages cross the host link; its roofline is the
+  link's measured read ceiling.
 
 Inputs are seeded synthetic tensors drawn on the GPU and resident in HBM
 before timing starts.  The line carries the step time (the metric),
@@ -704,6 +707,91 @@ def bench_page32(args, torch, qa, synth):
         "points": rows, "gpu": torch.cuda.get_device_name(0)}
 
 
+def bench_host_kv(args, torch, qa, synth):
+    """The LongChat layer with its K/V pools in pinned host memory: metadata,
+    scores and selection stay in HBM, and attention reads only the kept
+    pages over the host link ("Guide to Quest": the cache stays in host or
+    device memory and only the critical pages are loaded)."""
+    rot = 2
+    wls = [synth.longchat_layer_workload(seed=1 + 1000 * i) for i in range(rot)]
+    insts = [make_layer(qa, synth, wl) for wl in wls]
+    for c in insts:                      # move the pools to the host
+        c["k_pool"], c["v_pool"] = qa.host_pool_like(c["k_pool"]), \
+            qa.host_pool_like(c["v_pool"])
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    kv = insts[0]["kv"]
+    k = wls[0].k_pages
+    sm = 1.0 / math.sqrt(128)
+    steps = [qa.SparseDecodeStep(kv, k, sm) for _ in range(rot)]
+    denses = [qa.DenseDecode(kv, sm) for _ in range(rot)]
+
+    def step_call(i):
+        c = insts[i]
+        steps[i](c["q"], c["k_pool"], c["v_pool"], c["kmin"], c["kmax"],
+                 c["page_table"], c["seq_lens"])
+
+    def dense_call(i):
+        c = insts[i]
+        denses[i](c["q"], c["k_pool"], c["v_pool"], c["page_table"], c["seq_lens"])
+
+    for i in range(rot):
+        step_call(i)
+        dense_call(i)
+    torch.cuda.synchronize()
+    g_step = capture(torch, lambda: [step_call(i) for i in range(rot)])
+    g_dense = capture(torch, lambda: [dense_call(i) for i in range(rot)])
+    tm = Timer(torch)
+    us = tm.run(lambda i: g_step.replay(), max(2, args.steps // (4 * rot)), 2, 1,
+                events=False)["mean"] / rot
+    us_dense = tm.run(lambda i: g_dense.replay(), 3, 1, 1, events=False)["mean"] / rot
+    lens = [int(x) for x in insts[0]["seq_lens"].cpu()]
+    b = step_bytes(lens, kv.num_kv_heads, kv.num_q_heads, k,
+                   sel=steps[0].sel.cpu().numpy())
+    link_bytes = b["kv"]                 # what crosses the host link
+    dense_link = sum(L * kv.num_kv_heads * 2 * 128 * 2 for L in lens)
+    # the link's read ceiling: the streaming probe over pinned host memory
+    buf = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    buf.fill_(1)
+    hbuf = qa.HostPool(buf)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qa.quest_stream_read_probe(hbuf, sink)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        qa.quest_stream_read_probe(hbuf, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    link_ceiling = (1 << 30) * 3 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    link_gbps = link_bytes / (us * 1e-6) / 1e9
+    return {
+        "metric": "µs/decode step with K/V in pinned host memory, 32 heads, "
+                  "32K ctx, 2048-token budget",
+        "value": round(us, 3), "unit": "us/step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (as longchat); K/V pools in pinned host memory, "
+                "metadata in HBM",
+        "config": {"workload": "longchat7b_layer_decode_host_kv", "batch": 1,
+                   "q_heads": 32, "kv_heads": 32, "ctx": 32768,
+                   "budget_tokens": 2048, "rotating_caches": rot},
+        "link_bytes_per_step": int(link_bytes),
+        "link_GBps": round(link_gbps, 2),
+        "link_read_ceiling_GBps": round(link_ceiling, 2),
+        "roofline": {"bound": "host link", "achieved": round(link_gbps, 2),
+                     "peak": round(link_ceiling, 2), "unit": "GB/s",
+                     "frac": round(link_gbps / link_ceiling, 4), "traffic": None,
+                     "kernel": "whole step (kept K/V read from host memory)"},
+        "dense_us_per_step": round(us_dense, 3),
+        "dense_link_bytes_per_step": int(dense_link),
+        "speedup_vs_dense": round(us_dense / us, 3),
+        "gpu": torch.cuda.get_device_name(0)}
+
+
 # ------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(gpu, budget_s):
@@ -796,7 +884,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="longchat",
                     choices=["longchat", "gqa_multistep", "ragged", "sweep",
-                             "gqa_union", "page32"])
+                             "gqa_union", "page32", "host_kv"])
     ap.add_argument("--rotate", type=int, default=8,
                     help="independent caches the steps cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -837,7 +925,8 @@ def main():
 
     fn = {"longchat": bench_longchat, "gqa_multistep": bench_gqa_multistep,
           "ragged": bench_ragged, "sweep": bench_sweep,
-          "gqa_union": bench_gqa_union, "page32": bench_page32}[args.workload]
+          "gqa_union": bench_gqa_union, "page32": bench_page32,
+          "host_kv": bench_host_kv}[args.workload]
     print(json.dumps(fn(args, torch, qa, synth)), flush=True)
 
 

@@ -16,7 +16,9 @@
  * Conventions shared by every call
  * --------------------------------
  * - All array arguments are DEVICE pointers to row-major, contiguous memory,
- *   16-byte aligned (the kernels read and write 16 bytes per lane).  The
+ *   16-byte aligned (the kernels read and write 16 bytes per lane).  The K/V
+ *   pools may instead be pinned host memory seen through its device address
+ *   (quest_host_device_pointer).  The
  *   caller allocates and owns every buffer; the library allocates nothing,
  *   keeps no state between calls, and may be called from several host
  *   threads on different streams.
@@ -284,6 +286,21 @@ QUEST_API quest_status quest_step_workspace_size(const quest_paged_kv* kv,
  * pages per row (pass max_pages_per_seq for quest_decode_attn). */
 QUEST_API quest_status quest_workspace_size(const quest_paged_kv* kv,
                                             int32_t k_pages, size_t* bytes);
+
+/*
+ * Host-resident KV pools.  [G] (the introduction) keeps the full KV cache in
+ * host or device memory and loads only the critical pages for the current
+ * query.  k_pool and v_pool of quest_update_page_meta,
+ * quest_sparse_decode_attn(_ex), quest_topk_sparse_decode_attn(_ex) and
+ * quest_decode_attn may point to pinned host memory (allocated pinned, e.g.
+ * with hipHostMalloc) through the device address this call returns: the
+ * kernels then read, over the host link, only the 16-token tiles of the
+ * pages they use, while kmin/kmax, scores and everything else stay in HBM.
+ * Results are bit-identical to device-resident pools.  Host only; returns
+ * QUEST_ERR_HIP if `host_ptr` is not pinned host memory.
+ */
+QUEST_API quest_status quest_host_device_pointer(const void* host_ptr,
+                                                 void** device_ptr);
 
 /*
  * Diagnostic, not part of the method: reads `bytes` (a positive multiple of

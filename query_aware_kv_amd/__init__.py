@@ -13,7 +13,7 @@ import math
 import torch
 
 from ._abi import (  # noqa: F401
-    LIB, LIB_PATH, PagedKV, QuestError, QUEST_BF16, QUEST_F16, QUEST_OK,
+    LIB, LIB_PATH, HostPool, PagedKV, QuestError, QUEST_BF16, QUEST_F16, QUEST_OK,
     QUEST_ERR_HIP, QUEST_ERR_INVALID_ARGUMENT, QUEST_ERR_UNSUPPORTED,
     QUEST_ERR_WORKSPACE_TOO_SMALL, paged_kv, paged_kv_like,
     quest_decode_attn, quest_estimate, quest_sparse_decode_attn,
@@ -37,6 +37,14 @@ def alloc_workspace(kv: PagedKV, k_pages: int, device="cuda") -> torch.Tensor:
     """Zero-filled attention workspace (the calls keep its counters zero)."""
     n = quest_workspace_size(kv, k_pages)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def host_pool_like(pool: torch.Tensor) -> HostPool:
+    """A pinned host copy of a K or V pool, for the kernels to read in place
+    (only the pages a call uses cross the host link)."""
+    t = torch.empty(pool.shape, dtype=pool.dtype, pin_memory=True)
+    t.copy_(pool)
+    return HostPool(t)
 
 
 def alloc_meta(kv: PagedKV, device="cuda"):

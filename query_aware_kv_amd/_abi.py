@@ -82,6 +82,7 @@ def _load():
         "quest_topk_sparse_decode_attn": [KV, P, P, P, P, P, P, I, ctypes.c_float,
                                           P, P, P, ctypes.c_size_t, P],
         "quest_stream_read_probe": [P, ctypes.c_size_t, P, P],
+        "quest_host_device_pointer": [P, ctypes.POINTER(ctypes.c_void_p)],
         "quest_topk_pages_ex": [KV, P, P, I, I, I, P, P],
         "quest_estimate_heads": [KV, P, P, P, P, P, P, P],
         "quest_union_pages": [KV, P, I, P, P],
@@ -108,9 +109,34 @@ def _check(status: int) -> None:
         raise QuestError(status, LIB.quest_last_error().decode())
 
 
-def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+class HostPool:
+    """A K or V pool in pinned host memory, read by the kernels in place
+    through its device address (only the pages a call uses cross the host
+    link).  `tensor` must be a pinned CPU tensor, e.g. allocated with
+    ``torch.empty(..., pin_memory=True)``."""
+
+    def __init__(self, tensor: torch.Tensor):
+        if tensor.device.type != "cpu" or not tensor.is_pinned():
+            raise ValueError("HostPool needs a pinned CPU tensor")
+        if not tensor.is_contiguous():
+            raise ValueError("HostPool tensor must be contiguous")
+        self.tensor = tensor
+        dev = ctypes.c_void_p()
+        _check(LIB.quest_host_device_pointer(ctypes.c_void_p(tensor.data_ptr()),
+                                             ctypes.byref(dev)))
+        self.device_ptr = int(dev.value)
+        self.dtype, self.shape = tensor.dtype, tuple(tensor.shape)
+
+
+def _ptr(t, name: str, dtype=None, shape=None, host_ok: bool = False):
     if t is None:
         return None
+    if host_ok and isinstance(t, HostPool):
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if shape is not None and t.shape != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {t.shape}")
+        return ctypes.c_void_p(t.device_ptr)
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -168,8 +194,8 @@ def quest_update_page_meta(kv: PagedKV, k_pool, v_pool, kmin, kmax,
     i32 = torch.int32
     _check(LIB.quest_update_page_meta(
         ctypes.byref(kv),
-        _ptr(k_pool, "k_pool", dt, _pool_shape(kv)),
-        _ptr(v_pool, "v_pool", dt, _pool_shape(kv)),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv), host_ok=True),
         _ptr(kmin, "kmin", dt, _meta_shape(kv)),
         _ptr(kmax, "kmax", dt, _meta_shape(kv)),
         _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
@@ -233,8 +259,8 @@ def quest_sparse_decode_attn(kv: PagedKV, q, k_pool, v_pool, page_table,
     _check(LIB.quest_sparse_decode_attn(
         ctypes.byref(kv),
         _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
-        _ptr(k_pool, "k_pool", dt, _pool_shape(kv)),
-        _ptr(v_pool, "v_pool", dt, _pool_shape(kv)),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv), host_ok=True),
         _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
         _ptr(seq_lens, "seq_lens", i32, (kv.batch,)),
         _ptr(sel_pages, "sel_pages", i32, (kv.batch, kv.num_kv_heads, k_pages)),
@@ -252,8 +278,8 @@ def quest_decode_attn(kv: PagedKV, q, k_pool, v_pool, page_table, seq_lens,
     _check(LIB.quest_decode_attn(
         ctypes.byref(kv),
         _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
-        _ptr(k_pool, "k_pool", dt, _pool_shape(kv)),
-        _ptr(v_pool, "v_pool", dt, _pool_shape(kv)),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv), host_ok=True),
         _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
         _ptr(seq_lens, "seq_lens", i32, (kv.batch,)),
         float(sm_scale),
@@ -279,8 +305,8 @@ def quest_sparse_decode_step(kv: PagedKV, q, k_pool, v_pool, kmin, kmax,
     _check(LIB.quest_sparse_decode_step(
         ctypes.byref(kv),
         _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
-        _ptr(k_pool, "k_pool", dt, _pool_shape(kv)),
-        _ptr(v_pool, "v_pool", dt, _pool_shape(kv)),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv), host_ok=True),
         _ptr(kmin, "kmin", dt, _meta_shape(kv)),
         _ptr(kmax, "kmax", dt, _meta_shape(kv)),
         _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
@@ -311,8 +337,8 @@ def quest_topk_sparse_decode_attn(kv: PagedKV, q, k_pool, v_pool, page_table,
     _check(LIB.quest_topk_sparse_decode_attn(
         ctypes.byref(kv),
         _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
-        _ptr(k_pool, "k_pool", dt, _pool_shape(kv)),
-        _ptr(v_pool, "v_pool", dt, _pool_shape(kv)),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv), host_ok=True),
         _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
         _ptr(seq_lens, "seq_lens", i32, (kv.batch,)),
         _ptr(scores, "scores", torch.float32,
@@ -327,8 +353,10 @@ def quest_topk_sparse_decode_attn(kv: PagedKV, q, k_pool, v_pool, page_table,
 def quest_stream_read_probe(buf, sink, stream=None) -> None:
     """Diagnostic: one streaming read of the whole of `buf` (any dtype,
     16-byte multiple); `sink` is a one-element int32/uint32 device tensor."""
-    nbytes = buf.numel() * buf.element_size()
-    _check(LIB.quest_stream_read_probe(_ptr(buf, "buf"), ctypes.c_size_t(nbytes),
+    t = buf.tensor if isinstance(buf, HostPool) else buf
+    nbytes = t.numel() * t.element_size()
+    _check(LIB.quest_stream_read_probe(_ptr(buf, "buf", host_ok=True),
+                                       ctypes.c_size_t(nbytes),
                                        _ptr(sink, "sink"), _stream(stream)))
 
 
@@ -343,8 +371,8 @@ def quest_topk_sparse_decode_attn_ex(kv: PagedKV, q, k_pool, v_pool,
     _check(LIB.quest_topk_sparse_decode_attn_ex(
         ctypes.byref(kv),
         _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
-        _ptr(k_pool, "k_pool", dt, _pool_shape(kv)),
-        _ptr(v_pool, "v_pool", dt, _pool_shape(kv)),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv), host_ok=True),
         _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
         _ptr(seq_lens, "seq_lens", i32, (kv.batch,)),
         _ptr(scores, "scores", torch.float32,

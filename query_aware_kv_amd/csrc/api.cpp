@@ -429,6 +429,22 @@ QUEST_API quest_status quest_workspace_size(const quest_paged_kv* kv,
   return ok();
 }
 
+QUEST_API quest_status quest_host_device_pointer(const void* host_ptr,
+                                                 void** device_ptr) {
+  const char* fn = "quest_host_device_pointer";
+  REQUIRE_PTR(host_ptr, true);
+  REQUIRE_PTR(device_ptr, true);
+  void* dev = nullptr;
+  const hipError_t e = hipHostGetDevicePointer(&dev, const_cast<void*>(host_ptr), 0);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear it: the caller's next HIP call must not see it
+    return fail(QUEST_ERR_HIP, "%s: %s (is the buffer pinned host memory?)", fn,
+                hipGetErrorString(e));
+  }
+  *device_ptr = dev;
+  return ok();
+}
+
 QUEST_API quest_status quest_stream_read_probe(const void* buf, size_t bytes,
                                                uint32_t* sink, void* stream) {
   const char* fn = "quest_stream_read_probe";

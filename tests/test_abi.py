@@ -227,3 +227,18 @@ def test_union_and_heads_validation():
     assert qa.LIB.quest_estimate_heads(ctypes.byref(k), *([P(FAKE)] * 5), None,
                                        None) == _abi.QUEST_ERR_INVALID_ARGUMENT
     assert "scores" in qa.LIB.quest_last_error().decode()
+
+
+def test_host_device_pointer_rejects_null():
+    P = ctypes.c_void_p
+    out = ctypes.c_void_p()
+    assert qa.LIB.quest_host_device_pointer(None, ctypes.byref(out)) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert qa.LIB.quest_host_device_pointer(P(FAKE), None) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+
+
+def test_host_pool_needs_pinned_cpu_tensor():
+    import torch
+    with pytest.raises(ValueError, match="pinned"):
+        qa.HostPool(torch.zeros(4, 128, dtype=torch.float16))

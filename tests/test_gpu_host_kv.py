@@ -1,0 +1,90 @@
+"""K/V pools in pinned host memory ("Guide to Quest": the full cache stays
+in host or device memory and only the critical pages are loaded): every
+call that reads or writes the pools gives bit-identical results when the
+pools live in host memory and the kernels read them over the host link."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import query_aware_kv_amd as qa
+
+import gpu_cases as C
+from test_gpu_parity import make as make16
+from test_gpu_page32 import make as make32
+
+pytestmark = pytest.mark.gpu
+
+SM = 1.0 / math.sqrt(128)
+
+
+def host_pools(c):
+    return qa.host_pool_like(c["k_pool"]), qa.host_pool_like(c["v_pool"])
+
+
+@pytest.mark.parametrize("maker,name", [(make16, "mha_ragged_f16"),
+                                        (make16, "gqa4_f16"),
+                                        (make16, "with_empty_request"),
+                                        (make32, "p32_gqa8_bf16")])
+def test_host_pools_match_device_pools(maker, name):
+    wl, c = maker(name)
+    kv = c["kv"]
+    hk, hv = host_pools(c)
+    dmin, dmax = C.gpu_meta(c)
+    hmin, hmax = qa.alloc_meta(kv)
+    qa.quest_update_page_meta(kv, hk, hv, hmin, hmax, c["page_table"], c["seq_lens"])
+    torch.cuda.synchronize()
+    o_pages = C.used_pages(c["page_table"].cpu().numpy(), c["seq_lens"].cpu().numpy(),
+                           kv.page_size)
+    idx = torch.tensor(o_pages, dtype=torch.long, device="cuda")
+    assert torch.equal(hmin[idx].view(torch.int16), dmin[idx].view(torch.int16))
+    assert torch.equal(hmax[idx].view(torch.int16), dmax[idx].view(torch.int16))
+    for fused in (True, False):
+        a = qa.SparseDecodeStep(kv, wl.k_pages, SM, fused_topk=fused)
+        b = qa.SparseDecodeStep(kv, wl.k_pages, SM, fused_topk=fused)
+        a(c["q"], c["k_pool"], c["v_pool"], dmin, dmax, c["page_table"], c["seq_lens"])
+        b(c["q"], hk, hv, dmin, dmax, c["page_table"], c["seq_lens"])
+        torch.cuda.synchronize()
+        assert torch.equal(a.sel, b.sel)
+        assert torch.equal(a.out.view(torch.int32), b.out.view(torch.int32))
+    d1 = qa.DenseDecode(kv, SM)(c["q"], c["k_pool"], c["v_pool"], c["page_table"],
+                                c["seq_lens"]).clone()
+    d2 = qa.DenseDecode(kv, SM)(c["q"], hk, hv, c["page_table"], c["seq_lens"])
+    torch.cuda.synchronize()
+    assert torch.equal(d1.view(torch.int32), d2.view(torch.int32))
+
+
+def test_append_into_host_pool():
+    wl, c = make16("gqa4_f16")
+    kv = c["kv"]
+    hk, hv = host_pools(c)
+    kmin, kmax = C.gpu_meta(c)
+    # one more token for requests whose last page has room (others pass
+    # L = 0, which the append skips)
+    old = c["seq_lens"]
+    lens = torch.where(old % 16 != 0, old + 1, torch.zeros_like(old)).to(torch.int32)
+    assert int((lens > 0).sum()) > 0
+    g = torch.Generator(device="cuda").manual_seed(9)
+    k_new = torch.randn(kv.batch, kv.num_kv_heads, 128, generator=g,
+                        device="cuda").to(c["k_pool"].dtype)
+    v_new = torch.randn(kv.batch, kv.num_kv_heads, 128, generator=g,
+                        device="cuda").to(c["k_pool"].dtype)
+    dk, dv = c["k_pool"].clone(), c["v_pool"].clone()
+    dmin, dmax = kmin.clone(), kmax.clone()
+    qa.quest_update_page_meta(kv, dk, dv, dmin, dmax, c["page_table"], lens,
+                              k_new=k_new, v_new=v_new)
+    qa.quest_update_page_meta(kv, hk, hv, kmin, kmax, c["page_table"], lens,
+                              k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    assert torch.equal(kmin.view(torch.int16), dmin.view(torch.int16))
+    assert torch.equal(kmax.view(torch.int16), dmax.view(torch.int16))
+    pt = c["page_table"].cpu().long()
+    for b, L in enumerate(lens.cpu().tolist()):
+        if L == 0:
+            continue
+        p, slot = pt[b, (L - 1) // 16], (L - 1) % 16
+        assert torch.equal(hk.tensor[p, :, slot].view(torch.int16),
+                           dk[p, :, slot].cpu().view(torch.int16))
+        assert torch.equal(hv.tensor[p, :, slot].view(torch.int16),
+                           dv[p, :, slot].cpu().view(torch.int16))
