@@ -13,8 +13,10 @@ Workloads (each prints ONE JSON line):
   pages) together exceed the 256 MB Infinity Cache, so every step reads its
   bytes from HBM.
 * ``gqa_multistep``: 32 layers of 32 q-heads / 8 kv-heads; every step
-  appends one token per layer (quest_update_page_meta, append mode), runs
-  dense attention on layers 0-1 and the sparse step on layers 2-31.  A step
+  appends one token per layer, runs dense attention on layers 0-1
+  (quest_update_page_meta in append mode, then quest_decode_attn) and the
+  sparse step on layers 2-31 (quest_append_estimate, then
+  quest_topk_sparse_decode_attn).  A step
   is all 32 layers; the timed steps walk the 128 appends in order.
 * ``ragged``: 32 requests x 32 heads, contexts uniform in [8K, 32K], bf16,
   pages scattered through a shared pool.
@@ -515,15 +517,16 @@ def bench_gqa_multistep(args, torch, qa, synth):
     def one_step(s):
         for layer, st in enumerate(layers):
             c, kv = st["c"], st["kv"]
-            qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], c["kmin"],
-                                      c["kmax"], c["page_table"], lens[s],
-                                      k_new=st["k_new"][s], v_new=st["v_new"][s])
             if layer < wl.dense_layers:
+                qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], c["kmin"],
+                                          c["kmax"], c["page_table"], lens[s],
+                                          k_new=st["k_new"][s], v_new=st["v_new"][s])
                 st["dense"](st["q"][s], c["k_pool"], c["v_pool"],
                             c["page_table"], lens[s])
-            else:
-                st["step"](st["q"][s], c["k_pool"], c["v_pool"], c["kmin"],
-                           c["kmax"], c["page_table"], lens[s])
+            else:   # the append rides on the estimate launch
+                st["step"].append_step(st["q"][s], c["k_pool"], c["v_pool"],
+                                       c["kmin"], c["kmax"], c["page_table"],
+                                       lens[s], st["k_new"][s], st["v_new"][s])
 
     # Warm-up steps re-append the same tokens at the same positions; they
     # leave every page box a superset of the timed run's, which changes no
@@ -573,7 +576,7 @@ def bench_gqa_multistep(args, torch, qa, synth):
         "eager_us_per_step": round(us_eager, 3),
         "graph_us_per_step": round(tg["mean"], 3),
         "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
-        "launches_per_step": wl.dense_layers * 3 + (wl.layers - wl.dense_layers) * 4,
+        "launches_per_step": wl.dense_layers * 3 + (wl.layers - wl.dense_layers) * 3,
         "gpu": torch.cuda.get_device_name(0),
     }
 

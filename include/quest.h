@@ -128,6 +128,21 @@ QUEST_API quest_status quest_estimate(
     float* scores, void* stream);
 
 /*
+ * quest_update_page_meta in append mode followed by quest_estimate, in one
+ * launch, with the same results bit for bit: each request appends token
+ * L_b - 1 (k_new / v_new [batch][Hkv][d], written into k_pool / v_pool at
+ * slot (L_b - 1) % S of logical page (L_b - 1) / S, folded into that page's
+ * box in kmin / kmax -- [G] §1, the box forms as its page forms), and the
+ * scores are those of the updated boxes.  Requests with L_b = 0 append
+ * nothing.  The decode step of one layer becomes this call plus
+ * quest_topk_sparse_decode_attn.
+ */
+QUEST_API quest_status quest_append_estimate(
+    const quest_paged_kv* kv, void* k_pool, void* v_pool, void* kmin, void* kmax,
+    const int32_t* page_table, const int32_t* seq_lens, const void* k_new,
+    const void* v_new, const void* q, float* scores, void* stream);
+
+/*
  * Per-query-head estimate.  [G] §2 upper-bound inequality for each query
  * head h against the boxes of its kv-head g = h / G, as [G] Best Practices 2
  * asks for before the union of the heads' selections:

@@ -18,7 +18,7 @@ from ._abi import (  # noqa: F401
     QUEST_ERR_WORKSPACE_TOO_SMALL, paged_kv, paged_kv_like,
     quest_decode_attn, quest_estimate, quest_sparse_decode_attn,
     quest_sparse_decode_step, quest_step_workspace_size,
-    quest_estimate_heads, quest_union_pages,
+    quest_append_estimate, quest_estimate_heads, quest_union_pages,
     quest_stream_read_probe, quest_topk_pages, quest_topk_pages_ex,
     quest_topk_sparse_decode_attn, quest_topk_sparse_decode_attn_ex,
     quest_update_page_meta,
@@ -88,6 +88,27 @@ class SparseDecodeStep:
                  stream=None) -> torch.Tensor:
         quest_estimate(self.kv, q, kmin, kmax, page_table, seq_lens,
                        self.scores, stream)
+        if self.fused_topk:
+            quest_topk_sparse_decode_attn_ex(
+                self.kv, q, k_pool, v_pool, page_table, seq_lens, self.scores,
+                self.k_pages, self.n_sink, self.n_local, self.sm_scale,
+                self.sel, self.out, self.workspace, stream)
+            return self.out
+        quest_topk_pages_ex(self.kv, self.scores, seq_lens, self.k_pages,
+                            self.n_sink, self.n_local, self.sel, stream)
+        quest_sparse_decode_attn(self.kv, q, k_pool, v_pool, page_table,
+                                 seq_lens, self.sel, self.k_pages,
+                                 self.sm_scale, self.out, self.workspace,
+                                 stream)
+        return self.out
+
+    def append_step(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_lens,
+                    k_new, v_new, stream=None) -> torch.Tensor:
+        """One generated token per request: append k_new / v_new at position
+        seq_lens - 1 (which already counts it) together with the estimate
+        (quest_append_estimate), then select and attend."""
+        quest_append_estimate(self.kv, k_pool, v_pool, kmin, kmax, page_table,
+                              seq_lens, k_new, v_new, q, self.scores, stream)
         if self.fused_topk:
             quest_topk_sparse_decode_attn_ex(
                 self.kv, q, k_pool, v_pool, page_table, seq_lens, self.scores,

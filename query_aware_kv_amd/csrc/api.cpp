@@ -217,6 +217,31 @@ QUEST_API quest_status quest_estimate(const quest_paged_kv* kv, const void* q,
                       stream, "quest_estimate");
 }
 
+QUEST_API quest_status quest_append_estimate(
+    const quest_paged_kv* kv, void* k_pool, void* v_pool, void* kmin, void* kmax,
+    const int32_t* page_table, const int32_t* seq_lens, const void* k_new,
+    const void* v_new, const void* q, float* scores, void* stream) {
+  const char* fn = "quest_append_estimate";
+  quest_status s = check_kv(kv, fn);
+  if (s != QUEST_OK) return s;
+  if ((s = check_group(kv, fn)) != QUEST_OK) return s;
+  REQUIRE_PTR(k_pool, aligned16(k_pool));
+  REQUIRE_PTR(v_pool, aligned16(v_pool));
+  REQUIRE_PTR(k_new, aligned16(k_new));
+  REQUIRE_PTR(v_new, aligned16(v_new));
+  REQUIRE_PTR(q, aligned16(q));
+  REQUIRE_PTR(kmin, aligned16(kmin));
+  REQUIRE_PTR(kmax, aligned16(kmax));
+  REQUIRE_PTR(page_table, aligned4(page_table));
+  REQUIRE_PTR(seq_lens, aligned4(seq_lens));
+  REQUIRE_PTR(scores, aligned4(scores));
+  return hip_status(quest::launch_estimate(*kv, q, kmin, kmax, page_table, seq_lens,
+                                           scores, false,
+                                           static_cast<hipStream_t>(stream), k_pool,
+                                           v_pool, k_new, v_new),
+                    fn);
+}
+
 QUEST_API quest_status quest_estimate_heads(const quest_paged_kv* kv,
                                             const void* q, const void* kmin,
                                             const void* kmax,

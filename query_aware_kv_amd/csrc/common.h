@@ -52,6 +52,30 @@ __device__ __forceinline__ uint32_t unord16(int32_t k) {
   return (uint32_t)(uint16_t)(int16_t)s;
 }
 
+// Fold eight 16-bit values (one 16-byte piece) into running ord16 minima and
+// maxima, and pack such keys back into eight 16-bit values.
+__device__ __forceinline__ void fold8(const uint4& x, int32_t (&mn)[8],
+                                      int32_t (&mx)[8]) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t lo = ord16(w[i] & 0xffffu), hi = ord16(w[i] >> 16);
+    mn[2 * i] = min(mn[2 * i], lo);
+    mx[2 * i] = max(mx[2 * i], lo);
+    mn[2 * i + 1] = min(mn[2 * i + 1], hi);
+    mx[2 * i + 1] = max(mx[2 * i + 1], hi);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const int32_t (&k)[8]) {
+  uint4 r;
+  r.x = unord16(k[0]) | (unord16(k[1]) << 16);
+  r.y = unord16(k[2]) | (unord16(k[3]) << 16);
+  r.z = unord16(k[4]) | (unord16(k[5]) << 16);
+  r.w = unord16(k[6]) | (unord16(k[7]) << 16);
+  return r;
+}
+
 // ------------------------------------------------------------ cross-lane
 
 template <int CTRL>

@@ -87,6 +87,43 @@ __device__ __forceinline__ void est_score(const float (&qf)[G][8],
   }
 }
 
+// Append one token to page u of the block in registers and in memory, as
+// quest_update_page_meta's append mode does ("Guide to Quest" §1: the box
+// forms with its page; a token in slot 0 starts a new box): the row's 16
+// lanes write the token's K and V row (8 channels each) and the updated box.
+// `u` is uniform over the row; the loop keeps register indices constant.
+__device__ __forceinline__ void est_append(int u, int slot, int64_t p, int Hkv, int g,
+                                           int c, int S, const uint4& kn,
+                                           const uint4& vn, uint16_t* __restrict__ k_pool,
+                                           uint16_t* __restrict__ v_pool,
+                                           uint16_t* __restrict__ kmin,
+                                           uint16_t* __restrict__ kmax,
+                                           uint4 (&lo)[kEstPages], uint4 (&hi)[kEstPages]) {
+  const int64_t row = ((p * Hkv + g) * S + slot) * kHeadDim + c * 8;
+  *reinterpret_cast<uint4*>(k_pool + row) = kn;
+  *reinterpret_cast<uint4*>(v_pool + row) = vn;
+#pragma unroll
+  for (int w = 0; w < kEstPages; ++w) {
+    if (w != u) continue;
+    if (slot == 0) {
+      lo[w] = kn;
+      hi[w] = kn;
+    } else {
+      int32_t mn[8], mx[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { mn[e] = 0x7fffffff; mx[e] = -0x7fffffff - 1; }
+      fold8(kn, mn, mx);
+      fold8(lo[w], mn, mx);
+      fold8(hi[w], mn, mx);
+      lo[w] = pack8(mn);
+      hi[w] = pack8(mx);
+    }
+    const int64_t m = (p * Hkv + g) * kHeadDim + c * 8;
+    *reinterpret_cast<uint4*>(kmin + m) = lo[w];
+    *reinterpret_cast<uint4*>(kmax + m) = hi[w];
+  }
+}
+
 // Per-query-head bounds of the 4 pages: s[h][u] for the G heads of the
 // group, from one read of each box ("Guide to Quest", Best Practices 2).
 template <DType T, int G>

@@ -15,17 +15,29 @@ namespace {
 
 constexpr int kRowsPerBlock = 16;  // 256 threads
 
+// Extra arguments of the append mode (null otherwise).
+struct EstAppend {
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const uint16_t* k_new;  // [B][Hkv][128]
+  const uint16_t* v_new;
+};
+
 // PER_HEAD: scores hold one row per query head ([B][Hq][max_pages], head
 // g * G + h) instead of one per kv-head with the group's sum.
-template <DType T, int G, bool PER_HEAD>
+// APPEND: first append token L_b - 1 (k_new / v_new) to its page and box,
+// as quest_update_page_meta's append mode; the row that owns that page
+// does it and scores the page with the updated box.
+template <DType T, int G, bool PER_HEAD, bool APPEND>
 __global__ void __launch_bounds__(256)
 estimate_kernel(const uint16_t* __restrict__ q,
-                const uint16_t* __restrict__ kmin,
-                const uint16_t* __restrict__ kmax,
+                uint16_t* __restrict__ kmin,
+                uint16_t* __restrict__ kmax,
                 const int32_t* __restrict__ page_table,
                 const int32_t* __restrict__ seq_lens,
                 float* __restrict__ scores, int Hkv, int max_pages,
-                int rows_per_head, int num_pool_pages, int page_size) {
+                int rows_per_head, int num_pool_pages, int page_size,
+                EstAppend ap) {
   const int b = blockIdx.y;
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
@@ -47,6 +59,22 @@ estimate_kernel(const uint16_t* __restrict__ q,
     est_page_ids(ent, n, jb * kEstPages, num_pool_pages, pid);
     uint4 lo[kEstPages], hi[kEstPages];
     est_load_meta(kmin, kmax, pid, Hkv, g, c, lo, hi);
+    if constexpr (APPEND) {
+      const int jl = L > 0 ? (L - 1) / page_size : -1;  // the appended token's page
+      const int u = jl - jb * kEstPages;
+      if (u >= 0 && u < kEstPages) {
+        int64_t p = -1;
+#pragma unroll
+        for (int w = 0; w < kEstPages; ++w) if (w == u) p = pid[w];
+        if (p >= 0) {  // a pool page below n: L - 1 < n * page_size
+          const int64_t src = ((int64_t)b * Hkv + g) * kHeadDim + c * 8;
+          const uint4 kn = *reinterpret_cast<const uint4*>(ap.k_new + src);
+          const uint4 vn = *reinterpret_cast<const uint4*>(ap.v_new + src);
+          est_append(u, (L - 1) - jl * page_size, p, Hkv, g, c, page_size, kn, vn,
+                     ap.k_pool, ap.v_pool, kmin, kmax, lo, hi);
+        }
+      }
+    }
     est_table(pt_row, max_pages, (jb + rows_per_head) * kEstPages, ent);  // prefetch
     if constexpr (PER_HEAD) {
       float s[G][kEstPages];
@@ -62,10 +90,11 @@ estimate_kernel(const uint16_t* __restrict__ q,
   }
 }
 
-template <DType T, int G, bool PER_HEAD>
+template <DType T, int G, bool PER_HEAD, bool APPEND>
 void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
               const void* kmax, const int32_t* page_table,
-              const int32_t* seq_lens, float* scores, hipStream_t stream) {
+              const int32_t* seq_lens, float* scores, const EstAppend& ap,
+              hipStream_t stream) {
   const int Hkv = kv.num_kv_heads;
   const int blocks_per_head = (kv.max_pages_per_seq + kEstPages - 1) / kEstPages;
   // Enough rows to keep ~24 waves per CU busy on 256 CUs, and never more
@@ -77,23 +106,27 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
   const int64_t rows = rph * Hkv;
   dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock),
             (unsigned)kv.batch);
-  estimate_kernel<T, G, PER_HEAD><<<grid, 256, 0, stream>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kmin),
-      static_cast<const uint16_t*>(kmax), page_table, seq_lens, scores, Hkv,
-      kv.max_pages_per_seq, (int)rph, kv.num_pool_pages, kv.page_size);
+  estimate_kernel<T, G, PER_HEAD, APPEND><<<grid, 256, 0, stream>>>(
+      static_cast<const uint16_t*>(q),
+      static_cast<uint16_t*>(const_cast<void*>(kmin)),
+      static_cast<uint16_t*>(const_cast<void*>(kmax)), page_table, seq_lens, scores,
+      Hkv, kv.max_pages_per_seq, (int)rph, kv.num_pool_pages, kv.page_size, ap);
 }
 
-template <DType T, bool PER_HEAD>
+template <DType T, bool PER_HEAD, bool APPEND>
 void dispatch_group(int G, const quest_paged_kv& kv, const void* q,
                     const void* kmin, const void* kmax,
                     const int32_t* page_table, const int32_t* seq_lens,
-                    float* scores, hipStream_t stream) {
+                    float* scores, const EstAppend& ap, hipStream_t stream) {
+#define QUEST_EST(GG) \
+  launch_t<T, GG, PER_HEAD, APPEND>(kv, q, kmin, kmax, page_table, seq_lens, scores, ap, stream)
   switch (G) {
-    case 1: launch_t<T, 1, PER_HEAD>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
-    case 2: launch_t<T, 2, PER_HEAD>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
-    case 4: launch_t<T, 4, PER_HEAD>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
-    default: launch_t<T, 8, PER_HEAD>(kv, q, kmin, kmax, page_table, seq_lens, scores, stream); break;
+    case 1: QUEST_EST(1); break;
+    case 2: QUEST_EST(2); break;
+    case 4: QUEST_EST(4); break;
+    default: QUEST_EST(8); break;
   }
+#undef QUEST_EST
 }
 
 }  // namespace
@@ -105,19 +138,24 @@ bool estimate_supported(int group) {
 hipError_t launch_estimate(const quest_paged_kv& kv, const void* q,
                            const void* kmin, const void* kmax,
                            const int32_t* page_table, const int32_t* seq_lens,
-                           float* scores, bool per_head, hipStream_t stream) {
+                           float* scores, bool per_head, hipStream_t stream,
+                           void* k_pool, void* v_pool, const void* k_new,
+                           const void* v_new) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
-  if (per_head) {
-    if (kv.dtype == QUEST_F16)
-      dispatch_group<DType::F16, true>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, stream);
-    else
-      dispatch_group<DType::BF16, true>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, stream);
+  const EstAppend ap{static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
+                     static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new)};
+  const bool append = k_new != nullptr;
+#define QUEST_EST_D(TT, PH, AP) \
+  dispatch_group<TT, PH, AP>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, ap, stream)
+  if (kv.dtype == QUEST_F16) {
+    if (per_head) { if (append) QUEST_EST_D(DType::F16, true, true); else QUEST_EST_D(DType::F16, true, false); }
+    else { if (append) QUEST_EST_D(DType::F16, false, true); else QUEST_EST_D(DType::F16, false, false); }
   } else {
-    if (kv.dtype == QUEST_F16)
-      dispatch_group<DType::F16, false>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, stream);
-    else
-      dispatch_group<DType::BF16, false>(G, kv, q, kmin, kmax, page_table, seq_lens, scores, stream);
+    if (per_head) { if (append) QUEST_EST_D(DType::BF16, true, true); else QUEST_EST_D(DType::BF16, true, false); }
+    else { if (append) QUEST_EST_D(DType::BF16, false, true); else QUEST_EST_D(DType::BF16, false, false); }
   }
+#undef QUEST_EST_D
   return hipGetLastError();
 }
 

@@ -25,11 +25,15 @@ hipError_t launch_meta_append(const quest_paged_kv& kv, void* k_pool,
 // True when an estimate kernel exists for this group size.
 bool estimate_supported(int group);
 // per_head: one score row per query head ([B][Hq][max_pages]) instead of
-// one per kv-head holding the group's sum.
+// one per kv-head holding the group's sum.  k_new non-null: append token
+// L_b - 1 first (k_new / v_new into k_pool / v_pool and its page's box; the
+// boxes are then written, so kmin / kmax must be writable).
 hipError_t launch_estimate(const quest_paged_kv& kv, const void* q,
                            const void* kmin, const void* kmax,
                            const int32_t* page_table, const int32_t* seq_lens,
-                           float* scores, bool per_head, hipStream_t stream);
+                           float* scores, bool per_head, hipStream_t stream,
+                           void* k_pool = nullptr, void* v_pool = nullptr,
+                           const void* k_new = nullptr, const void* v_new = nullptr);
 
 // union.hip: per (request, kv-head), the ascending union of the G query
 // heads' k-entry lists, -1 padded to G*k; max_pages <= kTopkMaxPages.

@@ -18,28 +18,6 @@
 namespace quest {
 namespace {
 
-__device__ __forceinline__ void fold8(const uint4& x, int32_t (&mn)[8],
-                                      int32_t (&mx)[8]) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int32_t lo = ord16(w[i] & 0xffffu), hi = ord16(w[i] >> 16);
-    mn[2 * i] = min(mn[2 * i], lo);
-    mx[2 * i] = max(mx[2 * i], lo);
-    mn[2 * i + 1] = min(mn[2 * i + 1], hi);
-    mx[2 * i + 1] = max(mx[2 * i + 1], hi);
-  }
-}
-
-__device__ __forceinline__ uint4 pack8(const int32_t (&k)[8]) {
-  uint4 r;
-  r.x = unord16(k[0]) | (unord16(k[1]) << 16);
-  r.y = unord16(k[2]) | (unord16(k[3]) << 16);
-  r.z = unord16(k[4]) | (unord16(k[5]) << 16);
-  r.w = unord16(k[6]) | (unord16(k[7]) << 16);
-  return r;
-}
-
 // One wave per (request b, logical page j, kv-head g).
 __global__ void __launch_bounds__(256)
 meta_rebuild_kernel(const uint16_t* __restrict__ k_pool,

@@ -177,11 +177,15 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
                          scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o,  \
                          ws_ml, pl.nsplit, stream)
   const bool s32 = kv.page_size == 32;
+  // scores per thread: the fewest that cover the row (fewer VGPRs, shorter
+  // load and select)
   if (kv.dtype == QUEST_F16) {
     if (mp <= 2048) { if (s32) QUEST_TA_D(DType::F16, 8, 2); else QUEST_TA_D(DType::F16, 8, 1); }
+    else if (mp <= 4096) { if (s32) QUEST_TA_D(DType::F16, 16, 2); else QUEST_TA_D(DType::F16, 16, 1); }
     else { if (s32) QUEST_TA_D(DType::F16, 32, 2); else QUEST_TA_D(DType::F16, 32, 1); }
   } else {
     if (mp <= 2048) { if (s32) QUEST_TA_D(DType::BF16, 8, 2); else QUEST_TA_D(DType::BF16, 8, 1); }
+    else if (mp <= 4096) { if (s32) QUEST_TA_D(DType::BF16, 16, 2); else QUEST_TA_D(DType::BF16, 16, 1); }
     else { if (s32) QUEST_TA_D(DType::BF16, 32, 2); else QUEST_TA_D(DType::BF16, 32, 1); }
   }
 #undef QUEST_TA_D

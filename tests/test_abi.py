@@ -242,3 +242,16 @@ def test_host_pool_needs_pinned_cpu_tensor():
     import torch
     with pytest.raises(ValueError, match="pinned"):
         qa.HostPool(torch.zeros(4, 128, dtype=torch.float16))
+
+
+def test_append_estimate_validation():
+    k = kv()
+    P = ctypes.c_void_p
+    args = [P(FAKE)] * 10   # k_pool v_pool kmin kmax pt lens k_new v_new q scores
+    for i, name in enumerate(["k_pool", "v_pool", "kmin", "kmax", "page_table",
+                              "seq_lens", "k_new", "v_new", "q", "scores"]):
+        bad = list(args)
+        bad[i] = None
+        assert qa.LIB.quest_append_estimate(ctypes.byref(k), *bad, None) == \
+            _abi.QUEST_ERR_INVALID_ARGUMENT
+        assert name in qa.LIB.quest_last_error().decode()

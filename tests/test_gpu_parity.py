@@ -28,6 +28,8 @@ CASES = {
     "gqa8_f16": (1, 16, 2, (1500,), 320, "f16", True, 0, 0),
     "planted_f16": (2, 8, 8, (4096, 3000), 256, "f16", False, 4, 5),
     "with_empty_request": (3, 2, 2, (0, 33, 16), 32, "f16", True, 0, 0),
+    # rows of 2048..4096 pages (the 16-scores-per-thread Top-K variant)
+    "gqa4_2500_pages": (1, 8, 2, (39990,), 512, "f16", True, 4, 0),
 }
 
 
