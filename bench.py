@@ -70,9 +70,15 @@ CSRC = os.path.join(ROOT, "query_aware_kv_amd", "csrc")
 # The kernels each timed call launches, and the sources they compile from
 # (a change to any of them invalidates the recorded HBM traffic).
 CALLS = {
+    "quest_sparse_decode_attn": {
+        "kernels": ["attn_split_kernel", "attn_merge_kernel"],
+        "sources": ["attention.hip", "dev_attn.h", "common.h", "launch.h"]},
     "quest_estimate": {
         "kernels": ["estimate_kernel"],
         "sources": ["estimate.hip", "dev_estimate.h", "common.h", "launch.h"]},
+    "quest_topk_pages": {
+        "kernels": ["topk_kernel"],
+        "sources": ["topk.hip", "dev_topk.h", "common.h", "launch.h"]},
     "quest_topk_sparse_decode_attn": {
         "kernels": ["topk_attn_kernel", "attn_merge_kernel"],
         "sources": ["topk_attn.hip", "attention.hip", "dev_topk.h",
@@ -257,13 +263,13 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
     kv = insts[0]["kv"]
     k = wls[0].k_pages
     sm = 1.0 / math.sqrt(128)
-    steps = [qa.SparseDecodeStep(kv, k, sm) for _ in range(rot)]
+    steps = [qa.SparseDecodeStep(kv, k, sm, select=args.select) for _ in range(rot)]
     denses = [qa.DenseDecode(kv, sm) for _ in range(rot)] if with_dense else []
 
-    def step_call(i):
+    def step_call(i, sts=steps):
         c = insts[i]
-        steps[i](c["q"], c["k_pool"], c["v_pool"], c["kmin"], c["kmax"],
-                 c["page_table"], c["seq_lens"])
+        sts[i](c["q"], c["k_pool"], c["v_pool"], c["kmin"], c["kmax"],
+               c["page_table"], c["seq_lens"])
 
     def dense_call(i):
         c = insts[i]
@@ -279,13 +285,27 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
     t_graph = tm.run(lambda i: step_graphs[i].replay(), args.steps, args.warmup,
                      rot, events=percentiles)
     t_eager = tm.run(step_call, args.steps, args.warmup, rot, events=False)
+
     # One graph holding one step per cache, back to back (as a serving loop
     # captures consecutive layers): no host work between steps.
-    all_steps = capture(torch, lambda: [step_call(i) for i in range(rot)])
-    reps = max(1, args.steps // rot)
-    t_batch = tm.run(lambda i: all_steps.replay(), reps, max(1, args.warmup // rot),
-                     1, events=False)
-    t_batch = dict(mean=t_batch["mean"] / rot)
+    def batch_us(sts):
+        g = capture(torch, lambda: [step_call(i, sts) for i in range(rot)])
+        t = tm.run(lambda i: g.replay(), max(1, args.steps // rot),
+                   max(1, args.warmup // rot), 1, events=False)
+        return t["mean"] / rot
+
+    t_batch = dict(mean=batch_us(steps))
+    # the other places the selection can run, timed the same way
+    by_select = {steps[0].select: round(t_batch["mean"], 3)}
+    for mode in ("attention", "separate"):
+        if mode in by_select:
+            continue
+        alt = [qa.SparseDecodeStep(kv, k, sm, select=mode) for _ in range(rot)]
+        for i in range(rot):
+            step_call(i, alt)
+        torch.cuda.synchronize()
+        by_select[mode] = round(batch_us(alt), 3)
+        del alt
     t_dense = None
     if with_dense:
         dense_all = capture(torch, lambda: [dense_call(i) for i in range(rot)])
@@ -321,14 +341,19 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
                                     sm, st.out, st.workspace)
 
     reps = max(10, args.steps // rot)
-    us_est = call_us(torch, est, rot, reps)
-    other = {}
-    if steps[0].fused_topk:
-        other["quest_topk_sparse_decode_attn_ex (2 sink + 2 local pages)"] = \
-            round(call_us(torch, topk_attn_forced, rot, reps), 3)
-    other["quest_topk_pages"] = round(call_us(torch, topk_sep, rot, reps), 3)
-    other["quest_sparse_decode_attn"] = round(call_us(torch, attn_sep, rot, reps), 3)
-    us_ta = call_us(torch, topk_attn, rot, reps) if steps[0].fused_topk else None
+    mode = steps[0].select
+    fits = kv.max_pages_per_seq <= qa.TOPK_ATTN_MAX_PAGES
+    us = {}
+    us["quest_estimate"] = call_us(torch, est, rot, reps)
+    us["quest_topk_pages"] = call_us(torch, topk_sep, rot, reps)
+    us["quest_sparse_decode_attn"] = call_us(torch, attn_sep, rot, reps)
+    if fits:
+        us["quest_topk_sparse_decode_attn"] = call_us(torch, topk_attn, rot, reps)
+        us["quest_topk_sparse_decode_attn_ex (2 sink + 2 local pages)"] = \
+            call_us(torch, topk_attn_forced, rot, reps)
+    for i in range(rot):                 # leave the plain selection in every step
+        topk_sep(i)
+    torch.cuda.synchronize()
 
     sels = [st.sel.cpu().numpy() for st in steps]
     lens_all = [[int(x) for x in c["seq_lens"].cpu()] for c in insts]
@@ -337,17 +362,25 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
              for i in range(rot)]
     avg = {key: sum(b[key] for b in bstep) / rot for key in bstep[0]}
     B = kv.batch
-    est_bytes = avg["meta"] + avg["q"] + avg["table"] + \
-        kv.num_kv_heads * kv.max_pages_per_seq * 4 * B
-    ta_bytes = avg["kv"] + avg["q"] + avg["out"] + \
-        kv.num_kv_heads * (kv.max_pages_per_seq + k) * 4 * B
-    calls = {"quest_estimate": (us_est, est_bytes)}
-    if us_ta is not None:
-        calls["quest_topk_sparse_decode_attn"] = (us_ta, ta_bytes)
+    # per launch: what the call must read and write (its own outputs
+    # included), as the step's byte model counts them
+    score_bytes = kv.num_kv_heads * kv.max_pages_per_seq * 4 * B
+    sel_bytes = kv.num_kv_heads * k * 4 * B
+    est_bytes = avg["meta"] + avg["q"] + avg["table"] + score_bytes
+    kv_bytes = avg["kv"] + avg["q"] + avg["out"] + kv.num_kv_heads * k * 4 * B
+    nbytes = {"quest_estimate": est_bytes,
+              "quest_topk_pages": score_bytes + sel_bytes,
+              "quest_sparse_decode_attn": kv_bytes + sel_bytes,
+              "quest_topk_sparse_decode_attn": kv_bytes + score_bytes + sel_bytes}
+    step_calls = {"attention": ["quest_estimate", "quest_topk_sparse_decode_attn"],
+                  "separate": ["quest_estimate", "quest_topk_pages",
+                               "quest_sparse_decode_attn"]}[mode]
+    calls = {c: (us[c], nbytes[c]) for c in step_calls}
+    other = {c: round(v, 3) for c, v in us.items() if c not in calls}
     dbytes = sum(dense_bytes(l, kv.num_kv_heads, kv.num_q_heads, page_size=kv.page_size)
                  for l in lens_all) / rot
     return dict(t_graph=t_graph, t_eager=t_eager, t_batch=t_batch,
-                t_dense=t_dense, bytes=avg, other_calls=other,
+                t_dense=t_dense, bytes=avg, other_calls=other, by_select=by_select,
                 calls=calls, dense_bytes=dbytes, insts=insts, kv=kv, k_pages=k,
                 sm=sm)
 
@@ -408,6 +441,7 @@ def bench_longchat(args, torch, qa, synth):
         "graph_us_per_step": round(tg["mean"], 3),
         "graph_batch_us_per_step": round(tb["mean"], 3),
         "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
+        "step_us_by_select": r["by_select"],
         "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
         "other_call_us": r["other_calls"],
         "roofline": roofline(r["calls"], traffic_recorded=True),
@@ -445,6 +479,7 @@ def bench_ragged(args, torch, qa, synth):
         "graph_us_per_step": round(tg["mean"], 3),
         "graph_batch_us_per_step": round(tb["mean"], 3),
         "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
+        "step_us_by_select": r["by_select"],
         "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
         "roofline": roofline(r["calls"]),
         "gpu": torch.cuda.get_device_name(0),
@@ -502,7 +537,7 @@ def bench_gqa_multistep(args, torch, qa, synth):
         if layer < wl.dense_layers:
             st["dense"] = qa.DenseDecode(c["kv"], sm)
         else:
-            st["step"] = qa.SparseDecodeStep(c["kv"], k, sm)
+            st["step"] = qa.SparseDecodeStep(c["kv"], k, sm, select=args.select)
         st["q"] = torch.stack([synth.draw_query(wl, layer, dev, step=s)
                                for s in range(nsteps)])
         kn, vn = zip(*[synth.draw_append_token(wl, layer, s, dev)
@@ -888,6 +923,9 @@ def main():
     ap.add_argument("--workload", default="longchat",
                     choices=["longchat", "gqa_multistep", "ragged", "sweep",
                              "gqa_union", "page32", "host_kv"])
+    ap.add_argument("--select", default="auto",
+                    choices=["auto", "attention", "separate"],
+                    help="where the sparse step runs its Top-K (SparseDecodeStep)")
     ap.add_argument("--rotate", type=int, default=8,
                     help="independent caches the steps cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -54,20 +54,36 @@ def alloc_meta(kv: PagedKV, device="cuda"):
 
 
 TOPK_ATTN_MAX_PAGES = 8192
+SELECT_MODES = ("auto", "attention", "separate")
+# With more (request, kv-head) rows than this, a separate Top-K launch (one
+# selection per row) beats selecting in every attention workgroup (one per
+# row and split): measured on the 32 x 32-head ragged batch (1024 rows).
+AUTO_ATTENTION_MAX_ROWS = 256
 
 
 class SparseDecodeStep:
     """Buffers and call sequence of one sparse decode step for a fixed
-    geometry: quest_estimate, then quest_topk_sparse_decode_attn_ex (Top-K
-    and attention in one launch) -- or, with ``fused_topk=False`` or beyond
-    its size limit, quest_topk_pages_ex then quest_sparse_decode_attn.
-    ``n_sink`` / ``n_local`` force the first / last pages of every row into
-    the selection (0, 0: plain Top-K).
+    geometry: quest_estimate, then the Top-K and the sparse attention.
+    ``select`` says where the Top-K runs:
+
+    - "attention": inside the attention launch
+      (quest_topk_sparse_decode_attn_ex: every workgroup of a row selects
+      the row's pages itself, so no selection crosses memory);
+    - "separate": its own launch (quest_topk_pages_ex, one workgroup per
+      row), then quest_sparse_decode_attn;
+    - "auto" (default): "attention" for up to 256 (request, kv-head) rows,
+      "separate" beyond.
+
+    "attention" needs max_pages_per_seq <= 8192 and falls back to
+    "separate" beyond it.  ``n_sink`` / ``n_local`` force the first / last
+    pages of every row into the selection (0, 0: plain Top-K).
     """
 
     def __init__(self, kv: PagedKV, k_pages: int, sm_scale: float | None = None,
-                 device="cuda", fused_topk: bool = True, n_sink: int = 0,
+                 device="cuda", select: str = "auto", n_sink: int = 0,
                  n_local: int = 0):
+        if select not in SELECT_MODES:
+            raise ValueError(f"select must be one of {SELECT_MODES}, got {select!r}")
         self.kv = kv
         self.k_pages = int(k_pages)
         self.n_sink, self.n_local = int(n_sink), int(n_local)
@@ -80,15 +96,14 @@ class SparseDecodeStep:
         self.out = torch.empty(B, Hq, kv.head_dim, dtype=torch.float32,
                                device=device)
         self.workspace = alloc_workspace(kv, self.k_pages, device)
-        self.fused_topk = bool(fused_topk) and \
-            kv.max_pages_per_seq <= TOPK_ATTN_MAX_PAGES and \
+        if select == "auto":
+            select = "attention" if B * Hkv <= AUTO_ATTENTION_MAX_ROWS else "separate"
+        fits = kv.max_pages_per_seq <= TOPK_ATTN_MAX_PAGES and \
             self.k_pages <= TOPK_ATTN_MAX_PAGES
+        self.select = select if fits else "separate"
 
-    def __call__(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_lens,
-                 stream=None) -> torch.Tensor:
-        quest_estimate(self.kv, q, kmin, kmax, page_table, seq_lens,
-                       self.scores, stream)
-        if self.fused_topk:
+    def _select_attend(self, q, k_pool, v_pool, page_table, seq_lens, stream):
+        if self.select == "attention":
             quest_topk_sparse_decode_attn_ex(
                 self.kv, q, k_pool, v_pool, page_table, seq_lens, self.scores,
                 self.k_pages, self.n_sink, self.n_local, self.sm_scale,
@@ -101,6 +116,12 @@ class SparseDecodeStep:
                                  self.sm_scale, self.out, self.workspace,
                                  stream)
         return self.out
+
+    def __call__(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_lens,
+                 stream=None) -> torch.Tensor:
+        quest_estimate(self.kv, q, kmin, kmax, page_table, seq_lens,
+                       self.scores, stream)
+        return self._select_attend(q, k_pool, v_pool, page_table, seq_lens, stream)
 
     def append_step(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_lens,
                     k_new, v_new, stream=None) -> torch.Tensor:
@@ -109,19 +130,7 @@ class SparseDecodeStep:
         (quest_append_estimate), then select and attend."""
         quest_append_estimate(self.kv, k_pool, v_pool, kmin, kmax, page_table,
                               seq_lens, k_new, v_new, q, self.scores, stream)
-        if self.fused_topk:
-            quest_topk_sparse_decode_attn_ex(
-                self.kv, q, k_pool, v_pool, page_table, seq_lens, self.scores,
-                self.k_pages, self.n_sink, self.n_local, self.sm_scale,
-                self.sel, self.out, self.workspace, stream)
-            return self.out
-        quest_topk_pages_ex(self.kv, self.scores, seq_lens, self.k_pages,
-                            self.n_sink, self.n_local, self.sel, stream)
-        quest_sparse_decode_attn(self.kv, q, k_pool, v_pool, page_table,
-                                 seq_lens, self.sel, self.k_pages,
-                                 self.sm_scale, self.out, self.workspace,
-                                 stream)
-        return self.out
+        return self._select_attend(q, k_pool, v_pool, page_table, seq_lens, stream)
 
 
 class UnionDecodeStep:

@@ -135,9 +135,9 @@ def oracle_inputs(c, heads=None):
                 seq_lens=c["seq_lens"].cpu().numpy().astype(np.int64))
 
 
-def run_gpu_step(c, k_pages, kmin, kmax, sm_scale, fused_topk=True, n_sink=0,
+def run_gpu_step(c, k_pages, kmin, kmax, sm_scale, select="attention", n_sink=0,
                  n_local=0):
-    step = qa.SparseDecodeStep(c["kv"], k_pages, sm_scale, fused_topk=fused_topk,
+    step = qa.SparseDecodeStep(c["kv"], k_pages, sm_scale, select=select,
                                n_sink=n_sink, n_local=n_local)
     out = step(c["q"], c["k_pool"], c["v_pool"], kmin, kmax,
                c["page_table"], c["seq_lens"])

@@ -70,16 +70,16 @@ def test_append_estimate_equals_two_calls(name):
     assert torch.equal(i16(kp_a), i16(kp_b)) and torch.equal(i16(vp_a), i16(vp_b))
 
 
-@pytest.mark.parametrize("fused_topk", [True, False], ids=["topk_attn", "separate"])
+@pytest.mark.parametrize("select", ["attention", "separate"])
 @pytest.mark.parametrize("name", ["gqa4_bf16", "p32_gqa4_f16"])
-def test_append_step_equals_composition(name, fused_topk):
+def test_append_step_equals_composition(name, select):
     wl, c = make(name)
     kv = c["kv"]
     kmin_a, kmax_a = C.gpu_meta(c)
     kmin_b, kmax_b = kmin_a.clone(), kmax_a.clone()
     kp_b, vp_b = c["k_pool"].clone(), c["v_pool"].clone()
-    a = qa.SparseDecodeStep(kv, wl.k_pages, SM, fused_topk=fused_topk)
-    b = qa.SparseDecodeStep(kv, wl.k_pages, SM, fused_topk=fused_topk)
+    a = qa.SparseDecodeStep(kv, wl.k_pages, SM, select=select)
+    b = qa.SparseDecodeStep(kv, wl.k_pages, SM, select=select)
     for step in range(5):
         lens, k_new, v_new = appended(wl, c, step)
         q = synth.draw_query(wl, 0, "cuda", step=step)

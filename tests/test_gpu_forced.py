@@ -70,8 +70,8 @@ def test_topk_attn_ex_equals_separate_calls(name, ns, nl):
     kv = c["kv"]
     k = wl.k_pages
     kmin, kmax = C.gpu_meta(c)
-    a = qa.SparseDecodeStep(kv, k, SM, fused_topk=True, n_sink=ns, n_local=nl)
-    b = qa.SparseDecodeStep(kv, k, SM, fused_topk=False, n_sink=ns, n_local=nl)
+    a = qa.SparseDecodeStep(kv, k, SM, select="attention", n_sink=ns, n_local=nl)
+    b = qa.SparseDecodeStep(kv, k, SM, select="separate", n_sink=ns, n_local=nl)
     a.sel.fill_(-777)
     args = (c["q"], c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"],
             c["seq_lens"])
@@ -83,15 +83,15 @@ def test_topk_attn_ex_equals_separate_calls(name, ns, nl):
     assert torch.equal(a.out.view(torch.int32), b.out.view(torch.int32))
 
 
-@pytest.mark.parametrize("fused_topk", [True, False], ids=["topk_attn", "separate"])
+@pytest.mark.parametrize("select", ["attention", "separate"])
 @pytest.mark.parametrize("name,ns,nl", [
     ("planted_f16", 1, 2), ("gqa4_f16", 2, 4), ("mha_ragged_bf16", 3, 1)])
-def test_forced_step_matches_oracle(name, ns, nl, fused_topk):
+def test_forced_step_matches_oracle(name, ns, nl, select):
     wl, c = make(name)
     kv = c["kv"]
     kmin, kmax = C.gpu_meta(c)
     s_gpu, sel_gpu, out_gpu = C.run_gpu_step(c, wl.k_pages, kmin, kmax, SM,
-                                             fused_topk=fused_topk, n_sink=ns,
+                                             select=select, n_sink=ns,
                                              n_local=nl)
     o = C.oracle_inputs(c)
     omin, omax = O.page_meta(o["k_pool"], o["page_table"], o["seq_lens"], 16)

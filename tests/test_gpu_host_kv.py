@@ -40,9 +40,9 @@ def test_host_pools_match_device_pools(maker, name):
     idx = torch.tensor(o_pages, dtype=torch.long, device="cuda")
     assert torch.equal(hmin[idx].view(torch.int16), dmin[idx].view(torch.int16))
     assert torch.equal(hmax[idx].view(torch.int16), dmax[idx].view(torch.int16))
-    for fused in (True, False):
-        a = qa.SparseDecodeStep(kv, wl.k_pages, SM, fused_topk=fused)
-        b = qa.SparseDecodeStep(kv, wl.k_pages, SM, fused_topk=fused)
+    for select in qa.SELECT_MODES:
+        a = qa.SparseDecodeStep(kv, wl.k_pages, SM, select=select)
+        b = qa.SparseDecodeStep(kv, wl.k_pages, SM, select=select)
         a(c["q"], c["k_pool"], c["v_pool"], dmin, dmax, c["page_table"], c["seq_lens"])
         b(c["q"], hk, hv, dmin, dmax, c["page_table"], c["seq_lens"])
         torch.cuda.synchronize()

@@ -133,14 +133,14 @@ def test_topk_p32_rows_follow_page_count():
         assert np.array_equal(got[r, 0], O.topk_pages(s[r, 0].astype(np.float64), n, k))
 
 
-@pytest.mark.parametrize("fused_topk", [True, False], ids=["topk_attn", "separate"])
+@pytest.mark.parametrize("select", ["attention", "separate"])
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_sparse_step_p32(name, fused_topk):
+def test_sparse_step_p32(name, select):
     wl, c = make(name)
     kv = c["kv"]
     kmin, kmax = C.gpu_meta(c)
     s_gpu, sel_gpu, out_gpu = C.run_gpu_step(c, wl.k_pages, kmin, kmax, SM,
-                                             fused_topk=fused_topk)
+                                             select=select)
     o = C.oracle_inputs(c)
     omin, omax = oracle_meta(o)
     s_ora = O.estimate(o["q"], omin, omax, o["page_table"], o["seq_lens"], S,

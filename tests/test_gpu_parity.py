@@ -215,14 +215,14 @@ def test_topk_kernel_bitexact(mp, k):
         assert np.array_equal(got[r, 0], ref), f"row {r} n={n_list[r]}"
 
 
-@pytest.mark.parametrize("fused_topk", [True, False], ids=["topk_attn", "separate"])
+@pytest.mark.parametrize("select", ["attention", "separate"])
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_sparse_step_matches_oracle(name, fused_topk):
+def test_sparse_step_matches_oracle(name, select):
     wl, c = make(name)
     kv = c["kv"]
     kmin, kmax = C.gpu_meta(c)
     s_gpu, sel_gpu, out_gpu = C.run_gpu_step(c, wl.k_pages, kmin, kmax, SM,
-                                             fused_topk=fused_topk)
+                                             select=select)
     o = C.oracle_inputs(c)
     omin, omax = O.page_meta(o["k_pool"], o["page_table"], o["seq_lens"], 16)
     s_ora = O.estimate(o["q"], omin, omax, o["page_table"], o["seq_lens"], 16,
@@ -336,9 +336,9 @@ def test_topk_attn_equals_separate_calls(name, k_extra):
     k = wl.k_pages if k_extra is None else k_extra
     kv = c["kv"]
     kmin, kmax = C.gpu_meta(c)
-    a = qa.SparseDecodeStep(kv, k, SM, fused_topk=True)
-    b = qa.SparseDecodeStep(kv, k, SM, fused_topk=False)
-    if not a.fused_topk:
+    a = qa.SparseDecodeStep(kv, k, SM, select="attention")
+    b = qa.SparseDecodeStep(kv, k, SM, select="separate")
+    if a.select != "attention":
         pytest.skip("beyond the one-launch Top-K size limit")
     a.sel.fill_(-777)
     args = (c["q"], c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"],
@@ -351,16 +351,16 @@ def test_topk_attn_equals_separate_calls(name, k_extra):
     assert torch.equal(a.out.view(torch.int32), b.out.view(torch.int32))
 
 
-@pytest.mark.parametrize("fused_topk", [True, False], ids=["topk_attn", "separate"])
-def test_graph_replay_matches_eager(fused_topk):
+@pytest.mark.parametrize("select", ["attention", "separate"])
+def test_graph_replay_matches_eager(select):
     """The step captured in a HIP graph: every replay, with eager work and
     synchronisations in between and new queries copied in, equals an eager
     step on the same inputs."""
     wl, c = make("mha_ragged_f16")
     kv = c["kv"]
     kmin, kmax = C.gpu_meta(c)
-    step = qa.SparseDecodeStep(kv, wl.k_pages, SM, fused_topk=fused_topk)
-    ref = qa.SparseDecodeStep(kv, wl.k_pages, SM, fused_topk=fused_topk)
+    step = qa.SparseDecodeStep(kv, wl.k_pages, SM, select=select)
+    ref = qa.SparseDecodeStep(kv, wl.k_pages, SM, select=select)
     q = c["q"].clone()
     args = lambda qq: (qq, c["k_pool"], c["v_pool"], kmin, kmax,
                        c["page_table"], c["seq_lens"])
