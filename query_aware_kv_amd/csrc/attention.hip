@@ -122,16 +122,19 @@ using Plan = AttnPlan;
 }  // namespace
 
 // Pages per wave: as many as the group size allows while the grid keeps at
-// least ~1024 workgroups (4 per CU) to spread the loads over all 256 CUs.
-AttnPlan attention_plan(const quest_paged_kv& kv, int list_len) {
+// least ~4096 waves (16 per CU) to spread the loads over all 256 CUs.  With
+// fewer waves per workgroup than kAttnWaves the split count can only shrink,
+// so quest_workspace_size (planned for kAttnWaves) covers every plan.
+AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
   const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
+  const int64_t min_wgs = 4096 / waves;
   int ppw = 1;
   for (int cand = max_ppw(G, kv.page_size / kTileRows); cand > 1; cand /= 2) {
-    const int64_t ns = (list_len + kAttnWaves * cand - 1) / (kAttnWaves * cand);
-    if (units * ns >= 1024) { ppw = cand; break; }
+    const int64_t ns = (list_len + waves * cand - 1) / (waves * cand);
+    if (units * ns >= min_wgs) { ppw = cand; break; }
   }
-  const int nsplit = (list_len + kAttnWaves * ppw - 1) / (kAttnWaves * ppw);
+  const int nsplit = (list_len + waves * ppw - 1) / (waves * ppw);
   return {ppw, nsplit < 1 ? 1 : nsplit};
 }
 

@@ -146,18 +146,18 @@ __device__ __forceinline__ void attn_combine_rows(AttnState<G>& st) {
   }
 }
 
-constexpr int kAttnWaves = 4;  // waves per attention workgroup
+constexpr int kAttnWaves = 4;  // waves per attention workgroup (attn_split_kernel)
 
-template <int G>
+template <int G, int WAVES = kAttnWaves>
 struct AttnSmem {
-  float o[kAttnWaves][G][kHeadDim];
-  float m[kAttnWaves][G], l[kAttnWaves][G];
+  float o[WAVES][G][kHeadDim];
+  float m[WAVES][G], l[WAVES][G];
 };
 
 // Publish each wave's (row-combined) state to LDS.  Caller syncs after.
-template <int G>
+template <int G, int WAVES>
 __device__ __forceinline__ void attn_stage_wave(const AttnState<G>& st,
-                                                AttnSmem<G>& sm, int wid, int r,
+                                                AttnSmem<G, WAVES>& sm, int wid, int r,
                                                 int c) {
   if (r == 0) {
 #pragma unroll
@@ -173,16 +173,16 @@ __device__ __forceinline__ void attn_stage_wave(const AttnState<G>& st,
 }
 
 // The workgroup's combined (M, den, num[ch]) for head h, channel ch.
-template <int G>
-__device__ __forceinline__ void attn_wg_partial(const AttnSmem<G>& sm, int h, int ch,
+template <int G, int WAVES>
+__device__ __forceinline__ void attn_wg_partial(const AttnSmem<G, WAVES>& sm, int h, int ch,
                                                 float& M, float& den, float& num) {
   M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm.m[w][h]);
+  for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sm.m[w][h]);
   den = 0.f;
   num = 0.f;
 #pragma unroll
-  for (int w = 0; w < kAttnWaves; ++w) {
+  for (int w = 0; w < WAVES; ++w) {
     const float s = exp2_or_zero(sm.m[w][h], M);
     den += sm.l[w][h] * s;
     num += sm.o[w][h][ch] * s;

@@ -53,7 +53,8 @@ struct AttnPlan {
   int ppw;     // pages per wave
   int nsplit;  // workgroups (splits) per (request, kv-head) row
 };
-AttnPlan attention_plan(const quest_paged_kv& kv, int list_len);
+// waves: per workgroup (attn_split_kernel: 4; topk_attn_kernel: 8)
+AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves = 4);
 size_t attention_ml_offset(size_t slots);  // in floats, into the workspace
 void launch_merge(const quest_paged_kv& kv, const float* ws_o,
                   const float* ws_ml, int nsplit, float* out,

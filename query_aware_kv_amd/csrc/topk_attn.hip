@@ -12,6 +12,10 @@
 // deterministic), so none has to wait for another; each then writes its own
 // slice of sel_pages and attends over the same slice of the list.  This
 // removes a launch and the global round trip of the selection.
+//
+// Workgroups have 8 waves (one slice of 8 * PPW pages): the selection is
+// repeated once per workgroup, so half as many workgroups as with 4 waves
+// halves that repeated work while the same number of waves stream K/V.
 #include "dev_attn.h"
 #include "dev_topk.h"
 #include "launch.h"
@@ -19,8 +23,11 @@
 namespace quest {
 namespace {
 
+constexpr int kTaWaves = 8;
+constexpr int kTaThreads = kTaWaves * kWave;
+
 template <DType T, int G, int KPT, int PPW, int SUB>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kTaThreads)
 topk_attn_kernel(const uint16_t* __restrict__ q,
                  const uint16_t* __restrict__ k_pool,
                  const uint16_t* __restrict__ v_pool,
@@ -32,11 +39,11 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
                  int32_t* __restrict__ sel, float* __restrict__ out,
                  float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   __shared__ union {
-    TopkSmem<256> topk;
-    AttnSmem<G> attn;
+    TopkSmem<kTaThreads> topk;
+    AttnSmem<G, kTaWaves> attn;
   } sm;
   // This workgroup's slice of the row's selection.
-  __shared__ int32_t kept[kAttnWaves * PPW];
+  __shared__ int32_t kept[kTaWaves * PPW];
   const int unit = blockIdx.y;       // b * Hkv + g
   const int b = unit / Hkv, g = unit - (unit / Hkv) * Hkv;
   const int split = blockIdx.x, nsplit = gridDim.x;
@@ -45,19 +52,19 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
 
   // Scores, the length and q are independent loads.
   float v[KPT];
-  topk_load<256, KPT>(scores + (int64_t)unit * max_pages, max_pages, v);
+  topk_load<kTaThreads, KPT>(scores + (int64_t)unit * max_pages, max_pages, v);
   const int L = seq_lens[b];
   float qf[G][8];
   attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
   constexpr int S = SUB * kTileRows;
   const int n = pages_of(L, S, max_pages);
-  const int s0 = split * kAttnWaves * PPW;
-  topk_row<256, KPT>(v, n, k, n_sink, n_local, kept, nullptr, nullptr, sm.topk, s0,
-                     s0 + kAttnWaves * PPW);
+  const int s0 = split * kTaWaves * PPW;
+  topk_row<kTaThreads, KPT>(v, n, k, n_sink, n_local, kept, nullptr, nullptr, sm.topk,
+                            s0, s0 + kTaWaves * PPW);
   __syncthreads();
 
   // This workgroup's slice of the list: publish it, then attend over it.
-  for (int i = tid; i < kAttnWaves * PPW && s0 + i < k; i += 256)
+  for (int i = tid; i < kTaWaves * PPW && s0 + i < k; i += kTaThreads)
     sel[(int64_t)unit * k + s0 + i] = kept[i];
   int pj[PPW];
   int64_t pp[PPW];
@@ -91,7 +98,7 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
   __syncthreads();
 
   const int Hq = Hkv * G;
-  for (int idx = tid; idx < G * kHeadDim; idx += 256) {
+  for (int idx = tid; idx < G * kHeadDim; idx += kTaThreads) {
     const int h = idx / kHeadDim, ch = idx - h * kHeadDim;
     float M, den, num;
     attn_wg_partial(sm.attn, h, ch, M, den, num);
@@ -116,7 +123,7 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* k_pool,
               int n_local, float qscale, int32_t* sel, float* out, float* ws_o,
               float* ws_ml, int nsplit, hipStream_t stream) {
   dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
-  topk_attn_kernel<T, G, KPT, PPW, SUB><<<grid, 256, 0, stream>>>(
+  topk_attn_kernel<T, G, KPT, PPW, SUB><<<grid, kTaThreads, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), page_table, seq_lens, scores, k,
       n_sink, n_local, kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages, qscale, sel, out,
@@ -166,7 +173,7 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
                                  float sm_scale, int32_t* sel, float* out,
                                  void* workspace, hipStream_t stream) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
-  const AttnPlan pl = attention_plan(kv, k_pages);
+  const AttnPlan pl = attention_plan(kv, k_pages, kTaWaves);
   const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = ws_o ? ws_o + attention_ml_offset(slots) : nullptr;
@@ -177,16 +184,16 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
                          scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o,  \
                          ws_ml, pl.nsplit, stream)
   const bool s32 = kv.page_size == 32;
-  // scores per thread: the fewest that cover the row (fewer VGPRs, shorter
-  // load and select)
+  // scores per thread: the fewest (a multiple of 4) that cover the row
+  // (fewer VGPRs, shorter load and select)
   if (kv.dtype == QUEST_F16) {
-    if (mp <= 2048) { if (s32) QUEST_TA_D(DType::F16, 8, 2); else QUEST_TA_D(DType::F16, 8, 1); }
-    else if (mp <= 4096) { if (s32) QUEST_TA_D(DType::F16, 16, 2); else QUEST_TA_D(DType::F16, 16, 1); }
-    else { if (s32) QUEST_TA_D(DType::F16, 32, 2); else QUEST_TA_D(DType::F16, 32, 1); }
+    if (mp <= 2048) { if (s32) QUEST_TA_D(DType::F16, 4, 2); else QUEST_TA_D(DType::F16, 4, 1); }
+    else if (mp <= 4096) { if (s32) QUEST_TA_D(DType::F16, 8, 2); else QUEST_TA_D(DType::F16, 8, 1); }
+    else { if (s32) QUEST_TA_D(DType::F16, 16, 2); else QUEST_TA_D(DType::F16, 16, 1); }
   } else {
-    if (mp <= 2048) { if (s32) QUEST_TA_D(DType::BF16, 8, 2); else QUEST_TA_D(DType::BF16, 8, 1); }
-    else if (mp <= 4096) { if (s32) QUEST_TA_D(DType::BF16, 16, 2); else QUEST_TA_D(DType::BF16, 16, 1); }
-    else { if (s32) QUEST_TA_D(DType::BF16, 32, 2); else QUEST_TA_D(DType::BF16, 32, 1); }
+    if (mp <= 2048) { if (s32) QUEST_TA_D(DType::BF16, 4, 2); else QUEST_TA_D(DType::BF16, 4, 1); }
+    else if (mp <= 4096) { if (s32) QUEST_TA_D(DType::BF16, 8, 2); else QUEST_TA_D(DType::BF16, 8, 1); }
+    else { if (s32) QUEST_TA_D(DType::BF16, 16, 2); else QUEST_TA_D(DType::BF16, 16, 1); }
   }
 #undef QUEST_TA_D
   if (pl.nsplit > 1) launch_merge(kv, ws_o, ws_ml, pl.nsplit, out, stream);

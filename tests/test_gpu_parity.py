@@ -330,8 +330,9 @@ def test_workspace_reuse_is_stateless():
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_topk_attn_equals_separate_calls(name, k_extra):
     """quest_topk_sparse_decode_attn == quest_topk_pages then
-    quest_sparse_decode_attn, bit for bit, and it writes every slot of
-    sel_pages (which starts out full of a sentinel)."""
+    quest_sparse_decode_attn: the same selection bit for bit (and every slot
+    of sel_pages written, which starts out full of a sentinel), the same
+    output up to the float32 rounding of a different split and merge order."""
     wl, c = make(name)
     k = wl.k_pages if k_extra is None else k_extra
     kv = c["kv"]
@@ -348,7 +349,7 @@ def test_topk_attn_equals_separate_calls(name, k_extra):
     torch.cuda.synchronize()
     assert int((a.sel == -777).sum()) == 0
     assert torch.equal(a.sel, b.sel)
-    assert torch.equal(a.out.view(torch.int32), b.out.view(torch.int32))
+    C.assert_same_up_to_split_order(a.out, b.out)
 
 
 @pytest.mark.parametrize("select", ["attention", "separate"])
