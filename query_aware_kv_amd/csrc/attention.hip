@@ -7,7 +7,10 @@
 // arithmetic (PPW * 8 KiB in flight per wave).  The four waves meet in LDS;
 // with one split per row the workgroup writes the output directly, otherwise
 // a partial (o[128], M, den) per query head, which the merge kernel combines.
+#include <type_traits>
+
 #include "dev_attn.h"
+#include "dev_attn_mfma.h"
 #include "launch.h"
 
 namespace quest {
@@ -47,8 +50,6 @@ attn_split_kernel(const uint16_t* __restrict__ q,
     pp[pi] = (jr[pi] >= 0 && jr[pi] < max_pages)
                  ? page_table[(int64_t)b * max_pages + jr[pi]] : -1;
   const int L = seq_lens[b];
-  float qf[G][8];
-  attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
   constexpr int S = SUB * kTileRows;
   const int n = pages_of(L, S, max_pages);
   int pj[PPW];
@@ -56,26 +57,54 @@ attn_split_kernel(const uint16_t* __restrict__ q,
   for (int pi = 0; pi < PPW; ++pi)
     pj[pi] = (jr[pi] >= 0 && jr[pi] < n && pp[pi] >= 0 && pp[pi] < num_pool_pages)
                  ? jr[pi] : -1;
+  // valid tokens of tile s of page pi (<= 0: absent); uniform over the wave
+  auto tile_valid = [&](int pi, int s) {
+    return pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
+  };
   uint4 kx[PPW][SUB][4], vx[PPW][SUB][4];
+  if constexpr (G >= 2) {
+    // a query group: both products on the matrix cores (dev_attn_mfma.h)
+    uint4 qb[4];
+    mfma_load_q<G>(q, (int64_t)unit * G, lane, qb);
 #pragma unroll
-  for (int pi = 0; pi < PPW; ++pi)
+    for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
-    for (int s = 0; s < SUB; ++s)
-      if (pj[pi] >= 0 && L - pj[pi] * S - s * kTileRows > 0)
-        attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
-                       kx[pi][s], vx[pi][s]);
-
-  AttnState<G> st;
-  attn_init(st);
+      for (int s = 0; s < SUB; ++s)
+        if (tile_valid(pi, s) > 0)
+          mfma_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), lane,
+                         kx[pi][s], vx[pi][s]);
+    MfmaAttnState st;
+    mfma_attn_init(st);
 #pragma unroll
-  for (int pi = 0; pi < PPW; ++pi)
+    for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      const int v = pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
-      if (v > 0) attn_page<T, G>(st, qf, kx[pi][s], vx[pi][s], v, r);
-    }
-  attn_combine_rows(st);
-  attn_stage_wave(st, sm, wid, r, c);
+      for (int s = 0; s < SUB; ++s) {
+        const int v = tile_valid(pi, s);
+        if (v > 0) mfma_attn_page<T>(st, qb, kx[pi][s], vx[pi][s], v, qscale, lane);
+      }
+    mfma_attn_stage_wave(st, sm, wid, lane);
+  } else {
+    float qf[G][8];
+    attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+      for (int s = 0; s < SUB; ++s)
+        if (tile_valid(pi, s) > 0)
+          attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
+                         kx[pi][s], vx[pi][s]);
+    AttnState<G> st;
+    attn_init(st);
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        const int v = tile_valid(pi, s);
+        if (v > 0) attn_page<T, G>(st, qf, kx[pi][s], vx[pi][s], v, r);
+      }
+    attn_combine_rows(st);
+    attn_stage_wave(st, sm, wid, r, c);
+  }
   __syncthreads();
 
   const int Hq = Hkv * G;
@@ -110,10 +139,12 @@ attn_merge_kernel(const float* __restrict__ ws_o,
                out + qh * kHeadDim, sm);
 }
 
-// Pages per wave the registers allow: 16-token tiles per wave at most 4
-// (G = 1), 2 (G <= 4) or 1 (G = 8).
-int max_ppw(int G, int sub) {
-  const int tiles = G == 1 ? 4 : G <= 4 ? 2 : 1;
+// Pages per wave the registers allow: at most 4 16-token tiles per wave.
+// A group keeps its q as one MFMA operand (16 VGPRs whatever G is) and its
+// output in 32 accumulators, so every group size holds as many tiles as
+// G = 1.
+int max_ppw(int /*G*/, int sub) {
+  const int tiles = 4;
   return tiles / sub > 0 ? tiles / sub : 1;
 }
 
@@ -177,25 +208,18 @@ void dispatch(int G, int ppw, const quest_paged_kv& kv, const void* q,
   launch_split<T, GG, PP, SUB>(kv, q, k_pool, v_pool, page_table, seq_lens, sel,  \
                                list_len, qscale, out, ws_o, ws_ml, nsplit, stream)
   // ppw never exceeds max_ppw(G, SUB): only those variants are built
-  if (G == 1) {
+  auto by_ppw = [&](auto gg) {
+    constexpr int GG = decltype(gg)::value;
     if constexpr (SUB == 1) {
-      if (ppw == 4) { QUEST_SPLIT(1, 4); return; }
+      if (ppw == 4) { QUEST_SPLIT(GG, 4); return; }
     }
-    if (ppw == 2) QUEST_SPLIT(1, 2);
-    else QUEST_SPLIT(1, 1);
-  } else if (G == 2) {
-    if constexpr (SUB == 1) {
-      if (ppw == 2) { QUEST_SPLIT(2, 2); return; }
-    }
-    QUEST_SPLIT(2, 1);
-  } else if (G == 4) {
-    if constexpr (SUB == 1) {
-      if (ppw == 2) { QUEST_SPLIT(4, 2); return; }
-    }
-    QUEST_SPLIT(4, 1);
-  } else {
-    QUEST_SPLIT(8, 1);
-  }
+    if (ppw == 2) QUEST_SPLIT(GG, 2);
+    else QUEST_SPLIT(GG, 1);
+  };
+  if (G == 1) by_ppw(std::integral_constant<int, 1>{});
+  else if (G == 2) by_ppw(std::integral_constant<int, 2>{});
+  else if (G == 4) by_ppw(std::integral_constant<int, 4>{});
+  else by_ppw(std::integral_constant<int, 8>{});
 #undef QUEST_SPLIT
 }
 

@@ -16,7 +16,10 @@
 // Workgroups have 8 waves (one slice of 8 * PPW pages): the selection is
 // repeated once per workgroup, so half as many workgroups as with 4 waves
 // halves that repeated work while the same number of waves stream K/V.
+#include <type_traits>
+
 #include "dev_attn.h"
+#include "dev_attn_mfma.h"
 #include "dev_topk.h"
 #include "launch.h"
 
@@ -54,8 +57,13 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
   float v[KPT];
   topk_load<kTaThreads, KPT>(scores + (int64_t)unit * max_pages, max_pages, v);
   const int L = seq_lens[b];
+  // q: float registers for one head (VALU path), the MFMA operand for a group
   float qf[G][8];
-  attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
+  uint4 qb[4];
+  if constexpr (G >= 2)
+    mfma_load_q<G>(q, (int64_t)unit * G, lane, qb);
+  else
+    attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
   constexpr int S = SUB * kTileRows;
   const int n = pages_of(L, S, max_pages);
   const int s0 = split * kTaWaves * PPW;
@@ -75,26 +83,52 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
     pp[pi] = (j >= 0 && j < n) ? page_table[(int64_t)b * max_pages + j] : -1;
     pj[pi] = (pp[pi] >= 0 && pp[pi] < num_pool_pages) ? j : -1;
   }
+  // valid tokens of tile s of page pi (<= 0: absent); uniform over the wave
+  auto tile_valid = [&](int pi, int s) {
+    return pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
+  };
   uint4 kx[PPW][SUB][4], vx[PPW][SUB][4];
+  if constexpr (G >= 2) {
+    // a query group: both products on the matrix cores (dev_attn_mfma.h)
 #pragma unroll
-  for (int pi = 0; pi < PPW; ++pi)
+    for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
-    for (int s = 0; s < SUB; ++s)
-      if (pj[pi] >= 0 && L - pj[pi] * S - s * kTileRows > 0)
-        attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
-                       kx[pi][s], vx[pi][s]);
-  AttnState<G> st;
-  attn_init(st);
+      for (int s = 0; s < SUB; ++s)
+        if (tile_valid(pi, s) > 0)
+          mfma_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), lane,
+                         kx[pi][s], vx[pi][s]);
+    MfmaAttnState st;
+    mfma_attn_init(st);
 #pragma unroll
-  for (int pi = 0; pi < PPW; ++pi)
+    for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      const int v = pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
-      if (v > 0) attn_page<T, G>(st, qf, kx[pi][s], vx[pi][s], v, r);
-    }
-  attn_combine_rows(st);
-  __syncthreads();  // the Top-K scratch becomes the attention scratch
-  attn_stage_wave(st, sm.attn, wid, r, c);
+      for (int s = 0; s < SUB; ++s) {
+        const int v = tile_valid(pi, s);
+        if (v > 0) mfma_attn_page<T>(st, qb, kx[pi][s], vx[pi][s], v, qscale, lane);
+      }
+    __syncthreads();  // the Top-K scratch becomes the attention scratch
+    mfma_attn_stage_wave(st, sm.attn, wid, lane);
+  } else {
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+      for (int s = 0; s < SUB; ++s)
+        if (tile_valid(pi, s) > 0)
+          attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
+                         kx[pi][s], vx[pi][s]);
+    AttnState<G> st;
+    attn_init(st);
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        const int v = tile_valid(pi, s);
+        if (v > 0) attn_page<T, G>(st, qf, kx[pi][s], vx[pi][s], v, r);
+      }
+    attn_combine_rows(st);
+    __syncthreads();  // the Top-K scratch becomes the attention scratch
+    attn_stage_wave(st, sm.attn, wid, r, c);
+  }
   __syncthreads();
 
   const int Hq = Hkv * G;
@@ -141,25 +175,18 @@ void dispatch_g(int G, int ppw, const quest_paged_kv& kv, const void* q,
                            k, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,    \
                            nsplit, s)
   // ppw never exceeds the plan's limit for SUB: only those variants are built
-  if (G == 1) {
+  auto by_ppw = [&](auto gg) {
+    constexpr int GG = decltype(gg)::value;
     if constexpr (SUB == 1) {
-      if (ppw == 4) { QUEST_TA(1, 4); return; }
+      if (ppw == 4) { QUEST_TA(GG, 4); return; }
     }
-    if (ppw == 2) QUEST_TA(1, 2);
-    else QUEST_TA(1, 1);
-  } else if (G == 2) {
-    if constexpr (SUB == 1) {
-      if (ppw == 2) { QUEST_TA(2, 2); return; }
-    }
-    QUEST_TA(2, 1);
-  } else if (G == 4) {
-    if constexpr (SUB == 1) {
-      if (ppw == 2) { QUEST_TA(4, 2); return; }
-    }
-    QUEST_TA(4, 1);
-  } else {
-    QUEST_TA(8, 1);
-  }
+    if (ppw == 2) QUEST_TA(GG, 2);
+    else QUEST_TA(GG, 1);
+  };
+  if (G == 1) by_ppw(std::integral_constant<int, 1>{});
+  else if (G == 2) by_ppw(std::integral_constant<int, 2>{});
+  else if (G == 4) by_ppw(std::integral_constant<int, 4>{});
+  else by_ppw(std::integral_constant<int, 8>{});
 #undef QUEST_TA
 }
 
