@@ -97,9 +97,12 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
               hipStream_t stream) {
   const int Hkv = kv.num_kv_heads;
   const int blocks_per_head = (kv.max_pages_per_seq + kEstPages - 1) / kEstPages;
-  // Enough rows to keep ~24 waves per CU busy on 256 CUs, and never more
-  // rows per head than 4-page blocks.
-  const int64_t target_rows = 24576;
+  // About 196608 16-lane rows (768 waves per CU over the launch, a few
+  // 4-page blocks per row), never more rows per head than 4-page blocks.
+  // Measured on the 32 x 32-head ragged batch: 24576 rows 156 us, 98304
+  // 144 us, 196608 141 us, one block per row 145 us; rows of one head
+  // (B * Hkv <= 384) get one block per row either way.
+  const int64_t target_rows = 196608;
   int64_t rph = target_rows / ((int64_t)Hkv * kv.batch);
   if (rph < 1) rph = 1;
   if (rph > blocks_per_head) rph = blocks_per_head;
