@@ -100,8 +100,8 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
   // About 196608 16-lane rows (768 waves per CU over the launch, a few
   // 4-page blocks per row), never more rows per head than 4-page blocks.
   // Measured on the 32 x 32-head ragged batch: 24576 rows 156 us, 98304
-  // 144 us, 196608 141 us, one block per row 145 us; rows of one head
-  // (B * Hkv <= 384) get one block per row either way.
+  // 144 us, 196608 141 us, one block per row 145 us.  A single request
+  // of 32 heads gets one block per row up to 24K pages.
   const int64_t target_rows = 196608;
   int64_t rph = target_rows / ((int64_t)Hkv * kv.batch);
   if (rph < 1) rph = 1;
