@@ -139,29 +139,27 @@ attn_merge_kernel(const float* __restrict__ ws_o,
                out + qh * kHeadDim, sm);
 }
 
-// Pages per wave the registers allow: at most 4 16-token tiles per wave.
-// A group keeps its q as one MFMA operand (16 VGPRs whatever G is) and its
-// output in 32 accumulators, so every group size holds as many tiles as
-// G = 1.
-int max_ppw(int /*G*/, int sub) {
-  const int tiles = 4;
-  return tiles / sub > 0 ? tiles / sub : 1;
+// Pages per wave the registers allow: at most 4 16-token tiles per wave,
+// for every group size (a group keeps its q as one 16-VGPR MFMA operand and
+// its output in 32 accumulators, whatever G is).
+int max_ppw(int sub) {
+  constexpr int kTiles = 4;
+  return kTiles / sub > 0 ? kTiles / sub : 1;
 }
 
 using Plan = AttnPlan;
 
 }  // namespace
 
-// Pages per wave: as many as the group size allows while the grid keeps at
+// Pages per wave: as many as the registers allow while the grid keeps at
 // least ~4096 waves (16 per CU) to spread the loads over all 256 CUs.  With
-// fewer waves per workgroup than kAttnWaves the split count can only shrink,
+// more waves per workgroup than kAttnWaves the split count can only shrink,
 // so quest_workspace_size (planned for kAttnWaves) covers every plan.
 AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves) {
-  const int G = kv.num_q_heads / kv.num_kv_heads;
   const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
   const int64_t min_wgs = 4096 / waves;
   int ppw = 1;
-  for (int cand = max_ppw(G, kv.page_size / kTileRows); cand > 1; cand /= 2) {
+  for (int cand = max_ppw(kv.page_size / kTileRows); cand > 1; cand /= 2) {
     const int64_t ns = (list_len + waves * cand - 1) / (waves * cand);
     if (units * ns >= min_wgs) { ppw = cand; break; }
   }
@@ -207,7 +205,7 @@ void dispatch(int G, int ppw, const quest_paged_kv& kv, const void* q,
 #define QUEST_SPLIT(GG, PP)                                                        \
   launch_split<T, GG, PP, SUB>(kv, q, k_pool, v_pool, page_table, seq_lens, sel,  \
                                list_len, qscale, out, ws_o, ws_ml, nsplit, stream)
-  // ppw never exceeds max_ppw(G, SUB): only those variants are built
+  // ppw never exceeds max_ppw(SUB): only those variants are built
   auto by_ppw = [&](auto gg) {
     constexpr int GG = decltype(gg)::value;
     if constexpr (SUB == 1) {
