@@ -72,7 +72,8 @@ CSRC = os.path.join(ROOT, "query_aware_kv_amd", "csrc")
 CALLS = {
     "quest_sparse_decode_attn": {
         "kernels": ["attn_split_kernel", "attn_merge_kernel"],
-        "sources": ["attention.hip", "dev_attn.h", "common.h", "launch.h"]},
+        "sources": ["attention.hip", "dev_attn.h", "dev_attn_mfma.h", "common.h",
+                    "launch.h"]},
     "quest_estimate": {
         "kernels": ["estimate_kernel"],
         "sources": ["estimate.hip", "dev_estimate.h", "common.h", "launch.h"]},
@@ -82,7 +83,7 @@ CALLS = {
     "quest_topk_sparse_decode_attn": {
         "kernels": ["topk_attn_kernel", "attn_merge_kernel"],
         "sources": ["topk_attn.hip", "attention.hip", "dev_topk.h",
-                    "dev_attn.h", "common.h", "launch.h"]},
+                    "dev_attn.h", "dev_attn_mfma.h", "common.h", "launch.h"]},
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_longchat32k.md")
 
