@@ -119,8 +119,11 @@ QUEST_API quest_status quest_update_page_meta(
  *   p = page_table[b][j], for j < n_b; scores[b][g][j] = -inf for
  *   n_b <= j < max_pages_per_seq.
  * Unscaled (no 1/sqrt(d)); a GQA group's score is the sum of its G query
- * heads' bounds.  Products are exact in float32 for fp16/bf16 inputs of
- * normal range; the sum rounds in float32.
+ * heads' bounds.  The boxes must satisfy kmin <= kmax in every channel, as
+ * quest_update_page_meta writes them: each term is then evaluated as
+ * q_i * kmax_i for q_i >= 0 and q_i * kmin_i otherwise, which is the max.
+ * Products are exact in float32 for fp16/bf16 inputs of normal range; the
+ * sum rounds in float32.
  */
 QUEST_API quest_status quest_estimate(
     const quest_paged_kv* kv, const void* q, const void* kmin,

@@ -5,11 +5,19 @@
 // inequality): a page's score is sum_i max(q_i * kmin_i, q_i * kmax_i); here
 // unscaled, and a GQA group sums the bounds of its G query heads.
 //
-// Lane c of the row holds channels 8c..8c+7 of the G query heads (G*8 floats)
-// and reads 16 B of kmin and 16 B of kmax per page, so a page's 512 B of
-// metadata is read once with 16-byte loads; the 16 partial sums of a page
-// meet in a DPP row reduction.  Products of two fp16 (or bf16) values are
-// exact in float32; only the sum rounds.
+// Lane c of the row holds channels 8c..8c+7 of the G query heads (four
+// packed 16-bit pairs per head) and reads 16 B of kmin and 16 B of kmax per
+// page, so a page's 512 B of metadata is read once with 16-byte loads; the
+// 16 partial sums of a page meet in a DPP row reduction.
+//
+// A box has kmin_i <= kmax_i in every channel, so max(q_i kmin_i, q_i kmax_i)
+// is q_i kmax_i when q_i >= 0 and q_i kmin_i when q_i < 0 (for q_i = +-0 both
+// products are zero).  The bound is therefore a dot product of q with the
+// corner of the box that q's signs pick: a bit-select of the packed kmin /
+// kmax words by a mask of q's sign bits, then v_dot2_f32_{f16,bf16}, which
+// multiplies two pairs of 16-bit values and adds both products to a float32
+// accumulator.  Products of two fp16 (or bf16) values are exact in float32;
+// only the sum rounds.
 #pragma once
 
 #include "common.h"
@@ -18,14 +26,55 @@ namespace quest {
 
 constexpr int kEstPages = 4;  // pages per 16-lane row per block
 
-template <DType T, int G>
+// One lane's share of the G query heads: channels 8c..8c+7 of head h as
+// four words of two 16-bit values, and per word a mask that is 0xffff in
+// each half whose q value has its sign bit set (negative, or -0).
+template <int G>
+struct EstQ {
+  uint32_t w[G][4];
+  uint32_t neg[G][4];
+};
+
+template <int G>
 __device__ __forceinline__ void est_load_q(const uint16_t* __restrict__ q,
-                                           int64_t first_head, int c,
-                                           float (&qf)[G][8]) {
+                                           int64_t first_head, int c, EstQ<G>& qq) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-    widen8<T>(*reinterpret_cast<const uint4*>(q + (first_head + h) * kHeadDim + c * 8),
-              qf[h]);
+  for (int h = 0; h < G; ++h) {
+    const uint4 v = *reinterpret_cast<const uint4*>(q + (first_head + h) * kHeadDim + c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qq.w[h][i] = w[i];
+      qq.neg[h][i] = ((w[i] >> 15) & 0x00010001u) * 0xffffu;
+    }
+  }
+}
+
+// acc + a.lo * b.lo + a.hi * b.hi for two packed fp16 (bf16) pairs.
+template <DType T>
+__device__ __forceinline__ float est_dot2(uint32_t a, uint32_t b, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef short s2 __attribute__((ext_vector_type(2)));
+  if constexpr (T == DType::F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), acc,
+                                  false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s2, a), __builtin_bit_cast(s2, b),
+                                           acc, false);
+}
+
+// One lane's 8-channel part of head h's bound on a box (lo, hi).
+template <DType T, int G>
+__device__ __forceinline__ float est_part(const EstQ<G>& qq, int h, const uint4& lo,
+                                          const uint4& hi, float acc) {
+  const uint32_t l[4] = {lo.x, lo.y, lo.z, lo.w};
+  const uint32_t u[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = qq.neg[h][i];
+    acc = est_dot2<T>(qq.w[h][i], (l[i] & m) | (u[i] & ~m), acc);
+  }
+  return acc;
 }
 
 // Page-table entries of logical pages j0..j0+3.  Entries up to max_pages
@@ -66,7 +115,7 @@ __device__ __forceinline__ void est_load_meta(const uint16_t* __restrict__ kmin,
 
 // Bound of each of the 4 pages (every lane of the row gets all 4).
 template <DType T, int G>
-__device__ __forceinline__ void est_score(const float (&qf)[G][8],
+__device__ __forceinline__ void est_score(const EstQ<G>& qq,
                                           const int (&pid)[kEstPages],
                                           const uint4 (&lo)[kEstPages],
                                           const uint4 (&hi)[kEstPages],
@@ -75,13 +124,8 @@ __device__ __forceinline__ void est_score(const float (&qf)[G][8],
   for (int u = 0; u < kEstPages; ++u) {
     float acc = 0.f;
     if (pid[u] >= 0) {
-      float a[8], z[8];
-      widen8<T>(lo[u], a);
-      widen8<T>(hi[u], z);
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += fmaxf(qf[h][e] * a[e], qf[h][e] * z[e]);
+      for (int h = 0; h < G; ++h) acc = est_part<T, G>(qq, h, lo[u], hi[u], acc);
     }
     s[u] = row16_sum(acc);
   }
@@ -127,23 +171,16 @@ __device__ __forceinline__ void est_append(int u, int slot, int64_t p, int Hkv, 
 // Per-query-head bounds of the 4 pages: s[h][u] for the G heads of the
 // group, from one read of each box ("Guide to Quest", Best Practices 2).
 template <DType T, int G>
-__device__ __forceinline__ void est_score_heads(const float (&qf)[G][8],
+__device__ __forceinline__ void est_score_heads(const EstQ<G>& qq,
                                                 const int (&pid)[kEstPages],
                                                 const uint4 (&lo)[kEstPages],
                                                 const uint4 (&hi)[kEstPages],
                                                 float (&s)[G][kEstPages]) {
 #pragma unroll
   for (int u = 0; u < kEstPages; ++u) {
-    float a[8], z[8];
-    widen8<T>(lo[u], a);
-    widen8<T>(hi[u], z);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float acc = 0.f;
-      if (pid[u] >= 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += fmaxf(qf[h][e] * a[e], qf[h][e] * z[e]);
-      }
+      const float acc = pid[u] >= 0 ? est_part<T, G>(qq, h, lo[u], hi[u], 0.f) : 0.f;
       s[h][u] = row16_sum(acc);
     }
   }

@@ -50,8 +50,8 @@ estimate_kernel(const uint16_t* __restrict__ q,
   int ent[kEstPages];
   est_table(pt_row, max_pages, jb0 * kEstPages, ent);
   const int L = seq_lens[b];
-  float qf[G][8];
-  est_load_q<T, G>(q, ((int64_t)b * Hkv + g) * G, c, qf);
+  EstQ<G> qq;
+  est_load_q<G>(q, ((int64_t)b * Hkv + g) * G, c, qq);
   const int n = pages_of(L, page_size, max_pages);
 
   for (int jb = jb0; jb * kEstPages < max_pages; jb += rows_per_head) {
@@ -78,13 +78,13 @@ estimate_kernel(const uint16_t* __restrict__ q,
     est_table(pt_row, max_pages, (jb + rows_per_head) * kEstPages, ent);  // prefetch
     if constexpr (PER_HEAD) {
       float s[G][kEstPages];
-      est_score_heads<T, G>(qf, pid, lo, hi, s);
+      est_score_heads<T, G>(qq, pid, lo, hi, s);
 #pragma unroll
       for (int h = 0; h < G; ++h)
         est_store(srow + (int64_t)h * max_pages, jb * kEstPages, max_pages, c, pid, s[h]);
     } else {
       float s[kEstPages];
-      est_score<T, G>(qf, pid, lo, hi, s);
+      est_score<T, G>(qq, pid, lo, hi, s);
       est_store(srow, jb * kEstPages, max_pages, c, pid, s);
     }
   }

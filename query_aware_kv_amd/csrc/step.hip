@@ -106,15 +106,15 @@ __device__ __forceinline__ void est_item(const StepArgs& a, uint32_t t, StepSmem
   const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
   float* srow = a.scores + (int64_t)row * a.max_pages;
   if (j0 < a.max_pages) {
-    float qf[G][8];
-    est_load_q<T, G>(a.q, (int64_t)row * G, c, qf);
+    EstQ<G> qq;
+    est_load_q<G>(a.q, (int64_t)row * G, c, qq);
     int ent[kEstPages], pid[kEstPages];
     est_table(pt_row, a.max_pages, j0, ent);
     est_page_ids(ent, n, j0, a.num_pool_pages, pid);
     uint4 lo[kEstPages], hi[kEstPages];
     est_load_meta(a.kmin, a.kmax, pid, a.Hkv, g, c, lo, hi);
     float s[kEstPages];
-    est_score<T, G>(qf, pid, lo, hi, s);
+    est_score<T, G>(qq, pid, lo, hi, s);
     est_store(srow, j0, a.max_pages, c, pid, s);
   }
   if (blk >= counted) return;  // a padding-only item: nobody waits for it
