@@ -84,7 +84,7 @@ attn_split_kernel(const uint16_t* __restrict__ q,
       }
     mfma_attn_stage_wave(st, sm, wid, lane);
   } else {
-    float qf[G][8];
+    AttnQ<G> qf;
     attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
 #pragma unroll
     for (int pi = 0; pi < PPW; ++pi)

@@ -40,6 +40,31 @@ __device__ __forceinline__ void widen8(const uint4& v, float (&f)[8]) {
   }
 }
 
+// One 16-bit value of a packed word (half 0 = bits 0..15) widened to
+// float32; for fp16 the conversion folds into v_fma_mix_f32 when the result
+// feeds a multiply-add.
+template <DType T>
+__device__ __forceinline__ float widen_half(uint32_t w, int half) {
+  if constexpr (T == DType::F16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(half ? (w >> 16) : (w & 0xffffu)));
+  else
+    return __builtin_bit_cast(float, half ? (w & 0xffff0000u) : (w << 16));
+}
+
+// acc + a.lo * b.lo + a.hi * b.hi for two packed fp16 (bf16) pairs
+// (v_dot2_f32_f16 / v_dot2_f32_bf16).  The products are exact in float32.
+template <DType T>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef short s2 __attribute__((ext_vector_type(2)));
+  if constexpr (T == DType::F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), acc,
+                                  false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s2, a), __builtin_bit_cast(s2, b),
+                                           acc, false);
+}
+
 // Total order on 16-bit floating-point encodings (fp16 and bf16 share the
 // sign-magnitude layout): -inf < ... < -0 < +0 < ... < +inf as signed ints.
 // The map is an involution on the encodings.
@@ -124,10 +149,16 @@ __device__ __forceinline__ float shfl_xor_f(float x, int m) {
   return __shfl_xor(x, m, kWave);
 }
 
+// 2^x on the transcendental unit (v_exp_f32, about 1 ulp), without the
+// rescaling that keeps results below 2^-126 denormal: those flush to zero.
+// Softmax weights that small are below float32 resolution of any sum they
+// join (the largest weight of a row is 1).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // exp2 that maps (-inf) - (-inf) style inputs to 0 instead of NaN: callers
 // pass a difference whose left side may be -inf.
 __device__ __forceinline__ float exp2_or_zero(float a, float m) {
-  return a == -INFINITY ? 0.f : exp2f(a - m);
+  return a == -INFINITY ? 0.f : exp2_hw(a - m);
 }
 
 }  // namespace quest

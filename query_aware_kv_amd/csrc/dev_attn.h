@@ -12,9 +12,10 @@
 // Each row group r keeps its own online-softmax state over its tokens, so
 // the page loop needs no cross-row traffic; row groups, waves and splits are
 // combined afterwards with the usual rescaling.  Softmax runs in the exp2
-// domain (q pre-scaled by sm_scale * log2 e); accumulation is float32.
-// Tokens past a request's end are masked by selection, never by
-// multiplication, so unused slots may hold NaN.
+// domain (logits scaled by sm_scale * log2 e); accumulation is float32.
+// q.k is taken on packed 16-bit pairs with v_dot2 (exact products, float32
+// sum) and scaled once per row.  Tokens past a request's end are masked by
+// selection, never by multiplication, so unused slots may hold NaN.
 #pragma once
 
 #include "common.h"
@@ -39,17 +40,27 @@ __device__ __forceinline__ void attn_init(AttnState<G>& st) {
   }
 }
 
+// A lane's q: channels 8c..8c+7 of each of the G heads as four packed
+// 16-bit pairs, and the logit scale (sm_scale * log2 e).
+template <int G>
+struct AttnQ {
+  uint32_t w[G][4];
+  float scale;
+};
+
 template <DType T, int G>
 __device__ __forceinline__ void attn_load_q(const uint16_t* __restrict__ q,
                                             int64_t first_head, int c, float qscale,
-                                            float (&qf)[G][8]) {
+                                            AttnQ<G>& qq) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    widen8<T>(*reinterpret_cast<const uint4*>(q + (first_head + h) * kHeadDim + c * 8),
-              qf[h]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[h][e] *= qscale;
+    const uint4 v = *reinterpret_cast<const uint4*>(q + (first_head + h) * kHeadDim + c * 8);
+    qq.w[h][0] = v.x;
+    qq.w[h][1] = v.y;
+    qq.w[h][2] = v.z;
+    qq.w[h][3] = v.w;
   }
+  qq.scale = qscale;
 }
 
 // Element offset of 16-token tile s of pool page p, kv-head g, for pages of
@@ -76,32 +87,32 @@ __device__ __forceinline__ void attn_load_tile(const uint16_t* __restrict__ k_po
 // Fold one 16-token tile (its first v tokens valid; v <= 0 changes nothing)
 // into the row group's state.
 template <DType T, int G>
-__device__ __forceinline__ void attn_page(AttnState<G>& st, const float (&qf)[G][8],
+__device__ __forceinline__ void attn_page(AttnState<G>& st, const AttnQ<G>& qq,
                                           const uint4 (&kx)[4], const uint4 (&vx)[4],
                                           int v, int r) {
   bool valid[4];
-  float kf[4][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    valid[i] = r + 4 * i < v;
-    widen8<T>(kx[i], kf[i]);
-  }
+  for (int i = 0; i < 4; ++i) valid[i] = r + 4 * i < v;
   float z[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf(qf[h][e], kf[i][e], acc);
-      z[h][i] = row16_sum(acc);
+      float acc = dot2<T>(qq.w[h][0], kx[i].x, 0.f);
+      acc = dot2<T>(qq.w[h][1], kx[i].y, acc);
+      acc = dot2<T>(qq.w[h][2], kx[i].z, acc);
+      acc = dot2<T>(qq.w[h][3], kx[i].w, acc);
+      z[h][i] = row16_sum(acc) * qq.scale;
     }
-  float vf[4][8];
+  // V rows past the valid tokens become zeros (they may hold NaN), as
+  // packed words, before widening
+  uint32_t vw[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    widen8<T>(vx[i], vf[i]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vf[i][e] = valid[i] ? vf[i][e] : 0.f;
+    vw[i][0] = valid[i] ? vx[i].x : 0u;
+    vw[i][1] = valid[i] ? vx[i].y : 0u;
+    vw[i][2] = valid[i] ? vx[i].z : 0u;
+    vw[i][3] = valid[i] ? vx[i].w : 0u;
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -112,7 +123,7 @@ __device__ __forceinline__ void attn_page(AttnState<G>& st, const float (&qf)[G]
     float p[4], ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = valid[i] ? exp2f(z[h][i] - mx) : 0.f;
+      p[i] = valid[i] ? exp2_hw(z[h][i] - mx) : 0.f;
       ps += p[i];
     }
     st.l[h] = st.l[h] * alpha + ps;
@@ -120,7 +131,7 @@ __device__ __forceinline__ void attn_page(AttnState<G>& st, const float (&qf)[G]
     for (int e = 0; e < 8; ++e) {
       float acc = st.o[h][e] * alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = fmaf(p[i], vf[i][e], acc);
+      for (int i = 0; i < 4; ++i) acc = fmaf(p[i], widen_half<T>(vw[i][e >> 1], e & 1), acc);
       st.o[h][e] = acc;
     }
     st.m[h] = mx;

@@ -156,7 +156,7 @@ __device__ __forceinline__ void mfma_attn_page(MfmaAttnState& st, const uint4 (&
   float p[4], ps = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    p[e] = valid[e] ? exp2f(z[e] - m_new) : 0.f;
+    p[e] = valid[e] ? exp2_hw(z[e] - m_new) : 0.f;
     ps += p[e];
   }
   ps += shfl_xor_f(ps, 16);

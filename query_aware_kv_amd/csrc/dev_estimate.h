@@ -50,19 +50,6 @@ __device__ __forceinline__ void est_load_q(const uint16_t* __restrict__ q,
   }
 }
 
-// acc + a.lo * b.lo + a.hi * b.hi for two packed fp16 (bf16) pairs.
-template <DType T>
-__device__ __forceinline__ float est_dot2(uint32_t a, uint32_t b, float acc) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  typedef short s2 __attribute__((ext_vector_type(2)));
-  if constexpr (T == DType::F16)
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), acc,
-                                  false);
-  else
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s2, a), __builtin_bit_cast(s2, b),
-                                           acc, false);
-}
-
 // One lane's 8-channel part of head h's bound on a box (lo, hi).
 template <DType T, int G>
 __device__ __forceinline__ float est_part(const EstQ<G>& qq, int h, const uint4& lo,
@@ -72,7 +59,7 @@ __device__ __forceinline__ float est_part(const EstQ<G>& qq, int h, const uint4&
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t m = qq.neg[h][i];
-    acc = est_dot2<T>(qq.w[h][i], (l[i] & m) | (u[i] & ~m), acc);
+    acc = dot2<T>(qq.w[h][i], (l[i] & m) | (u[i] & ~m), acc);
   }
   return acc;
 }

@@ -167,7 +167,7 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, uint32_t t, StepSme
   __syncthreads();
   fence_acquire();
 
-  float qf[G][8];
+  AttnQ<G> qf;
   attn_load_q<T, G>(a.q, (int64_t)row * G, c, a.qscale, qf);
   const int i0 = (split * kAttnWaves + wid) * PPW;
   int pj[PPW];

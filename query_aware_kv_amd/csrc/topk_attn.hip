@@ -57,8 +57,8 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
   float v[KPT];
   topk_load<kTaThreads, KPT>(scores + (int64_t)unit * max_pages, max_pages, v);
   const int L = seq_lens[b];
-  // q: float registers for one head (VALU path), the MFMA operand for a group
-  float qf[G][8];
+  // q: packed words of one head (VALU path), the MFMA operand for a group
+  AttnQ<G> qf;
   uint4 qb[4];
   if constexpr (G >= 2)
     mfma_load_q<G>(q, (int64_t)unit * G, lane, qb);
