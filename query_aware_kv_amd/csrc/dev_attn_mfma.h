@@ -181,17 +181,25 @@ __device__ __forceinline__ void mfma_attn_page(MfmaAttnState& st, const uint4 (&
   const uint2 a_hi = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
   const uint2 a_lo = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
   // V column block b: channel 8j + b of tokens g + 4e, i.e. 16-bit element b
-  // of vx[e]; rows past the valid tokens may hold any bits (NaN included) and
-  // are replaced by zeros, since 0 * NaN would not vanish in the product
+  // of vx[e].  Rows past the valid tokens may hold any bits (NaN included)
+  // and become zeros first, as whole words, since 0 * NaN would not vanish
+  // in the product.  Each B operand word pairs the same half of two rows'
+  // words: one v_perm_b32 (byte selector 0x05040100 takes the low halves of
+  // its second and first source, 0x07060302 the high halves).
+  uint32_t vw[4][4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vw[e][0] = valid[e] ? vx[e].x : 0u;
+    vw[e][1] = valid[e] ? vx[e].y : 0u;
+    vw[e][2] = valid[e] ? vx[e].z : 0u;
+    vw[e][3] = valid[e] ? vx[e].w : 0u;
+  }
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t word = b < 2 ? vx[e].x : b < 4 ? vx[e].y : b < 6 ? vx[e].z : vx[e].w;
-      w[e] = valid[e] ? ((b & 1) ? (word >> 16) : (word & 0xffffu)) : 0u;
-    }
-    const uint2 vb = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+    const uint32_t sel = (b & 1) ? 0x07060302u : 0x05040100u;
+    const int wi = b >> 1;
+    const uint2 vb = make_uint2(__builtin_amdgcn_perm(vw[1][wi], vw[0][wi], sel),
+                                __builtin_amdgcn_perm(vw[3][wi], vw[2][wi], sel));
     st.o[b] = mfma_pv<T>(a_hi, vb, st.o[b]);
     st.o[b] = mfma_pv<T>(a_lo, vb, st.o[b]);
   }
