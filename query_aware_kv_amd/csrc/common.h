@@ -145,8 +145,46 @@ __device__ __forceinline__ uint32_t wave_last(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
-__device__ __forceinline__ float shfl_xor_f(float x, int m) {
-  return __shfl_xor(x, m, kWave);
+// The values of lane l and of its partner l ^ OFF: OFF = 16 pairs the rows
+// of a wave two by two (v_permlane16_swap_b32), OFF = 32 pairs its halves
+// (v_permlane32_swap_b32); one VALU instruction, no LDS round trip.  Both
+// lanes of a pair receive the same two values in the same order, so a
+// combine written in terms of (a, b) leaves both lanes bit-identical.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(uint32_t x, uint32_t& a, uint32_t& b) {
+  static_assert(OFF == 16 || OFF == 32, "row pairs or wave halves");
+  if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+  }
+}
+
+template <int OFF>
+__device__ __forceinline__ void lane_pair_f(float x, float& a, float& b) {
+  uint32_t ua, ub;
+  lane_pair<OFF>(__builtin_bit_cast(uint32_t, x), ua, ub);
+  a = __builtin_bit_cast(float, ua);
+  b = __builtin_bit_cast(float, ub);
+}
+
+// Max and sum of x over the lanes l, l ^ 16, l ^ 32, l ^ 48 (a column of
+// the wave's four rows), identical on all four.
+__device__ __forceinline__ float column4_max(float x) {
+  float a, b;
+  lane_pair_f<16>(x, a, b);
+  lane_pair_f<32>(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float column4_sum(float x) {
+  float a, b;
+  lane_pair_f<16>(x, a, b);
+  lane_pair_f<32>(a + b, a, b);
+  return a + b;
 }
 
 // 2^x on the transcendental unit (v_exp_f32, about 1 ulp), without the

@@ -138,23 +138,32 @@ __device__ __forceinline__ void attn_page(AttnState<G>& st, const AttnQ<G>& qq,
   }
 }
 
-// Combine the four row groups of a wave (lanes c, c+16, c+32, c+48).
-template <int G>
-__device__ __forceinline__ void attn_combine_rows(AttnState<G>& st) {
+// Combine the four row groups of a wave (lanes c, c+16, c+32, c+48): two
+// pairwise merges, each computed identically on both lanes of a pair.
+template <int OFF, int G>
+__device__ __forceinline__ void attn_combine_pair(AttnState<G>& st) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    float ma, mb, la, lb;
+    lane_pair_f<OFF>(st.m[h], ma, mb);
+    lane_pair_f<OFF>(st.l[h], la, lb);
+    const float M = fmaxf(ma, mb);
+    const float sa = exp2_or_zero(ma, M), sb = exp2_or_zero(mb, M);
+    st.l[h] = la * sa + lb * sb;
 #pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float mo = shfl_xor_f(st.m[h], off), lo = shfl_xor_f(st.l[h], off);
-      const float M = fmaxf(st.m[h], mo);
-      const float sa = exp2_or_zero(st.m[h], M), sb = exp2_or_zero(mo, M);
-      st.l[h] = st.l[h] * sa + lo * sb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        st.o[h][e] = st.o[h][e] * sa + shfl_xor_f(st.o[h][e], off) * sb;
-      st.m[h] = M;
+    for (int e = 0; e < 8; ++e) {
+      float oa, ob;
+      lane_pair_f<OFF>(st.o[h][e], oa, ob);
+      st.o[h][e] = oa * sa + ob * sb;
     }
+    st.m[h] = M;
   }
+}
+
+template <int G>
+__device__ __forceinline__ void attn_combine_rows(AttnState<G>& st) {
+  attn_combine_pair<16>(st);
+  attn_combine_pair<32>(st);
 }
 
 constexpr int kAttnWaves = 4;  // waves per attention workgroup (attn_split_kernel)

@@ -149,8 +149,7 @@ __device__ __forceinline__ void mfma_attn_page(MfmaAttnState& st, const uint4 (&
   float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 4; ++e) mx = valid[e] ? fmaxf(mx, z[e]) : mx;
-  mx = fmaxf(mx, shfl_xor_f(mx, 16));
-  mx = fmaxf(mx, shfl_xor_f(mx, 32));
+  mx = column4_max(mx);
   const float m_new = fmaxf(st.m, mx);
   const float alpha = exp2_or_zero(st.m, m_new);
   float p[4], ps = 0.f;
@@ -159,8 +158,7 @@ __device__ __forceinline__ void mfma_attn_page(MfmaAttnState& st, const uint4 (&
     p[e] = valid[e] ? exp2_hw(z[e] - m_new) : 0.f;
     ps += p[e];
   }
-  ps += shfl_xor_f(ps, 16);
-  ps += shfl_xor_f(ps, 32);
+  ps = column4_sum(ps);
   st.l = st.l * alpha + ps;
   st.m = m_new;
   // rescale O rows (heads 4g + e) by their heads' alpha, held by lanes 4g + e

@@ -51,12 +51,18 @@ meta_rebuild_kernel(const uint16_t* __restrict__ k_pool,
     const int t = r + 4 * i;
     if (t >= t0 && t < v) fold8(src[t * 16 + c], mn, mx);
   }
+  // the four row groups (lanes c, c+16, c+32, c+48) meet
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    mn[e] = min(mn[e], __shfl_xor(mn[e], 16, kWave));
-    mx[e] = max(mx[e], __shfl_xor(mx[e], 16, kWave));
-    mn[e] = min(mn[e], __shfl_xor(mn[e], 32, kWave));
-    mx[e] = max(mx[e], __shfl_xor(mx[e], 32, kWave));
+    uint32_t a, b;
+    lane_pair<16>((uint32_t)mn[e], a, b);
+    mn[e] = min((int32_t)a, (int32_t)b);
+    lane_pair<16>((uint32_t)mx[e], a, b);
+    mx[e] = max((int32_t)a, (int32_t)b);
+    lane_pair<32>((uint32_t)mn[e], a, b);
+    mn[e] = min((int32_t)a, (int32_t)b);
+    lane_pair<32>((uint32_t)mx[e], a, b);
+    mx[e] = max((int32_t)a, (int32_t)b);
   }
   const int64_t m = (p * Hkv + g) * kHeadDim + c * 8;
   uint4* dmin = reinterpret_cast<uint4*>(kmin + m);
