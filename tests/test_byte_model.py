@@ -1,0 +1,65 @@
+"""The benchmark's algorithmic byte model against the figures the pages and
+the arithmetic fix.
+
+- "The Memory Bandwidth Bottleneck of Long-Context Decoding" (Guide to
+  Quest) prices decode attention by the K and V bytes it must load, and
+  "Quest: Query-Aware Sparsity for Efficient Long-Context LLM Inference"
+  (paper summary), Summary, puts a 7B model's KV cache at 32K tokens at
+  about 16 GB (32 layers, 32 heads, head dim 128, fp16).
+- "Guide to Quest", Best Practices 1: the metadata is 2 vectors per page,
+  2/S of the page's K (12.5% at 16-token pages, 6.25% at 32).
+- Reading the bounds of every page plus K/V of k of n pages moves
+  n/16 + k page-equivalents of K+V, so the ideal speedup over dense is
+  16 n / (n + 16 k): 8.0x at 32K context and a 2048-token budget.
+"""
+import pytest
+
+import bench
+
+pytestmark = pytest.mark.filterwarnings("ignore")
+
+
+def test_longchat_layer_bytes():
+    b = bench.step_bytes([32768], 32, 32, 128)
+    assert b["meta"] == 32 * 2048 * 2 * 128 * 2 == 32 * 2**20
+    assert b["kv"] == 32 * 128 * 16 * 2 * 128 * 2 == 32 * 2**20
+    assert b["q"] == 32 * 128 * 2 and b["out"] == 32 * 128 * 4
+    assert b["table"] == 2048 * 4
+    assert b["total"] == 67_141_632
+
+
+def test_kv_cache_of_a_7b_model_at_32k_is_16_gib():
+    assert bench.kv_cache_bytes(32, 32, 128, 32768) == 16 * 2**30
+
+
+@pytest.mark.parametrize("S, frac", [(16, 0.125), (32, 0.0625)])
+def test_metadata_fraction_of_k(S, frac):
+    L = 4096
+    n = L // S
+    meta = bench.step_bytes([L], 1, 1, 1, page_size=S)["meta"]
+    k_bytes = n * S * 128 * 2
+    assert meta / k_bytes == frac
+
+
+def test_ideal_speedup_at_32k_budget_2048():
+    sparse = bench.step_bytes([32768], 32, 32, 128)
+    dense = bench.dense_bytes([32768], 32, 32)
+    kv_only = (sparse["meta"] + sparse["kv"]) / (dense - 32 * 128 * 6 - 2048 * 4)
+    assert abs(1 / kv_only - 16 * 2048 / (2048 + 16 * 128)) < 1e-12
+    assert abs(1 / kv_only - 8.0) < 1e-12
+
+
+def test_partial_last_page_counts_valid_tokens_only():
+    # 17 tokens: page 0 full, page 1 holds one token
+    b = bench.step_bytes([17], 1, 1, 2, sel=[[[0, 1]]])
+    assert b["kv"] == (16 + 1) * 2 * 128 * 2
+    b = bench.step_bytes([17], 1, 1, 2, sel=[[[1, -1]]])
+    assert b["kv"] == 1 * 2 * 128 * 2
+
+
+def test_gqa_reads_kv_once_per_kv_head():
+    """Four query heads share a kv-head: K/V bytes follow Hkv, q and out Hq."""
+    b = bench.step_bytes([32768], 8, 32, 128)
+    assert b["kv"] == 8 * 128 * 16 * 2 * 128 * 2
+    assert b["meta"] == 8 * 2048 * 512
+    assert b["q"] == 32 * 128 * 2 and b["out"] == 32 * 128 * 4
