@@ -34,7 +34,8 @@ def default_sm_scale(head_dim: int = HEAD_DIM) -> float:
 
 
 def alloc_workspace(kv: PagedKV, k_pages: int, device="cuda") -> torch.Tensor:
-    """Zero-filled attention workspace (the calls keep its counters zero)."""
+    """Attention workspace: per-split partial results, whose contents on
+    entry do not matter (allocated zeroed all the same)."""
     n = quest_workspace_size(kv, k_pages)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
