@@ -228,14 +228,25 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ o,
   const int ch = tid & (kHeadDim - 1), half = tid >> 7;
   float mr = -INFINITY, num = 0.f, den = 0.f;
   for (int s0 = half; s0 < nsplit; s0 += 2 * kChunk) {
+    // Every load is issued, from a split index clamped into range, so the
+    // chunk's loads go out back to back; splits past the end are masked
+    // afterwards.
     float w[kChunk], l[kChunk], x[kChunk];
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
-      const int s = s0 + 2 * u;
-      const bool ok = s < nsplit;
-      w[u] = ok ? ml[2 * s] : -INFINITY;
-      l[u] = ok ? ml[2 * s + 1] : 0.f;
-      x[u] = ok ? o[(int64_t)s * kHeadDim + ch] : 0.f;
+      const int sc = min(s0 + 2 * u, nsplit - 1);
+      const float2 m_l = *reinterpret_cast<const float2*>(ml + 2 * sc);
+      w[u] = m_l.x;
+      l[u] = m_l.y;
+      x[u] = o[(int64_t)sc * kHeadDim + ch];
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (s0 + 2 * u >= nsplit) {
+        w[u] = -INFINITY;
+        l[u] = 0.f;
+        x[u] = 0.f;
+      }
     }
     float mc = mr;
 #pragma unroll
