@@ -36,19 +36,28 @@ attn_split_kernel(const uint16_t* __restrict__ q,
 
   // List entries, then their table entries: neither waits for the length
   // (both are in bounds on their own); the length only masks afterwards.
+  // The loads are unconditional, from indices clamped into the row (slots
+  // past the end read a valid entry and discard it), so each group goes
+  // out back to back with one wait.
   const int i0 = (split * kAttnWaves + wid) * PPW;
   int jr[PPW];
   int64_t pp[PPW];
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi) {
     const int i = i0 + pi;
-    jr[pi] = sel ? (i < list_len ? sel[(int64_t)unit * list_len + i] : -1)
-                 : (i < max_pages ? i : -1);
+    if (sel) {
+      const int e = sel[(int64_t)unit * list_len + min(i, list_len - 1)];
+      jr[pi] = i < list_len ? e : -1;
+    } else {
+      jr[pi] = i < max_pages ? i : -1;
+    }
   }
 #pragma unroll
-  for (int pi = 0; pi < PPW; ++pi)
-    pp[pi] = (jr[pi] >= 0 && jr[pi] < max_pages)
-                 ? page_table[(int64_t)b * max_pages + jr[pi]] : -1;
+  for (int pi = 0; pi < PPW; ++pi) {
+    const bool in_row = jr[pi] >= 0 && jr[pi] < max_pages;
+    const int64_t e = page_table[(int64_t)b * max_pages + (in_row ? jr[pi] : 0)];
+    pp[pi] = in_row ? e : -1;
+  }
   const int L = seq_lens[b];
   constexpr int S = SUB * kTileRows;
   const int n = pages_of(L, S, max_pages);
@@ -61,18 +70,26 @@ attn_split_kernel(const uint16_t* __restrict__ q,
   auto tile_valid = [&](int pi, int s) {
     return pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
   };
+  // The tile loads sit in one branch that depends on every page's table
+  // entry, so all of them are in before the first tile load and no wait
+  // separates the pages' loads.
+  bool any = false;
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi) any |= pj[pi] >= 0;
   uint4 kx[PPW][SUB][4], vx[PPW][SUB][4];
   if constexpr (G >= 2) {
     // a query group: both products on the matrix cores (dev_attn_mfma.h)
     uint4 qb[4];
     mfma_load_q<G>(q, (int64_t)unit * G, lane, qb);
+    if (any) {
 #pragma unroll
-    for (int pi = 0; pi < PPW; ++pi)
+      for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
-      for (int s = 0; s < SUB; ++s)
-        if (tile_valid(pi, s) > 0)
-          mfma_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), lane,
-                         kx[pi][s], vx[pi][s]);
+        for (int s = 0; s < SUB; ++s)
+          if (tile_valid(pi, s) > 0)
+            mfma_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), lane,
+                           kx[pi][s], vx[pi][s]);
+    }
     MfmaAttnState st;
     mfma_attn_init(st);
 #pragma unroll
@@ -86,13 +103,15 @@ attn_split_kernel(const uint16_t* __restrict__ q,
   } else {
     AttnQ<G> qf;
     attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
+    if (any) {
 #pragma unroll
-    for (int pi = 0; pi < PPW; ++pi)
+      for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
-      for (int s = 0; s < SUB; ++s)
-        if (tile_valid(pi, s) > 0)
-          attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
-                         kx[pi][s], vx[pi][s]);
+        for (int s = 0; s < SUB; ++s)
+          if (tile_valid(pi, s) > 0)
+            attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
+                           kx[pi][s], vx[pi][s]);
+    }
     AttnState<G> st;
     attn_init(st);
 #pragma unroll

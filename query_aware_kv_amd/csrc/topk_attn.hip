@@ -78,25 +78,37 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
   int64_t pp[PPW];
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi) {
+    // unconditional table loads (an empty slot reads entry 0 of the row and
+    // ignores it), so that a wave's loads go out back to back
     const int i = wid * PPW + pi;
     const int j = s0 + i < k ? kept[i] : -1;
-    pp[pi] = (j >= 0 && j < n) ? page_table[(int64_t)b * max_pages + j] : -1;
+    const bool in_row = j >= 0 && j < n;
+    const int64_t e = page_table[(int64_t)b * max_pages + (in_row ? j : 0)];
+    pp[pi] = in_row ? e : -1;
     pj[pi] = (pp[pi] >= 0 && pp[pi] < num_pool_pages) ? j : -1;
   }
   // valid tokens of tile s of page pi (<= 0: absent); uniform over the wave
   auto tile_valid = [&](int pi, int s) {
     return pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
   };
+  // The tile loads sit in one branch that depends on every page's table
+  // entry, so all of them are in before the first tile load and no wait
+  // separates the pages' loads.
+  bool any = false;
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi) any |= pj[pi] >= 0;
   uint4 kx[PPW][SUB][4], vx[PPW][SUB][4];
   if constexpr (G >= 2) {
     // a query group: both products on the matrix cores (dev_attn_mfma.h)
+    if (any) {
 #pragma unroll
-    for (int pi = 0; pi < PPW; ++pi)
+      for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
-      for (int s = 0; s < SUB; ++s)
-        if (tile_valid(pi, s) > 0)
-          mfma_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), lane,
-                         kx[pi][s], vx[pi][s]);
+        for (int s = 0; s < SUB; ++s)
+          if (tile_valid(pi, s) > 0)
+            mfma_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), lane,
+                           kx[pi][s], vx[pi][s]);
+    }
     MfmaAttnState st;
     mfma_attn_init(st);
 #pragma unroll
@@ -109,13 +121,15 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
     __syncthreads();  // the Top-K scratch becomes the attention scratch
     mfma_attn_stage_wave(st, sm.attn, wid, lane);
   } else {
+    if (any) {
 #pragma unroll
-    for (int pi = 0; pi < PPW; ++pi)
+      for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
-      for (int s = 0; s < SUB; ++s)
-        if (tile_valid(pi, s) > 0)
-          attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
-                         kx[pi][s], vx[pi][s]);
+        for (int s = 0; s < SUB; ++s)
+          if (tile_valid(pi, s) > 0)
+            attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
+                           kx[pi][s], vx[pi][s]);
+    }
     AttnState<G> st;
     attn_init(st);
 #pragma unroll
