@@ -213,27 +213,19 @@ struct MergeSmem {
   float m[kHeadDim], num[kHeadDim], den[kHeadDim];
 };
 
-// Merge nsplit partials of one (request, query head) into out_row[128] with
-// a 256-thread workgroup: partial s is (o[s*128 .. +128], ml[2s] = M,
-// ml[2s+1] = den).  Thread (half, ch) folds channel ch of the splits of its
-// parity with a running max (online softmax), 16 splits per chunk whose
-// loads are all issued together -- one memory round trip per chunk, so one
-// in all for up to 32 splits; the two halves then meet in LDS.
-__device__ __forceinline__ void merge_splits(const float* __restrict__ o,
-                                             const float* __restrict__ ml,
-                                             int nsplit, float* __restrict__ out_row,
-                                             MergeSmem& sm) {
-  constexpr int kChunk = 16;
-  const int tid = threadIdx.x;
-  const int ch = tid & (kHeadDim - 1), half = tid >> 7;
-  float mr = -INFINITY, num = 0.f, den = 0.f;
-  for (int s0 = half; s0 < nsplit; s0 += 2 * kChunk) {
-    // Every load is issued, from a split index clamped into range, so the
-    // chunk's loads go out back to back; splits past the end are masked
-    // afterwards.
-    float w[kChunk], l[kChunk], x[kChunk];
+// Fold the splits s = half, half + 2, ... of channel ch into a running
+// (max, num, den), CHUNK splits per memory round trip.  Every load of a
+// chunk is issued, from a split index clamped into range, so they go out
+// back to back; splits past the end are masked afterwards.
+template <int CHUNK>
+__device__ __forceinline__ void merge_half(const float* __restrict__ o,
+                                           const float* __restrict__ ml, int nsplit,
+                                           int half, int ch, float& mr, float& num,
+                                           float& den) {
+  for (int s0 = half; s0 < nsplit; s0 += 2 * CHUNK) {
+    float w[CHUNK], l[CHUNK], x[CHUNK];
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
+    for (int u = 0; u < CHUNK; ++u) {
       const int sc = min(s0 + 2 * u, nsplit - 1);
       const float2 m_l = *reinterpret_cast<const float2*>(ml + 2 * sc);
       w[u] = m_l.x;
@@ -241,7 +233,7 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ o,
       x[u] = o[(int64_t)sc * kHeadDim + ch];
     }
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
+    for (int u = 0; u < CHUNK; ++u) {
       if (s0 + 2 * u >= nsplit) {
         w[u] = -INFINITY;
         l[u] = 0.f;
@@ -250,18 +242,39 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ o,
     }
     float mc = mr;
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) mc = fmaxf(mc, w[u]);
+    for (int u = 0; u < CHUNK; ++u) mc = fmaxf(mc, w[u]);
     const float sc = exp2_or_zero(mr, mc);
     num *= sc;
     den *= sc;
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
+    for (int u = 0; u < CHUNK; ++u) {
       const float e = exp2_or_zero(w[u], mc);
       num += x[u] * e;
       den += l[u] * e;
     }
     mr = mc;
   }
+}
+
+// Merge nsplit partials of one (request, query head) into out_row[128] with
+// a 256-thread workgroup: partial s is (o[s*128 .. +128], ml[2s] = M,
+// ml[2s+1] = den).  Thread (half, ch) folds channel ch of the splits of its
+// parity with a running max (online softmax); the chunk matches the split
+// count (4, 8 or 16 splits per half), so up to 32 splits take one memory
+// round trip without loads to spare; the two halves then meet in LDS.
+__device__ __forceinline__ void merge_splits(const float* __restrict__ o,
+                                             const float* __restrict__ ml,
+                                             int nsplit, float* __restrict__ out_row,
+                                             MergeSmem& sm) {
+  const int tid = threadIdx.x;
+  const int ch = tid & (kHeadDim - 1), half = tid >> 7;
+  float mr = -INFINITY, num = 0.f, den = 0.f;
+  if (nsplit <= 8)
+    merge_half<4>(o, ml, nsplit, half, ch, mr, num, den);
+  else if (nsplit <= 16)
+    merge_half<8>(o, ml, nsplit, half, ch, mr, num, den);
+  else
+    merge_half<16>(o, ml, nsplit, half, ch, mr, num, den);
   if (half == 1) {
     sm.m[ch] = mr;
     sm.num[ch] = num;
