@@ -53,6 +53,19 @@ estimate_kernel(const uint16_t* __restrict__ q,
   EstQ<G> qq;
   est_load_q<G>(q, ((int64_t)b * Hkv + g) * G, c, qq);
   const int n = pages_of(L, page_size, max_pages);
+  // APPEND: the appended token's page, and the token itself, loaded up
+  // front by the row that scores that page's block
+  int jl = -1;
+  uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
+  if constexpr (APPEND) {
+    jl = L > 0 ? (L - 1) / page_size : -1;
+    const int jbl = jl >= 0 ? jl / kEstPages : -1;
+    if (jbl >= jb0 && (jbl - jb0) % rows_per_head == 0) {
+      const int64_t src = ((int64_t)b * Hkv + g) * kHeadDim + c * 8;
+      kn = *reinterpret_cast<const uint4*>(ap.k_new + src);
+      vn = *reinterpret_cast<const uint4*>(ap.v_new + src);
+    }
+  }
 
   for (int jb = jb0; jb * kEstPages < max_pages; jb += rows_per_head) {
     int pid[kEstPages];
@@ -60,19 +73,14 @@ estimate_kernel(const uint16_t* __restrict__ q,
     uint4 lo[kEstPages], hi[kEstPages];
     est_load_meta(kmin, kmax, pid, Hkv, g, c, lo, hi);
     if constexpr (APPEND) {
-      const int jl = L > 0 ? (L - 1) / page_size : -1;  // the appended token's page
-      const int u = jl - jb * kEstPages;
+      const int u = jl - jb * kEstPages;  // the appended token's page in the block
       if (u >= 0 && u < kEstPages) {
         int64_t p = -1;
 #pragma unroll
         for (int w = 0; w < kEstPages; ++w) if (w == u) p = pid[w];
-        if (p >= 0) {  // a pool page below n: L - 1 < n * page_size
-          const int64_t src = ((int64_t)b * Hkv + g) * kHeadDim + c * 8;
-          const uint4 kn = *reinterpret_cast<const uint4*>(ap.k_new + src);
-          const uint4 vn = *reinterpret_cast<const uint4*>(ap.v_new + src);
+        if (p >= 0)  // a pool page below n: L - 1 < n * page_size
           est_append(u, (L - 1) - jl * page_size, p, Hkv, g, c, page_size, kn, vn,
                      ap.k_pool, ap.v_pool, kmin, kmax, lo, hi);
-        }
       }
     }
     est_table(pt_row, max_pages, (jb + rows_per_head) * kEstPages, ent);  // prefetch
