@@ -23,23 +23,6 @@ enum class DType : int { F16 = 0, BF16 = 1 };
 
 // ---------------------------------------------------------------- storage
 
-// Eight 16-bit values (one 16-byte load) widened to float32.  Both widenings
-// are exact.
-template <DType T>
-__device__ __forceinline__ void widen8(const uint4& v, float (&f)[8]) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (T == DType::F16) {
-      f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
-      f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
-    } else {
-      f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-      f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
-    }
-  }
-}
-
 // One 16-bit value of a packed word (half 0 = bits 0..15) widened to
 // float32; for fp16 the conversion folds into v_fma_mix_f32 when the result
 // feeds a multiply-add.
