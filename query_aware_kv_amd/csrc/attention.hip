@@ -171,14 +171,23 @@ using Plan = AttnPlan;
 }  // namespace
 
 // Pages per wave: as many as the registers allow while the grid keeps at
-// least ~4096 waves (16 per CU) to spread the loads over all 256 CUs.  With
-// more waves per workgroup than kAttnWaves the split count can only shrink,
-// so quest_workspace_size (planned for kAttnWaves) covers every plan.
+// least ~4096 waves (16 per CU) to spread the loads over all 256 CUs.  The
+// 8-wave Top-K + attention workgroups repeat the row's selection each, so
+// fewer, fuller ones pay there: at least 256 of them (2048 waves), with at
+// most 2 pages per wave (4 made the kernel slower through its registers).
+// Measured on the 32-head layers: 8 splits of 2 pages per wave beat 16 of
+// one at budgets up to 2048 tokens.  The 8-wave split count never exceeds
+// the 4-wave one (PPW 4 for 4 waves needs units * ceil(L/16) >= 1024, which
+// gives 8 waves PPW 2 and the same count; PPW 2 for 4 waves gives 8 waves
+// PPW 2 and half the count), so quest_workspace_size, planned for
+// kAttnWaves, covers every plan.
 AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves) {
   const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
-  const int64_t min_wgs = 4096 / waves;
+  const bool topk_wg = waves == 8;
+  const int64_t min_wgs = topk_wg ? 256 : 4096 / waves;
+  const int cap = topk_wg ? 2 : max_ppw(kv.page_size / kTileRows);
   int ppw = 1;
-  for (int cand = max_ppw(kv.page_size / kTileRows); cand > 1; cand /= 2) {
+  for (int cand = min(cap, max_ppw(kv.page_size / kTileRows)); cand > 1; cand /= 2) {
     const int64_t ns = (list_len + waves * cand - 1) / (waves * cand);
     if (units * ns >= min_wgs) { ppw = cand; break; }
   }

@@ -215,6 +215,9 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
                                  void* workspace, hipStream_t stream) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
   const AttnPlan pl = attention_plan(kv, k_pages, kTaWaves);
+  // the caller's workspace holds the partials of the 4-wave plan, which
+  // never has fewer splits (see attention_plan); refuse rather than overrun
+  if (pl.nsplit > attention_plan(kv, k_pages).nsplit) return hipErrorInvalidValue;
   const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = ws_o ? ws_o + attention_ml_offset(slots) : nullptr;
