@@ -39,7 +39,14 @@ hipError_t launch_topk(const quest_paged_kv& kv, const float* scores,
                        const int32_t* seq_lens, int k_pages, int n_sink,
                        int n_local, int32_t* sel, hipStream_t stream) {
   const int mp = kv.max_pages_per_seq;
+  // Up to 2048 pages: with few rows the selection's latency is the cost,
+  // and 8 waves of 4 keys finish sooner than 4 waves of 8 (32 rows of 2048
+  // pages: 5.0 vs 5.7 us); with many rows the workgroups share the CUs, and
+  // the smaller ones go through faster (1024 rows: 16.9 vs 18.7 us).
+  const bool few_rows = (int64_t)kv.batch * kv.num_kv_heads <= 256;
   if (mp <= 1024)       launch_t<256, 4>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
+  else if (mp <= 2048 && few_rows)
+                        launch_t<512, 4>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
   else if (mp <= 2048)  launch_t<256, 8>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
   else if (mp <= 4096)  launch_t<512, 8>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
   else if (mp <= 8192)  launch_t<1024, 8>(kv, scores, seq_lens, k_pages, n_sink, n_local, sel, stream);
