@@ -6,29 +6,40 @@
 // index; the kept pages are written in ascending order, -1 padded.
 //
 // Scores become order-preserving uint32 keys (-0 folded onto +0 first, so
-// equal numbers get equal keys), KPT consecutive pages per thread, kept in
-// VGPRs.  The block's min and max key fix how many leading bits all keys
+// equal numbers get equal keys), kept in VGPRs: KPT per thread, in segments
+// of 4 consecutive pages -- thread t holds pages 4t..4t+3 of each stretch of
+// 4*BLOCK pages -- so that a row just longer than 4*BLOCK pages still spreads
+// over every wave.  The block's min and max key fix how many leading bits all keys
 // share; an MSB-first radix select then walks 8-bit digits of (key - min)
 // from the highest differing bit, with histograms in LDS (double-buffered,
 // so one barrier pair per pass), and stops as soon as the bin holding the
 // k-th largest key is taken whole -- usually after one or two passes.  One
 // block-wide exclusive scan of packed per-thread counts (above-threshold,
-// at-threshold) then gives every kept page its output slot: pages are
-// visited in index order, so the lowest-index ties are the ones kept and the
-// output is ascending without a sort.
+// at-threshold) per segment then gives every kept page its output slot:
+// pages are visited in index order, so the lowest-index ties are the ones
+// kept and the output is ascending without a sort.
 #pragma once
 
 #include "common.h"
 
 namespace quest {
 
+constexpr int kTopkSeg = 4;      // consecutive pages per segment
+constexpr int kTopkMaxSegs = 8;  // segments per thread (KPT <= 32)
+
 template <int BLOCK>
 struct TopkSmem {
   uint32_t hist[2][256];
-  uint32_t red[2][BLOCK / kWave];   // block min / max of the keys
-  uint32_t scan[BLOCK / kWave];     // per-wave totals of the final scan
+  uint32_t red[2][BLOCK / kWave];                 // block min / max of the keys
+  uint32_t scan[kTopkMaxSegs][BLOCK / kWave];     // per-wave totals of the final scan
   uint32_t prefix, need, count;
 };
+
+// Page of this thread's key i: segment i / SEG, position i % SEG.
+template <int BLOCK, int SEG>
+__device__ __forceinline__ int topk_page(int i) {
+  return (i / SEG) * (BLOCK * SEG) + (int)threadIdx.x * SEG + i % SEG;
+}
 
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -51,39 +62,49 @@ __device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t x) {
   return op(op(r0, r1), op(r2, r3));
 }
 
-// Load a thread's KPT consecutive scores; entries below `limit` are in
-// bounds (limit = the row's length in the buffer), so callers can issue this
-// before they know n.  A 16-byte-aligned row is read with 16-byte loads (KPT
-// is a multiple of 4): KPT/4 load instructions per thread instead of KPT.
-template <int BLOCK, int KPT>
+// Load a thread's KPT scores (topk_page order); entries below `limit` are
+// in bounds (limit = the row's length in the buffer), so callers can issue
+// this before they know n.  Every load is issued, from an index clamped into
+// the row, so they go out back to back; entries past `limit` hold anything
+// and are never used (they are not pages of the row).  A 16-byte-aligned
+// row whose length is a multiple of 4 is read with 16-byte loads.
+template <int BLOCK, int KPT, int SEG = kTopkSeg>
 __device__ __forceinline__ void topk_load(const float* __restrict__ s, int limit,
                                           float (&v)[KPT]) {
-  static_assert(KPT % 4 == 0, "16-byte pieces");
-  const int base = threadIdx.x * KPT;
-  const bool vec = (reinterpret_cast<uintptr_t>(s) & 15u) == 0;  // row-uniform
-  if (vec && base + KPT <= limit) {
+  static_assert(SEG % 4 == 0 && KPT % SEG == 0 && KPT / SEG <= kTopkMaxSegs,
+                "whole 16-byte pieces and segments");
+  const bool vec = (reinterpret_cast<uintptr_t>(s) & 15u) == 0 && (limit & 3) == 0 &&
+                   limit >= 4;
+  if (vec) {  // row-uniform
 #pragma unroll
     for (int i = 0; i < KPT; i += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(s + base + i);
+      const int b = min(topk_page<BLOCK, SEG>(i), limit - 4);  // each piece wholly in or out
+      const float4 x = *reinterpret_cast<const float4*>(s + b);
       v[i] = x.x;
       v[i + 1] = x.y;
       v[i + 2] = x.z;
       v[i + 3] = x.w;
     }
-  } else {
+  } else if (limit > 0) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) v[i] = base + i < limit ? s[base + i] : 0.f;
+    for (int i = 0; i < KPT; ++i) v[i] = s[min(topk_page<BLOCK, SEG>(i), limit - 1)];
+  } else {  // an empty row: nothing to read
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) v[i] = 0.f;
   }
 }
 
 // The page-table entries of the same KPT pages, so that the kept pages' pool
 // ids come out of the selection with no dependent load after it.
-template <int BLOCK, int KPT>
+template <int BLOCK, int KPT, int SEG = kTopkSeg>
 __device__ __forceinline__ void topk_load_table(const int32_t* __restrict__ pt_row,
                                                 int limit, int32_t (&e)[KPT]) {
-  const int base = threadIdx.x * KPT;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) e[i] = base + i < limit ? pt_row[base + i] : -1;
+  for (int i = 0; i < KPT; ++i) {
+    const int p = topk_page<BLOCK, SEG>(i);
+    const int32_t x = limit > 0 ? pt_row[min(p, limit - 1)] : -1;
+    e[i] = p < limit ? x : -1;
+  }
 }
 
 // Select for one row.  The whole block (BLOCK threads) must call it.
@@ -101,7 +122,7 @@ __device__ __forceinline__ void topk_load_table(const int32_t* __restrict__ pt_r
 // Forced pages take no part in the radix select: it picks k - n_sink -
 // n_local among the others, and the placement scan counts forced pages as
 // kept, so the list stays ascending.
-template <int BLOCK, int KPT>
+template <int BLOCK, int KPT, int SEG = kTopkSeg>
 __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
                          int n_sink, int n_local,
                          int32_t* __restrict__ out,
@@ -120,7 +141,7 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
     if (phys) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
-        const int p = tid * KPT + i;
+        const int p = topk_page<BLOCK, SEG>(i);
         if (p < n && p >= w_lo && p < w_hi) phys[p - w_lo] = (*ent)[i];
       }
     }
@@ -128,14 +149,13 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
   }
   // n > k >= n_sink + n_local: the forced ranges are disjoint and at least
   // one page competes.
-  const int base = tid * KPT;
   const int local0 = n - n_local;
   uint32_t key[KPT];
   bool forced[KPT], cand[KPT];
   uint32_t kmn = 0xffffffffu, kmx = 0u;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const int p = base + i;
+    const int p = topk_page<BLOCK, SEG>(i);
     forced[i] = p < n && (p < n_sink || p >= local0);
     cand[i] = p < n && !forced[i];
     key[i] = cand[i] ? score_key(v[i]) : 0u;
@@ -210,39 +230,54 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
   }
   // Kept: forced pages, competing keys whose decided bits exceed the
   // threshold's, and the first `need` (in page order) whose decided bits
-  // equal them.  "gt" counts the first two kinds.
+  // equal them.  "gt" counts the first two kinds.  Pages are ordered by
+  // segment, then thread, then position: one packed count per segment.
+  constexpr int NSEG = KPT / SEG;
   const uint32_t thr = shift >= 32 ? 0u : (prefix >> shift);
-  uint32_t gt = 0, eq = 0;
+  uint32_t packed[NSEG], incl[NSEG];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const uint32_t v = key[i] >> shift;
-    gt += forced[i] || (pick && cand[i] && v > thr);
-    eq += pick && cand[i] && v == thr;
-  }
-  const uint32_t packed = (gt << 16) | eq;  // both < 65536 (n <= 65535)
-  const uint32_t incl = wave_scan_incl(packed);
-  if (lane == kWave - 1) sm.scan[wid] = incl;
-  __syncthreads();
-  uint32_t before = incl - packed;
+  for (int sg = 0; sg < NSEG; ++sg) {
+    uint32_t gt = 0, eq = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w)
-    if (w < wid) before += sm.scan[w];
-  uint32_t gt_before = before >> 16, eq_before = before & 0xffffu;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    if (base + i >= n) break;
-    const uint32_t v = key[i] >> shift;
-    uint32_t slot = 0xffffffffu;
-    if (forced[i] || (pick && cand[i] && v > thr)) {
-      slot = gt_before + min(eq_before, need);
-      ++gt_before;
-    } else if (pick && cand[i] && v == thr) {
-      if (eq_before < need) slot = gt_before + eq_before;
-      ++eq_before;
+    for (int e = 0; e < SEG; ++e) {
+      const int i = sg * SEG + e;
+      const uint32_t v = key[i] >> shift;
+      gt += forced[i] || (pick && cand[i] && v > thr);
+      eq += pick && cand[i] && v == thr;
     }
-    if (slot - (uint32_t)w_lo < (uint32_t)(w_hi - w_lo)) {  // kept, in the window
-      out[slot - w_lo] = base + i;
-      if (phys) phys[slot - w_lo] = (*ent)[i];
+    packed[sg] = (gt << 16) | eq;  // both < 65536 (n <= 65535)
+    incl[sg] = wave_scan_incl(packed[sg]);
+    if (lane == kWave - 1) sm.scan[sg][wid] = incl[sg];
+  }
+  __syncthreads();
+  uint32_t seg_base = 0;  // packed totals of the earlier segments
+#pragma unroll
+  for (int sg = 0; sg < NSEG; ++sg) {
+    uint32_t before = incl[sg] - packed[sg] + seg_base;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wid) before += sm.scan[sg][w];
+      seg_base += sm.scan[sg][w];
+    }
+    uint32_t gt_before = before >> 16, eq_before = before & 0xffffu;
+#pragma unroll
+    for (int e = 0; e < SEG; ++e) {
+      const int i = sg * SEG + e;
+      const int page = topk_page<BLOCK, SEG>(i);
+      if (page >= n) continue;
+      const uint32_t v = key[i] >> shift;
+      uint32_t slot = 0xffffffffu;
+      if (forced[i] || (pick && cand[i] && v > thr)) {
+        slot = gt_before + min(eq_before, need);
+        ++gt_before;
+      } else if (pick && cand[i] && v == thr) {
+        if (eq_before < need) slot = gt_before + eq_before;
+        ++eq_before;
+      }
+      if (slot - (uint32_t)w_lo < (uint32_t)(w_hi - w_lo)) {  // kept, in the window
+        out[slot - w_lo] = page;
+        if (phys) phys[slot - w_lo] = (*ent)[i];
+      }
     }
   }
 }

@@ -7,7 +7,8 @@
 namespace quest {
 namespace {
 
-template <int BLOCK, int KPT>
+// SEG: consecutive pages per thread and segment (dev_topk.h).
+template <int BLOCK, int KPT, int SEG>
 __global__ void __launch_bounds__(BLOCK)
 topk_kernel(const float* __restrict__ scores,
             const int32_t* __restrict__ seq_lens, int Hkv, int max_pages,
@@ -17,18 +18,21 @@ topk_kernel(const float* __restrict__ scores,
   const int rowid = blockIdx.x;  // b * Hkv + g
   const int b = rowid / Hkv;
   float v[KPT];  // issued together with the length load
-  topk_load<BLOCK, KPT>(scores + (int64_t)rowid * max_pages, max_pages, v);
+  topk_load<BLOCK, KPT, SEG>(scores + (int64_t)rowid * max_pages, max_pages, v);
   const int L = seq_lens[b];
   const int n = pages_of(L, page_size, max_pages);
-  topk_row<BLOCK, KPT>(v, n, k, n_sink, n_local, sel + (int64_t)rowid * k, nullptr,
+  topk_row<BLOCK, KPT, SEG>(v, n, k, n_sink, n_local, sel + (int64_t)rowid * k, nullptr,
                        nullptr, sm);
 }
 
+// 256-thread launches serve many rows: one run of KPT pages per thread;
+// the wider ones serve few rows: segments of 4.
 template <int BLOCK, int KPT>
 void launch_t(const quest_paged_kv& kv, const float* scores,
               const int32_t* seq_lens, int k, int n_sink, int n_local,
               int32_t* sel, hipStream_t stream) {
-  topk_kernel<BLOCK, KPT><<<kv.batch * kv.num_kv_heads, BLOCK, 0, stream>>>(
+  constexpr int SEG = BLOCK <= 256 ? KPT : kTopkSeg;
+  topk_kernel<BLOCK, KPT, SEG><<<kv.batch * kv.num_kv_heads, BLOCK, 0, stream>>>(
       scores, seq_lens, kv.num_kv_heads, kv.max_pages_per_seq, k, n_sink, n_local,
       kv.page_size, sel);
 }
