@@ -380,3 +380,59 @@ def test_graph_replay_matches_eager(select):
         assert torch.equal(step.sel, ref.sel), i
         assert torch.equal(step.out.view(torch.int32), ref.out.view(torch.int32)), i
         assert torch.equal(step.scores.view(torch.int32), ref.scores.view(torch.int32)), i
+
+
+@pytest.mark.parametrize("mp,rows", [(2056, 12), (2056, 300), (4104, 12), (1027, 300),
+                                     (2048, 300)])
+def test_topk_segment_boundaries(mp, rows):
+    """Rows whose length crosses the 4-page segments of the selection's key
+    layout (1024, 2048 and 4096 pages and just past them), with few rows
+    (the 8-wave launch, keys in segments of 4) and many (the 4-wave one,
+    keys in runs): bit-exact against the oracle, every score kind."""
+    k = 128
+    g = np.random.default_rng(mp * 7 + rows)
+    edges = [n for n in (1023, 1024, 1025, 1028, 2047, 2048, 2049, 2052, 2056, 4095,
+                         4096, 4097, 4100, 4104) if n <= mp]
+    n_list = (edges * (rows // len(edges) + 1))[:rows]
+    n_list[-1] = int(g.integers(1, mp + 1))
+    C.say(f"[case] topk segments mp={mp} rows={rows}")
+    s = _topk_case(rows, n_list, mp, k, seed=mp + rows)
+    lens = torch.tensor([n * 16 for n in n_list], dtype=torch.int32)
+    kv = qa.paged_kv(rows, 1, 1, 1, mp, torch.float16)
+    sel = torch.full((rows, 1, k), -7, dtype=torch.int32, device="cuda")
+    qa.quest_topk_pages(kv, torch.from_numpy(s).cuda(), lens.cuda(), k, sel)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    for r in range(rows):
+        ref = O.topk_pages(s[r, 0].astype(np.float64), n_list[r], k)
+        assert np.array_equal(got[r, 0], ref), f"row {r} n={n_list[r]}"
+
+
+@pytest.mark.parametrize("mp", [2056, 4104])
+def test_topk_attn_selection_segment_boundaries(mp):
+    """The selection inside the attention launch (quest_topk_sparse_decode_attn,
+    keys in segments of 4) at lengths around the segment boundaries: its
+    sel_pages output bit-exact against the oracle."""
+    rows, k = 10, 128
+    edges = [n for n in (2047, 2048, 2049, 2052, 2056, 4096, 4097, 4104, 1, 129)
+             if n <= mp]
+    n_list = (edges * 2)[:rows]
+    C.say(f"[case] topk_attn segments mp={mp} n={n_list}")
+    s = _topk_case(rows, n_list, mp, k, seed=mp + 11)
+    s = np.nan_to_num(s, nan=0.0)  # the fused call reads its own rows only up to n
+    kv = qa.paged_kv(rows, 1, 1, mp, mp, torch.float16)
+    lens = torch.tensor([n * 16 for n in n_list], dtype=torch.int32, device="cuda")
+    pt = torch.arange(mp, dtype=torch.int32, device="cuda").repeat(rows, 1).contiguous()
+    q = torch.randn(rows, 1, 128, device="cuda").half()
+    kp = torch.randn(mp, 1, 16, 128, device="cuda").half()
+    vp = torch.randn(mp, 1, 16, 128, device="cuda").half()
+    out = torch.empty(rows, 1, 128, device="cuda")
+    sel = torch.full((rows, 1, k), -7, dtype=torch.int32, device="cuda")
+    ws = qa.alloc_workspace(kv, k)
+    qa.quest_topk_sparse_decode_attn(kv, q, kp, vp, pt, lens, torch.from_numpy(s).cuda(),
+                                     k, SM, sel, out, ws)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    for r in range(rows):
+        ref = O.topk_pages(s[r, 0].astype(np.float64), n_list[r], k)
+        assert np.array_equal(got[r, 0], ref), f"row {r} n={n_list[r]}"
