@@ -7,9 +7,12 @@
 //
 // Scores become order-preserving uint32 keys (-0 folded onto +0 first, so
 // equal numbers get equal keys), kept in VGPRs: KPT per thread, in segments
-// of 4 consecutive pages -- thread t holds pages 4t..4t+3 of each stretch of
-// 4*BLOCK pages -- so that a row just longer than 4*BLOCK pages still spreads
-// over every wave.  The block's min and max key fix how many leading bits all keys
+// of SEG consecutive pages -- thread t holds pages SEG*t .. SEG*t+SEG-1 of
+// each stretch of SEG*BLOCK pages.  SEG = 4 (the default) spreads a row just
+// longer than 4*BLOCK pages over every wave, which the latency-bound
+// launches want; SEG = KPT (one run per thread) needs one placement scan
+// instead of KPT/4, which the many-row launches that share the CUs want.
+// The block's min and max key fix how many leading bits all keys
 // share; an MSB-first radix select then walks 8-bit digits of (key - min)
 // from the highest differing bit, with histograms in LDS (double-buffered,
 // so one barrier pair per pass), and stops as soon as the bin holding the
@@ -24,7 +27,7 @@
 
 namespace quest {
 
-constexpr int kTopkSeg = 4;      // consecutive pages per segment
+constexpr int kTopkSeg = 4;      // consecutive pages per segment (default)
 constexpr int kTopkMaxSegs = 8;  // segments per thread (KPT <= 32)
 
 template <int BLOCK>
@@ -108,7 +111,8 @@ __device__ __forceinline__ void topk_load_table(const int32_t* __restrict__ pt_r
 }
 
 // Select for one row.  The whole block (BLOCK threads) must call it.
-//   v    : this thread's scores from topk_load (the row has n <= BLOCK*KPT)
+//   v    : this thread's scores from topk_load with the same SEG (the row
+//          has n <= BLOCK*KPT)
 //   n_sink, n_local : when n > k, pages j < n_sink and j >= n - n_local are
 //          kept whatever their scores ("Guide to Quest" §3: attention sinks
 //          and the local window) and the other k - n_sink - n_local slots
