@@ -1,10 +1,12 @@
 """Quest decode-step hot path for AMD Instinct MI355X (gfx950).
 
 The computation lives in libquest.so (hand-written HIP kernels behind a C
-ABI, declared in include/quest.h).  This package is its Python binding: the
-five entry points under the C names, plus `SparseDecodeStep`, which strings
-estimate -> Top-K -> sparse attention together on preallocated buffers.
-PyTorch only provides device memory and the stream.
+ABI, declared in include/quest.h).  This package is its Python binding:
+every entry point under its C name, plus the step compositions on
+preallocated buffers -- `SparseDecodeStep` (estimate -> Top-K -> sparse
+attention, optionally appending the step's token first), `UnionDecodeStep`
+(per-head Top-K and the group's union) and `DenseDecode`.  PyTorch only
+provides device memory and the stream.
 """
 from __future__ import annotations
 
