@@ -255,3 +255,34 @@ def test_append_estimate_validation():
         assert qa.LIB.quest_append_estimate(ctypes.byref(k), *bad, None) == \
             _abi.QUEST_ERR_INVALID_ARGUMENT
         assert name in qa.LIB.quest_last_error().decode()
+
+
+def test_last_error_is_per_thread():
+    """Each host thread reads the message of its own last failed call."""
+    import threading
+    k = kv()
+    P = ctypes.c_void_p
+    step = threading.Barrier(2)
+    seen = {}
+
+    def a():
+        assert qa.LIB.quest_topk_pages(ctypes.byref(k), P(FAKE), P(FAKE), 0,
+                                       P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+        step.wait()
+        step.wait()  # b has failed in between
+        seen["a"] = qa.LIB.quest_last_error().decode()
+
+    def b():
+        step.wait()
+        assert qa.LIB.quest_topk_pages_ex(ctypes.byref(k), P(FAKE), P(FAKE), 8, -1, 0,
+                                          P(FAKE), None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+        step.wait()
+        seen["b"] = qa.LIB.quest_last_error().decode()
+
+    ts = [threading.Thread(target=f) for f in (a, b)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=30)
+    assert seen["a"].startswith("quest_topk_pages:") and "k_pages" in seen["a"]
+    assert seen["b"].startswith("quest_topk_pages_ex:") and "n_sink" in seen["b"]
