@@ -955,9 +955,9 @@ def main():
         print(json.dumps({"copy_probe_bytes": args.copy_probe << 20}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
-              "path (the decode step shards over (request, kv-head) units "
-              "with no exchange; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU "
+              "path (the decode step would shard over (request, kv-head) "
+              "units with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -63,7 +63,7 @@ extern "C" {
 typedef enum quest_status {
   QUEST_OK = 0,
   QUEST_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, bad count */
-  QUEST_ERR_UNSUPPORTED = 2,      /* shape or dtype this build has no kernel for */
+  QUEST_ERR_UNSUPPORTED = 2,      /* shape or dtype the library has no kernel for */
   QUEST_ERR_WORKSPACE_TOO_SMALL = 3,
   QUEST_ERR_HIP = 4               /* the HIP runtime reported an error */
 } quest_status;
@@ -278,7 +278,7 @@ QUEST_API quest_status quest_decode_attn(
  * estimate is complete, overlapping the estimate and attention of other rows.
  * Requires max_pages_per_seq <= 8192 (QUEST_ERR_UNSUPPORTED otherwise).
  *
- * STATUS: switched off in this build -- every call returns
+ * STATUS: switched off -- every call returns
  * QUEST_ERR_UNSUPPORTED before launching anything (its kernel did not
  * complete on gfx950 and the cause is not yet found).  Use the three
  * separate calls.

@@ -398,7 +398,7 @@ QUEST_API quest_status quest_sparse_decode_step(
   if (s != QUEST_OK) return s;
   if (!kFusedStepEnabled)
     return fail(QUEST_ERR_UNSUPPORTED,
-                "%s: the one-launch step is switched off in this build (its "
+                "%s: the one-launch step is switched off (its "
                 "kernel did not complete on gfx950; cause not yet found) -- "
                 "use quest_estimate + quest_topk_pages + "
                 "quest_sparse_decode_attn", fn);

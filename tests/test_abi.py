@@ -170,7 +170,7 @@ def test_python_binding_rejects_host_tensors():
 
 
 def test_fused_step_is_switched_off():
-    """The one-launch step refuses work before any launch in this build."""
+    """The one-launch step is switched off: it refuses work before any launch."""
     k = kv()
     P = ctypes.c_void_p
     st = qa.LIB.quest_sparse_decode_step(
