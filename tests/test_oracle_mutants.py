@@ -206,6 +206,101 @@ def dense_off_by_one_token(q, kp, vp, pt, lens, scale, S):
                              * (np.asarray(lens) > 0), scale, S)
 
 
+def sparse_no_max_shift(q, kp, vp, pt, lens, sel, scale, S):
+    """softmax without subtracting the running maximum"""
+    B, Hq, d = q.shape
+    H = kp.shape[1]
+    G = Hq // H
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(Hq):
+            g = h // G
+            ks, vs = [], []
+            for j in sel[b, g]:
+                if j < 0:
+                    continue
+                v = max(0, min(S, L - int(j) * S))
+                p = int(pt[b, int(j)])
+                ks.append(kp[p, g, :v])
+                vs.append(vp[p, g, :v])
+            if ks:
+                w = np.exp(np.concatenate(ks) @ q[b, h] * scale)
+                out[b, h] = (w @ np.concatenate(vs)) / w.sum()
+    return out
+
+
+def dense_no_indirection(q, kp, vp, pt, lens, scale, S):
+    """pool page taken to be the logical page"""
+    ident = np.tile(np.arange(pt.shape[1]), (pt.shape[0], 1))
+    ident = np.minimum(ident, kp.shape[0] - 1)
+    return O.dense_attention(q, kp, vp, ident, lens, scale, S)
+
+
+def dense_wrong_heads(q, kp, vp, pt, lens, scale, S):
+    """query head h read against kv-head h % Hkv instead of h // G"""
+    B, Hq, d = q.shape
+    H = kp.shape[1]
+    out = np.zeros((B, Hq, d))
+    for h in range(Hq):
+        g = h % H
+        qh = np.zeros((B, H, d))
+        qh[:, g] = q[:, h]
+        out[:, h] = O.dense_attention(qh, kp, vp, pt, lens, scale, S)[:, g]
+    return out
+
+
+def append_next_slot(k_pool, v_pool, kmin, kmax, pt, b, new_len, k_new, v_new, S):
+    """the token written one slot past position new_len - 1"""
+    O.append_token(k_pool, v_pool, kmin, kmax, pt, b, new_len + 1, k_new, v_new, S)
+
+
+def est_floor_pages(q, kmin, kmax, pt, lens, S, max_pages=None):
+    """a partial last page is not scored (n = floor(L / S))"""
+    full = (np.asarray(lens) // S) * S
+    s = O.estimate(q, kmin, kmax, pt, full, S,
+                   pt.shape[1] if max_pages is None else max_pages)
+    return s
+
+
+def est_group_max(q, kmin, kmax, pt, lens, S, max_pages=None):
+    """a group scored by its best head instead of the sum of its heads"""
+    B, Hq, d = q.shape
+    H = kmin.shape[1]
+    G = Hq // H
+    s = O.estimate_heads(q, kmin, kmax, pt, lens, S, max_pages)
+    return s.reshape(B, H, G, -1).max(axis=2)
+
+
+def topk_signed_zero(scores, n, k):
+    """-0 ranked below +0 (bit order instead of value order)"""
+    s = np.asarray(scores[:n], dtype=np.float64).copy()
+    s[(s == 0) & np.signbit(s)] = -1e-300
+    return O.topk_pages(s, n, k)
+
+
+def forced_zero_window_is_everything(scores, n, k, ns, nl):
+    """n_local = 0 read as a window over every page (a [-0:] slice)"""
+    if nl == 0 and n > k:
+        return np.arange(n - k, n)  # the "window" takes the whole budget
+    return O.topk_pages_forced(scores, n, k, ns, nl)
+
+
+def union_keeps_padding(sel, G):
+    """the -1 padding counted as a page"""
+    u = O.union_pages(sel, G)
+    B, H, K = u.shape
+    out = np.full_like(u, -1)
+    for b in range(B):
+        for g in range(H):
+            pages = set(int(x) for x in u[b, g] if x >= 0)
+            if (sel[b, g * G:(g + 1) * G] < 0).any():
+                pages.add(-1)
+            srt = sorted(pages)
+            out[b, g, :len(srt)] = srt
+    return out
+
+
 MUTANTS = {
     "estimate_dropped_kmin": dict(estimate=est_dropped_kmin),
     "estimate_min_not_max": dict(estimate=est_min_instead_of_max),
@@ -234,6 +329,15 @@ MUTANTS = {
     "sparse_missing_scale": dict(sparse_attention=sparse_no_scale),
     "dense_unnormalised": dict(dense_attention=dense_unnormalised),
     "dense_drops_last_token": dict(dense_attention=dense_off_by_one_token),
+    "sparse_no_max_shift": dict(sparse_attention=sparse_no_max_shift),
+    "dense_no_page_table": dict(dense_attention=dense_no_indirection),
+    "dense_wrong_head_map": dict(dense_attention=dense_wrong_heads),
+    "append_next_slot": dict(append_token=append_next_slot),
+    "estimate_floor_pages": dict(estimate=est_floor_pages),
+    "estimate_group_max": dict(estimate=est_group_max),
+    "topk_signed_zero_order": dict(topk_pages=topk_signed_zero),
+    "forced_zero_window_everything": dict(topk_pages_forced=forced_zero_window_is_everything),
+    "union_keeps_padding": dict(union_pages=union_keeps_padding),
 }
 
 
