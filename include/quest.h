@@ -32,7 +32,7 @@
  * - Slots of a page past the sequence's last token, and pool pages no
  *   request owns, may hold any bits (NaN included): they are never used as
  *   values.
- * - Shapes (d = head_dim = 128, S = page_size = 16, G = Hq / Hkv):
+ * - Shapes (d = head_dim = 128, S = page_size = 16 or 32, G = Hq / Hkv):
  *     k_pool, v_pool  [num_pool_pages][Hkv][S][d]   (dtype)
  *     kmin, kmax      [num_pool_pages][Hkv][d]      (dtype)
  *     page_table      int32 [batch][max_pages_per_seq]; logical page j of
@@ -79,7 +79,7 @@ typedef struct quest_paged_kv {
   int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;      /* Hkv, >= 1 */
   int32_t head_dim;          /* d: must be 128 */
-  int32_t page_size;         /* S: must be 16 */
+  int32_t page_size;         /* S: 16 or 32 ("Guide to Quest", Best Practices 1) */
   int32_t num_pool_pages;    /* pages in k_pool / v_pool / kmin / kmax */
   int32_t max_pages_per_seq; /* columns of page_table and scores */
   int32_t dtype;             /* quest_dtype of q, K, V, kmin, kmax */
