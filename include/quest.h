@@ -231,7 +231,9 @@ QUEST_API quest_status quest_sparse_decode_attn(
 
 /*
  * quest_topk_pages followed by quest_sparse_decode_attn, in one launch (plus
- * the split merge): the same outputs sel_pages and out, bit for bit.  Every
+ * the split merge): the same sel_pages bit for bit, and the same out up to
+ * the float32 rounding of a different split and merge order (workgroups of
+ * 8 waves here, 4 in quest_sparse_decode_attn).  Every
  * attention workgroup of a (request, kv-head) row recomputes the row's exact
  * Top-K from `scores` (float32 [batch][Hkv][max_pages_per_seq], e.g. from
  * quest_estimate) and keeps it in LDS, so no workgroup waits for another and
