@@ -450,6 +450,8 @@ def bench_longchat(args, torch, qa, synth):
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds)
+        if args.cpu_all_cores:
+            line["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(r, args.cpu_seconds)
     return line
 
 
@@ -460,7 +462,7 @@ def bench_ragged(args, torch, qa, synth):
     us = min(tg["mean"], te["mean"], tb["mean"])
     gbps = r["bytes"]["total"] / (us * 1e-6) / 1e9
     us_dense = r["t_dense"]["mean"] if r["t_dense"] else float("nan")
-    return {
+    line = {
         "metric": "µs/decode step + effective HBM GB/s, batched ragged",
         "value": round(us, 3), "unit": "us/step", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
@@ -485,6 +487,9 @@ def bench_ragged(args, torch, qa, synth):
         "roofline": roofline(r["calls"]),
         "gpu": torch.cuda.get_device_name(0),
     }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_ragged(r, args.cpu_seconds)
+    return line
 
 
 def bench_sweep(args, torch, qa, synth):
@@ -592,7 +597,7 @@ def bench_gqa_multistep(args, torch, qa, synth):
     app_b = wl.layers * append_bytes(B, 8)
     total = sparse_b + dense_b + app_b
     all_dense = wl.layers * dense_bytes([L0 + nsteps], 8, 32) + app_b
-    return {
+    line = {
         "metric": "µs per 32-layer decode step, GQA 32/8, 32K ctx, "
                   "2048-token budget, layers 0-1 dense",
         "value": round(us, 3), "unit": "us/step", "n_gpus": 1,
@@ -615,6 +620,9 @@ def bench_gqa_multistep(args, torch, qa, synth):
         "launches_per_step": wl.dense_layers * 3 + (wl.layers - wl.dense_layers) * 3,
         "gpu": torch.cuda.get_device_name(0),
     }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_multistep(layers, wl, args.cpu_seconds)
+    return line
 
 
 def bench_gqa_union(args, torch, qa, synth):
@@ -870,6 +878,182 @@ def cpu_baseline(gpu, budget_s):
                        f"{gpu['kv'].num_q_heads // len(heads)} to 32 heads")}
 
 
+
+def _timed_loop(fn, budget_s):
+    """Call fn() until budget_s seconds have passed: (calls, seconds)."""
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return reps, el
+
+
+def _oracle_worker(task):
+    """One process of the all-cores oracle leg: the step on its kv-heads of
+    the layer saved under `path` (.npy files), one thread, repeated for
+    budget_s seconds.  Returns (steps, seconds, kv-heads)."""
+    path, heads, group, k_pages, sm, S, budget_s = task
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import quest_oracle as O
+
+    def ld(name, index=None):
+        a = np.load(os.path.join(path, name + ".npy"), mmap_mode="r")
+        return np.asarray(a if index is None else a[index], dtype=np.float64)
+
+    qh = [g * group + i for g in heads for i in range(group)]
+    q = ld("q", (slice(None), qh))
+    kp = ld("k_pool", (slice(None), heads))
+    vp = ld("v_pool", (slice(None), heads))
+    pt = ld("page_table").astype(np.int64)
+    lens = ld("seq_lens").astype(np.int64)
+    with threadpool_limits(limits=1):
+        kmin, kmax = O.page_meta(kp, pt, lens, S)
+        reps, el = _timed_loop(
+            lambda: O.decode_step(q, kp, vp, kmin, kmax, pt, lens, k_pages, sm, S),
+            budget_s)
+    return reps, el, len(heads)
+
+
+def cpu_baseline_all_cores(gpu, budget_s):
+    """The oracle's step on every kv-head of the same layer, one process
+    per host core (at most 16), each single-threaded over its share of the
+    heads; the per-process rates add up to the step rate.  The processes
+    start fresh interpreters (spawn) and read the layer from .npy files."""
+    import multiprocessing
+    import tempfile
+
+    import numpy as np
+    import torch
+
+    c, kv = gpu["insts"][0], gpu["kv"]
+    H = kv.num_kv_heads
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16, H))
+    groups = [list(range(H))[i::cores] for i in range(cores)]
+    with tempfile.TemporaryDirectory(prefix="quest_oracle_") as tmp:
+        for name in ("q", "k_pool", "v_pool", "page_table", "seq_lens"):
+            t = c[name].cpu()
+            if t.dtype == torch.bfloat16:
+                t = t.float()
+            np.save(os.path.join(tmp, name + ".npy"), t.numpy())
+        tasks = [(tmp, g, kv.num_q_heads // H, gpu["k_pages"], gpu["sm"],
+                  kv.page_size, budget_s) for g in groups]
+        with multiprocessing.get_context("spawn").Pool(len(groups)) as pool:
+            res = pool.map(_oracle_worker, tasks)
+    rate = sum(reps * h / el for reps, el, h in res)   # kv-head steps per second
+    return {"value": round(H / rate * 1e6, 1), "unit": "us/step",
+            "cores": len(groups), "kind": "oracle",
+            "sample": (f"all {H} kv-heads of the same layer, {len(groups)} "
+                       f"single-threaded processes of {budget_s:.0f} s each "
+                       f"({sum(r for r, _, _ in res)} head-group steps); the "
+                       f"processes' rates summed")}
+
+
+def cpu_baseline_ragged(gpu, budget_s, heads=(0, 1, 2, 3)):
+    """The oracle's step on the two requests of the batch whose lengths are
+    nearest its mean, 4 of the 32 heads, one thread; scaled to the whole
+    batch by (request, kv-head) units."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import quest_oracle as O
+
+    c, kv = gpu["insts"][0], gpu["kv"]
+    S, H = kv.page_size, kv.num_kv_heads
+    G = kv.num_q_heads // H
+    lens_all = c["seq_lens"].cpu().numpy().astype(np.int64)
+    pt_all = c["page_table"].cpu().numpy().astype(np.int64)
+    reqs = sorted(np.argsort(np.abs(lens_all - lens_all.mean()))[:2].tolist())
+    pages = [pt_all[b, :-(-int(lens_all[b]) // S)] for b in reqs]
+    idx = torch.from_numpy(np.concatenate(pages)).to(c["k_pool"].device)
+    f64 = lambda t: t.float().cpu().to(torch.float64).numpy()
+    hs = list(heads)
+    kp = f64(c["k_pool"][idx][:, hs])
+    vp = f64(c["v_pool"][idx][:, hs])
+    q = f64(c["q"][reqs][:, [g * G + i for g in hs for i in range(G)]])
+    pt = np.zeros((len(reqs), max(len(p) for p in pages)), dtype=np.int64)
+    off = 0
+    for i, p in enumerate(pages):
+        pt[i, :len(p)] = np.arange(off, off + len(p))
+        off += len(p)
+    lens = lens_all[reqs]
+    with threadpool_limits(limits=1):
+        kmin, kmax = O.page_meta(kp, pt, lens, S)
+        reps, el = _timed_loop(
+            lambda: O.decode_step(q, kp, vp, kmin, kmax, pt, lens, gpu["k_pages"],
+                                  gpu["sm"], S), budget_s)
+    scale = (len(lens_all) * H) / (len(reqs) * len(hs))
+    return {"value": round(el / reps * scale * 1e6, 1), "unit": "us/step",
+            "cores": 1, "kind": "oracle",
+            "sample": (f"{reps} oracle decode steps over requests {reqs} "
+                       f"(lengths {lens.tolist()}, batch mean "
+                       f"{lens_all.mean():.0f}) x {len(hs)} of {H} heads, "
+                       f"float64, 1 thread, {el:.1f} s, scaled x{scale:.0f} "
+                       f"by (request, kv-head) units")}
+
+
+def cpu_baseline_multistep(layers, wl, budget_s, heads=(0, 1)):
+    """The oracle on one dense and one sparse layer, 2 of the 8 kv-heads
+    (their 8 query heads), the first two decode steps (append, then dense
+    attention or the sparse step), one thread, repeated from the same
+    starting state; scaled to the 32-layer step of all 8 kv-heads."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import quest_oracle as O
+
+    S = wl.page_size
+    G = wl.num_q_heads // wl.num_kv_heads
+    hs = list(heads)
+    qh = [g * G + i for g in hs for i in range(G)]
+    f64 = lambda t: t.float().cpu().to(torch.float64).numpy()
+    nsteps = 2
+    L0 = np.array(wl.seq_lens, dtype=np.int64)
+    sm = 1.0 / math.sqrt(wl.head_dim)
+    legs = {}
+    for name, layer in (("dense", 0), ("sparse", wl.dense_layers)):
+        st = layers[layer]
+        c = st["c"]
+        kp, vp = f64(c["k_pool"][:, hs]), f64(c["v_pool"][:, hs])
+        pt = c["page_table"].cpu().numpy().astype(np.int64)
+        kmin, kmax = O.page_meta(kp, pt, L0, S)   # the boxes before the first append
+        q = [f64(st["q"][s][:, qh]) for s in range(nsteps)]
+        kn = [f64(st["k_new"][s][:, hs]) for s in range(nsteps)]
+        vn = [f64(st["v_new"][s][:, hs]) for s in range(nsteps)]
+        legs[name] = (layer, kp, vp, kmin, kmax, pt, q, kn, vn)
+    spent = {"dense": 0.0, "sparse": 0.0}
+    reps = 0
+    t_start = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t_start < budget_s:
+            for name, (layer, kp, vp, kmin, kmax, pt, q, kn, vn) in legs.items():
+                state = [a.copy() for a in (kp, vp, kmin, kmax)]   # untimed
+                t0 = time.perf_counter()
+                for s in range(nsteps):
+                    O.layer_step(layer, wl.dense_layers, q[s], *state, pt,
+                                 L0 + s + 1, kn[s], vn[s], wl.k_pages, sm, S)
+                spent[name] += time.perf_counter() - t0
+            reps += 1
+    per_layer = {n: spent[n] / (reps * nsteps) for n in spent}
+    scale = wl.num_kv_heads / len(hs)
+    us = (wl.dense_layers * per_layer["dense"] +
+          (wl.layers - wl.dense_layers) * per_layer["sparse"]) * scale * 1e6
+    return {"value": round(us, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
+            "sample": (f"one dense and one sparse layer, kv-heads {hs} of "
+                       f"{wl.num_kv_heads} ({len(qh)} query heads), the first "
+                       f"{nsteps} decode steps, replayed {reps} times from the "
+                       f"same start (float64, 1 thread; {per_layer['dense'] * 1e3:.1f} "
+                       f"and {per_layer['sparse'] * 1e3:.1f} ms per layer-step); "
+                       f"scaled to {wl.dense_layers} dense + "
+                       f"{wl.layers - wl.dense_layers} sparse layers and x{scale:.0f} "
+                       f"kv-heads")}
+
 # ------------------------------------------------------------- counters
 
 def _counter_medians(path):
@@ -931,6 +1115,9 @@ def main():
                     help="independent caches the steps cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-all-cores", action="store_true",
+                    help="also time the oracle on every kv-head with one "
+                         "process per host core (headline workload)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
