@@ -23,16 +23,17 @@ SM = 1.0 / math.sqrt(128)
 def build(wl, layer=0):
     c = synth.draw_layer(wl, layer, "cuda")
     c["kv"] = qa.paged_kv(wl.batch, wl.num_q_heads, wl.num_kv_heads,
-                          wl.pool_pages(), wl.max_pages, wl.torch_dtype)
+                          wl.pool_pages(), wl.max_pages, wl.torch_dtype,
+                          page_size=wl.page_size)
     return c
 
 
-def unit_oracle(c, b, heads, k, G):
+def unit_oracle(c, b, heads, k, G, S=16):
     """Oracle decode step for request b restricted to kv-heads `heads`."""
     kv = c["kv"]
     pt = c["page_table"][b:b + 1].cpu().numpy().astype(np.int64)
     lens = c["seq_lens"][b:b + 1].cpu().numpy().astype(np.int64)
-    n = -(-int(lens[0]) // 16)
+    n = -(-int(lens[0]) // S)
     pages = torch.from_numpy(pt[0, :n]).long().cuda()
     # compact pool: only this request's pages, only the sampled heads
     kp = C.to64(c["k_pool"][pages][:, heads])
@@ -41,25 +42,25 @@ def unit_oracle(c, b, heads, k, G):
     q = C.to64(c["q"][b:b + 1, qh])
     pt_c = np.zeros((1, kv.max_pages_per_seq), dtype=np.int64)
     pt_c[0, :n] = np.arange(n)
-    kmin, kmax = O.page_meta(kp, pt_c, lens, 16)
-    s = O.estimate(q, kmin, kmax, pt_c, lens, 16, kv.max_pages_per_seq)
+    kmin, kmax = O.page_meta(kp, pt_c, lens, S)
+    s = O.estimate(q, kmin, kmax, pt_c, lens, S, kv.max_pages_per_seq)
     return dict(q=q, kp=kp, vp=vp, pt=pt_c, lens=lens, kmin=kmin, kmax=kmax,
                 s=s, n=n, pages=pages)
 
 
-def check_units(c, step, units, k, G, check_meta=None):
+def check_units(c, step, units, k, G, check_meta=None, S=16):
     sel_all = step.sel.cpu().numpy().astype(np.int64)
     scores = step.scores.cpu().numpy().astype(np.float64)
     out = step.out.cpu().numpy().astype(np.float64)
     kv = c["kv"]
     # properties of every row
     for b, L in enumerate(c["seq_lens"].tolist()):
-        n = -(-L // 16)
+        n = -(-L // S)
         for g in range(kv.num_kv_heads):
             C.assert_valid_selection(sel_all[b, g], n, k)
     worst = 0.0
     for b, heads in units:
-        u = unit_oracle(c, b, heads, k, G)
+        u = unit_oracle(c, b, heads, k, G, S)
         if check_meta is not None:
             kmin_g, kmax_g = check_meta
             gm = kmin_g[u["pages"]][:, heads].cpu().view(torch.int16)
@@ -69,11 +70,11 @@ def check_units(c, step, units, k, G, check_meta=None):
             om = torch.from_numpy(u["kmax"]).to(kmax_g.dtype).view(torch.int16)
             assert torch.equal(gm, om), f"kmax differs (b={b})"
         s_gpu = scores[b:b + 1, heads]
-        C.assert_scores_close(s_gpu, u["s"], u["lens"])
+        C.assert_scores_close(s_gpu, u["s"], u["lens"], S)
         sel = sel_all[b:b + 1, heads]
-        C.assert_sets_match(sel, u["s"], u["lens"], k)
+        C.assert_sets_match(sel, u["s"], u["lens"], k, S)
         ref = O.sparse_attention(u["q"], u["kp"], u["vp"], u["pt"], u["lens"],
-                                 sel, SM, 16)
+                                 sel, SM, S)
         qh = [g * G + r for g in heads for r in range(G)]
         worst = max(worst, C.assert_attention_close(out[b:b + 1, qh], ref))
     return worst
@@ -125,6 +126,34 @@ def test_ragged_batch_bf16():
     step, meta = run_paths(c, wl.k_pages)
     check_units(c, step, [(0, [0]), (9, [13]), (17, [31]), (31, [2])],
                 wl.k_pages, 1, check_meta=meta)
+
+
+def test_gqa8_bf16_layer_32k():
+    """A 32 / 4-head GQA layer (groups of 8 query heads on the matrix cores)
+    in bf16 at 32K with a 2048-token budget, in the benchmark's launch
+    configuration (Top-K inside the attention launch)."""
+    wl = synth.Workload("gqa8_bf16_32k", 1, 32, 4, (32768,), 2048, "bf16",
+                        outliers=4, base_seed=71)
+    C.say(f"[case] {wl.name}: Hq 32 / Hkv 4, ctx 32768, k={wl.k_pages}, bf16")
+    c = build(wl)
+    step, meta = run_paths(c, wl.k_pages)
+    assert step.select == "attention"
+    worst = check_units(c, step, [(0, [0]), (0, [3])], wl.k_pages, wl.group,
+                        check_meta=meta)
+    C.say(f"  sampled attention max err {worst:.2e}")
+
+
+def test_page32_layer_128k():
+    """32-token pages at 128K context with a 2048-token budget (64 pages of
+    4096 per head), 32 heads, fp16."""
+    wl = synth.Workload("p32_128k", 1, 32, 32, (131072,), 2048, "f16",
+                        page_size=32, outliers=4, planted=5, base_seed=72)
+    C.say(f"[case] {wl.name}: 32 heads, ctx 131072, 32-token pages, k={wl.k_pages}")
+    c = build(wl)
+    step, meta = run_paths(c, wl.k_pages)
+    worst = check_units(c, step, [(0, [4]), (0, [29])], wl.k_pages, 1,
+                        check_meta=meta, S=32)
+    C.say(f"  sampled attention max err {worst:.2e}")
 
 
 def test_gqa_multistep_three_layers():
