@@ -296,11 +296,13 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
         return t["mean"] / rot
 
     t_batch = dict(mean=batch_us(steps))
-    # Warm, labelled apart: the first cache's step back to back, so that its
-    # bytes stay in the 256 MB Infinity Cache between steps.
-    g_warm = capture(torch, lambda: [step_call(0) for _ in range(rot)])
-    t_warm = tm.run(lambda i: g_warm.replay(), max(1, args.steps // rot),
-                    max(1, args.warmup // rot), 1, events=False)["mean"] / rot
+    # Warm (--warm), labelled apart: the first cache's step back to back, so
+    # that its bytes stay in the 256 MB Infinity Cache between steps.
+    t_warm = None
+    if args.warm:
+        g_warm = capture(torch, lambda: [step_call(0) for _ in range(rot)])
+        t_warm = tm.run(lambda i: g_warm.replay(), max(1, args.steps // rot),
+                        max(1, args.warmup // rot), 1, events=False)["mean"] / rot
     # the other places the selection can run, timed the same way
     by_select = {steps[0].select: round(t_batch["mean"], 3)}
     for mode in ("attention", "separate"):
@@ -442,13 +444,14 @@ def bench_longchat(args, torch, qa, synth):
                   f"holding a step on each of the {args.rotate} rotating caches "
                   "back to back (wall clock / steps); the dense baseline is "
                   "timed the last way; percentiles from HIP events around each "
-                  "one-step graph replay; warm_* repeats one cache's step back "
-                  "to back (its bytes stay in the Infinity Cache), not the value",
+                  "one-step graph replay; warm_* (with --warm) repeats one "
+                  "cache's step back to back (its bytes stay in the Infinity "
+                  "Cache), not the value",
         "eager_us_per_step": round(te["mean"], 3),
         "graph_us_per_step": round(tg["mean"], 3),
         "graph_batch_us_per_step": round(tb["mean"], 3),
         "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
-        "warm_graph_batch_us_per_step": round(r["t_warm"], 3),
+        "warm_graph_batch_us_per_step": None if r["t_warm"] is None else round(r["t_warm"], 3),
         "step_us_by_select": r["by_select"],
         "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
         "other_call_us": r["other_calls"],
@@ -1122,6 +1125,9 @@ def main():
                     help="independent caches the steps cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time one cache's step back to back (bytes held "
+                         "in the Infinity Cache), reported apart from the value")
     ap.add_argument("--cpu-all-cores", action="store_true",
                     help="also time the oracle on every kv-head with one "
                          "process per host core (headline workload)")
