@@ -61,6 +61,7 @@ def test_status_strings():
     ("num_q_heads", 96, _abi.QUEST_ERR_UNSUPPORTED),        # G = 3
     ("batch", 0, _abi.QUEST_ERR_INVALID_ARGUMENT),
     ("max_pages_per_seq", 0, _abi.QUEST_ERR_INVALID_ARGUMENT),
+    ("batch", 2048, _abi.QUEST_ERR_UNSUPPORTED),            # 65536 rows > 65535
 ])
 def test_geometry_validation(field, value, status):
     st, _ = ws_size(kv(**{field: value}))
