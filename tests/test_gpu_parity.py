@@ -169,7 +169,8 @@ def _topk_case(rows, n_list, mp, k, seed):
     """fp32 scores [B, 1, mp] with NaN beyond each row's n (must be ignored)."""
     g = np.random.default_rng(seed)
     s = np.full((rows, 1, mp), np.nan, dtype=np.float32)
-    kinds = ["normal", "ties", "equal", "zeros", "inf", "sorted_up", "sorted_dn"]
+    kinds = ["normal", "ties", "equal", "zeros", "inf", "sorted_up", "sorted_dn",
+             "denormal", "extreme"]
     for r in range(rows):
         n = n_list[r]
         kind = kinds[r % len(kinds)]
@@ -188,6 +189,16 @@ def _topk_case(rows, n_list, mp, k, seed):
             v[g.random(n) < 0.05] = np.inf
         elif kind == "sorted_up":
             v = np.arange(n, dtype=np.float32)
+        elif kind == "denormal":  # signed subnormals, signed zeros, ties among them
+            tiny = np.float32(1.4e-45)
+            v = (g.integers(-40, 41, n) * tiny).astype(np.float32)
+            v[g.random(n) < 0.2] = -0.0
+        elif kind == "extreme":  # the ends of the float32 range and its neighbours
+            pool = np.array([np.finfo(np.float32).max, -np.finfo(np.float32).max,
+                             np.nextafter(np.finfo(np.float32).max, np.float32(0)),
+                             np.finfo(np.float32).tiny, -np.finfo(np.float32).tiny,
+                             1.0, -1.0, np.inf, -np.inf], dtype=np.float32)
+            v = pool[g.integers(0, len(pool), n)]
         else:
             v = -np.arange(n, dtype=np.float32)
         s[r, 0, :n] = v
