@@ -122,8 +122,9 @@ QUEST_API quest_status quest_update_page_meta(
  * heads' bounds.  The boxes must satisfy kmin <= kmax in every channel, as
  * quest_update_page_meta writes them: each term is then evaluated as
  * q_i * kmax_i for q_i >= 0 and q_i * kmin_i otherwise, which is the max.
- * Products are exact in float32 for fp16/bf16 inputs of normal range; the
- * sum rounds in float32.
+ * Products are exact in float32 for fp16/bf16 inputs whenever the product
+ * is a normal float32 number (16-bit subnormal inputs are not flushed);
+ * the sum rounds in float32.
  */
 QUEST_API quest_status quest_estimate(
     const quest_paged_kv* kv, const void* q, const void* kmin,

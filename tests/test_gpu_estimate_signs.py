@@ -79,3 +79,43 @@ def test_estimate_all_zero_query_scores_zero():
         n = -(-int(L) // 16)
         assert torch.all(s[b, :, :n] == 0.0)
         assert torch.all(torch.isneginf(s[b, :, n:]))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_estimate_and_attention_with_subnormal_keys(dtype):
+    """Keys scaled into the 16-bit subnormal range (fp16: below 2^-14): the
+    boxes, the bounds and the attention must use their exact values (no
+    flush to zero of 16-bit inputs)."""
+    G = 4
+    wl = C.workload(2, 4 * G, 4, (333, 64), 64, dtype, seed=60, name="subnormal")
+    C.say(f"[case] subnormal keys {dtype}")
+    c = C.draw(wl)
+    # keys subnormal in their dtype; q scaled so that every product is a
+    # normal float32 number
+    k_scale, q_scale = (2.0 ** -20, 8.0) if dtype == "f16" else (2.0 ** -130, 2.0 ** 100)
+    c["k_pool"] = (c["k_pool"].float() * k_scale).to(wl.torch_dtype)
+    c["q"] = (c["q"].float() * q_scale).to(wl.torch_dtype)
+    o = C.oracle_inputs(c)
+    used = C.used_pages(o["page_table"], o["seq_lens"])
+    kp = o["k_pool"][used]
+    tiny = np.finfo(np.float16).tiny if dtype == "f16" else 2.0 ** -126
+    frac = np.mean((np.abs(kp) < tiny) & (kp != 0))
+    assert frac > 0.5, f"only {frac:.2f} of the keys are subnormal"
+    kmin, kmax = C.gpu_meta(c)
+    omin, omax = O.page_meta(o["k_pool"], o["page_table"], o["seq_lens"], 16)
+    C.assert_meta_bitexact(kmin, kmax, omin, omax, used)
+    kv = c["kv"]
+    s = torch.empty((kv.batch, kv.num_kv_heads, kv.max_pages_per_seq), device="cuda")
+    qa.quest_estimate(kv, c["q"], kmin, kmax, c["page_table"], c["seq_lens"], s)
+    torch.cuda.synchronize()
+    ora = O.estimate(o["q"], omin, omax, o["page_table"], o["seq_lens"], 16,
+                     kv.max_pages_per_seq)
+    C.assert_scores_close(s.cpu().numpy().astype(np.float64), ora, o["seq_lens"])
+    # attention over every page: the logits are tiny, the output the mean of V
+    step = qa.SparseDecodeStep(kv, kv.max_pages_per_seq, 1.0 / np.sqrt(128))
+    out = step(c["q"], c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"],
+               c["seq_lens"])
+    torch.cuda.synchronize()
+    ref = O.dense_attention(o["q"], o["k_pool"], o["v_pool"], o["page_table"],
+                            o["seq_lens"], 1.0 / np.sqrt(128), 16)
+    C.assert_attention_close(out.cpu().numpy().astype(np.float64), ref)
