@@ -82,3 +82,38 @@ def test_page_ids_outside_the_pool_are_absent(G, select, budget):
     ref_d = O.sparse_attention(o["q"], o["k_pool"], o["v_pool"], ok, o["seq_lens"],
                                every, SM, 16)
     C.assert_attention_close(d.cpu().numpy().astype(np.float64), ref_d)
+
+
+def test_lengths_past_the_table_are_clamped():
+    """A length above max_pages_per_seq * page_size counts as that many
+    tokens (quest.h): with a request whose pages are all full, raising its
+    length past the table changes no box, bound, list or output bit."""
+    lens = (64 * 16, 500)
+    wl = C.workload(2, 8, 4, lens, 20 * 16, "f16", seed=95, permute=True,
+                    name="clamped")
+    C.say(f"[case] lengths past the table lens={lens} max_pages={wl.max_pages}")
+    c = C.draw(wl)
+    kv = c["kv"]
+    assert kv.max_pages_per_seq == 64
+    long_lens = c["seq_lens"].clone()
+    long_lens[0] += 777
+    res = []
+    for L in (c["seq_lens"], long_lens):
+        kmin, kmax = qa.alloc_meta(kv)
+        kmin.fill_(float("nan"))
+        kmax.fill_(float("nan"))
+        qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], kmin, kmax,
+                                  c["page_table"], L)
+        step = qa.SparseDecodeStep(kv, wl.k_pages, SM)
+        step(c["q"], c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"], L)
+        dense = qa.DenseDecode(kv, SM)
+        d = dense(c["q"], c["k_pool"], c["v_pool"], c["page_table"], L)
+        torch.cuda.synchronize()
+        res.append((kmin.view(torch.int16).clone(), kmax.view(torch.int16).clone(),
+                    step.scores.view(torch.int32).clone(), step.sel.clone(),
+                    step.out.view(torch.int32).clone(), d.view(torch.int32).clone()))
+    used = torch.tensor(C.used_pages(c["page_table"].cpu().numpy(), lens), device="cuda")
+    a, b = res
+    assert torch.equal(a[0][used], b[0][used]) and torch.equal(a[1][used], b[1][used])
+    for x, y in zip(a[2:], b[2:]):
+        assert torch.equal(x, y)
