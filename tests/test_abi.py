@@ -287,3 +287,22 @@ def test_last_error_is_per_thread():
         t.join(timeout=30)
     assert seen["a"].startswith("quest_topk_pages:") and "k_pages" in seen["a"]
     assert seen["b"].startswith("quest_topk_pages_ex:") and "n_sink" in seen["b"]
+
+
+def test_paged_kv_like_reads_the_geometry_off_the_tensors():
+    import torch
+    q = torch.zeros(3, 8, 128, dtype=torch.bfloat16)
+    k_pool = torch.zeros(10, 2, 32, 128, dtype=torch.bfloat16)
+    pt = torch.zeros(3, 7, dtype=torch.int32)
+    kv = qa.paged_kv_like(q, k_pool, pt)
+    assert (kv.batch, kv.num_q_heads, kv.num_kv_heads, kv.num_pool_pages,
+            kv.max_pages_per_seq, kv.page_size, kv.head_dim) == (3, 8, 2, 10, 7, 32, 128)
+    assert kv.dtype == _abi.QUEST_BF16
+    st, n = ws_size(kv, 7)
+    assert st == _abi.QUEST_OK
+    with pytest.raises(ValueError):
+        qa.paged_kv_like(q, k_pool[..., :64], pt)      # head dims disagree
+    with pytest.raises(ValueError):
+        qa.paged_kv_like(q, k_pool, pt[:2])            # batch disagrees
+    with pytest.raises(ValueError):
+        qa.paged_kv_like(q.float(), k_pool.float(), pt)  # no float32 caches
