@@ -80,6 +80,19 @@ CALLS = {
     "quest_topk_pages": {
         "kernels": ["topk_kernel"],
         "sources": ["topk.hip", "dev_topk.h", "common.h", "launch.h"]},
+    "quest_estimate_heads": {
+        "kernels": ["estimate_kernel"],
+        "sources": ["estimate.hip", "dev_estimate.h", "common.h", "launch.h"]},
+    "quest_append_estimate": {
+        "kernels": ["estimate_kernel"],
+        "sources": ["estimate.hip", "dev_estimate.h", "common.h", "launch.h"]},
+    "quest_decode_attn": {
+        "kernels": ["attn_split_kernel", "attn_merge_kernel"],
+        "sources": ["attention.hip", "dev_attn.h", "dev_attn_mfma.h", "common.h",
+                    "launch.h"]},
+    "quest_union_pages": {
+        "kernels": ["union_kernel"],
+        "sources": ["union.hip", "common.h", "launch.h"]},
     "quest_topk_sparse_decode_attn": {
         "kernels": ["topk_attn_kernel", "attn_merge_kernel"],
         "sources": ["topk_attn.hip", "attention.hip", "dev_topk.h",
@@ -522,7 +535,8 @@ def bench_sweep(args, torch, qa, synth):
                 "dense_us": round(us_dense, 3),
                 "speedup_vs_dense": round(us_dense / us, 3),
                 "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
-                "other_call_us": r["other_calls"]})
+                "other_call_us": r["other_calls"],
+                "roofline": roofline(r["calls"])})
             print(json.dumps({"progress": points[-1]}), file=sys.stderr, flush=True)
             del r
             torch.cuda.empty_cache()
@@ -537,6 +551,7 @@ def bench_sweep(args, torch, qa, synth):
         "config": {"workload": "ctx_budget_sweep", "ctx": list(synth.SWEEP_CTX),
                    "budget_tokens": list(synth.SWEEP_BUDGET),
                    "value_at": "ctx 32768, budget 2048"},
+        "roofline": at["roofline"],
         "points": points, "gpu": torch.cuda.get_device_name(0)}
 
 
@@ -607,6 +622,51 @@ def bench_gqa_multistep(args, torch, qa, synth):
     app_b = wl.layers * append_bytes(B, 8)
     total = sparse_b + dense_b + app_b
     all_dense = wl.layers * dense_bytes([L0 + nsteps], 8, 32) + app_b
+
+    # the layers' calls at the last step, one by one (a graph of one call
+    # per layer, back to back, so that each reads its bytes from HBM); the
+    # roofline is that of the call with the most time per 32-layer step
+    s_l = nsteps - 1
+    sparse_l = layers[wl.dense_layers:wl.dense_layers + 8]
+    dense_l = layers[:wl.dense_layers]
+    Lf = L0 + nsteps
+    mp = sparse_l[0]["kv"].max_pages_per_seq
+
+    def ae(i):
+        sp = sparse_l[i]
+        c, st = sp["c"], sp["step"]
+        qa.quest_append_estimate(sp["kv"], c["k_pool"], c["v_pool"], c["kmin"], c["kmax"],
+                                 c["page_table"], lens[s_l], sp["k_new"][s_l],
+                                 sp["v_new"][s_l], sp["q"][s_l], st.scores)
+
+    def ta(i):
+        sp = sparse_l[i]
+        c, st = sp["c"], sp["step"]
+        qa.quest_topk_sparse_decode_attn(sp["kv"], sp["q"][s_l], c["k_pool"], c["v_pool"],
+                                         c["page_table"], lens[s_l], st.scores, k, sm,
+                                         st.sel, st.out, st.workspace)
+
+    def da(i):
+        de = dense_l[i]
+        c, d_ = de["c"], de["dense"]
+        qa.quest_decode_attn(de["kv"], de["q"][s_l], c["k_pool"], c["v_pool"],
+                             c["page_table"], lens[s_l], sm, d_.out, d_.workspace)
+
+    reps = max(10, args.steps // 8)
+    t_calls = {"quest_append_estimate": call_us(torch, ae, len(sparse_l), reps),
+               "quest_topk_sparse_decode_attn": call_us(torch, ta, len(sparse_l), reps),
+               "quest_decode_attn": call_us(torch, da, len(dense_l), reps)}
+    sb = step_bytes([Lf], 8, 32, k, sel=sparse_l[0]["step"].sel.cpu().numpy())
+    b_calls = {
+        "quest_append_estimate": sb["meta"] + sb["q"] + sb["table"] + 8 * mp * 4 +
+                                 append_bytes(1, 8),
+        "quest_topk_sparse_decode_attn": sb["kv"] + sb["q"] + sb["out"] + 8 * mp * 4 +
+                                         8 * k * 4,
+        "quest_decode_attn": dense_bytes([Lf], 8, 32)}
+    per_step = {"quest_append_estimate": wl.layers - wl.dense_layers,
+                "quest_topk_sparse_decode_attn": wl.layers - wl.dense_layers,
+                "quest_decode_attn": wl.dense_layers}
+    dom = max(t_calls, key=lambda c_: t_calls[c_] * per_step[c_])
     line = {
         "metric": "µs per 32-layer decode step, GQA 32/8, 32K ctx, "
                   "2048-token budget, layers 0-1 dense",
@@ -628,6 +688,8 @@ def bench_gqa_multistep(args, torch, qa, synth):
         "graph_us_per_step": round(tg["mean"], 3),
         "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
         "launches_per_step": wl.dense_layers * 3 + (wl.layers - wl.dense_layers) * 3,
+        "layer_call_us": {c_: round(v, 3) for c_, v in t_calls.items()},
+        "roofline": roofline({dom: (t_calls[dom], b_calls[dom])}),
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu:
@@ -671,6 +733,41 @@ def bench_gqa_union(args, torch, qa, synth):
         res[name] = dict(us=t["mean"] / rot, bytes=sum(b) / rot,
                          pages=sum(kept) / rot)
     u, sm_ = res["union"], res["sum"]
+
+    # the union step's calls one by one, for its roofline
+    def e_heads(i):
+        c, st = insts[i], unions[i]
+        qa.quest_estimate_heads(kv, c["q"], c["kmin"], c["kmax"], c["page_table"],
+                                c["seq_lens"], st.scores)
+
+    def tk_heads(i):
+        c, st = insts[i], unions[i]
+        qa.quest_topk_pages_ex(st.kv_heads, st.scores, c["seq_lens"], k, 0, 0,
+                               st.sel_heads)
+
+    def un(i):
+        st = unions[i]
+        qa.quest_union_pages(kv, st.sel_heads, k, st.sel)
+
+    def att(i):
+        c, st = insts[i], unions[i]
+        qa.quest_sparse_decode_attn(kv, c["q"], c["k_pool"], c["v_pool"],
+                                    c["page_table"], c["seq_lens"], st.sel, G * k,
+                                    sm, st.out, st.workspace)
+
+    reps = max(10, args.steps // rot)
+    t_calls = {name: call_us(torch, f, rot, reps) for name, f in (
+        ("quest_estimate_heads", e_heads), ("quest_topk_pages", tk_heads),
+        ("quest_union_pages", un), ("quest_sparse_decode_attn", att))}
+    lens = [int(x) for x in insts[0]["seq_lens"].cpu()]
+    Hq, Hkv, mp = kv.num_q_heads, kv.num_kv_heads, kv.max_pages_per_seq
+    sb = step_bytes(lens, Hkv, Hq, k, sel=unions[0].sel.cpu().numpy())
+    b_calls = {
+        "quest_estimate_heads": sb["meta"] + sb["q"] + sb["table"] + Hq * mp * 4,
+        "quest_topk_pages": Hq * mp * 4 + Hq * k * 4,
+        "quest_union_pages": Hq * k * 4 + Hkv * G * k * 4,
+        "quest_sparse_decode_attn": sb["kv"] + sb["q"] + sb["out"] + Hkv * G * k * 4}
+    calls = {c_: (t_calls[c_], b_calls[c_]) for c_ in t_calls}
     return {
         "metric": "µs/decode step, GQA 32/8 layer, per-head Top-K + union vs "
                   "group-sum Top-K",
@@ -690,6 +787,8 @@ def bench_gqa_union(args, torch, qa, synth):
                       "effective_GBps": round(sm_["bytes"] / (sm_["us"] * 1e-6) / 1e9, 1),
                       "pages_per_kv_head": round(sm_["pages"], 1)},
         "union_pages_over_k": round(u["pages"] / k, 3),
+        "union_call_us": {c_: round(v[0], 3) for c_, v in calls.items()},
+        "roofline": roofline(calls),
         "group": G, "gpu": torch.cuda.get_device_name(0)}
 
 
@@ -742,6 +841,7 @@ def bench_page32(args, torch, qa, synth):
                 "meta_bytes_per_step": int(r["bytes"]["meta"]),
                 "dense_us": round(r["t_dense"]["mean"], 3) if r["t_dense"] else None,
                 "call_us": {k_: round(v[0], 3) for k_, v in r["calls"].items()},
+                "roofline": roofline(r["calls"]),
                 "prefill_meta_build_us": round(meta_us, 2),
                 "prefill_meta_GBps": round(meta_bytes / (meta_us * 1e-6) / 1e9, 1),
                 "prefill_k_write_us": round(kwrite_us, 2),
@@ -761,6 +861,7 @@ def bench_page32(args, torch, qa, synth):
         "config": {"workload": "page_size_16_vs_32", "ctx": [32768, 131072],
                    "page_size": [16, 32], "budget_tokens": 2048,
                    "value_at": "ctx 131072, page size 32"},
+        "roofline": at["roofline"],
         "points": rows, "gpu": torch.cuda.get_device_name(0)}
 
 
