@@ -12,11 +12,17 @@ the arithmetic fix.
   n/16 + k page-equivalents of K+V, so the ideal speedup over dense is
   16 n / (n + 16 k): 8.0x at 32K context and a 2048-token budget.
 """
+import json
+import os
+
 import pytest
 
 import bench
 
 pytestmark = pytest.mark.filterwarnings("ignore")
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                     "byte_model.json")))
 
 
 def test_longchat_layer_bytes():
@@ -29,11 +35,14 @@ def test_longchat_layer_bytes():
 
 
 def test_kv_cache_of_a_7b_model_at_32k_is_16_gib():
-    assert bench.kv_cache_bytes(32, 32, 128, 32768) == 16 * 2**30
+    g = GOLDEN
+    assert bench.kv_cache_bytes(g["layers"], g["heads"], g["head_dim"], g["ctx"],
+                                g["bytes_per_elem"]) == g["kv_cache_bytes"] == 16 * 2**30
 
 
-@pytest.mark.parametrize("S, frac", [(16, 0.125), (32, 0.0625)])
-def test_metadata_fraction_of_k(S, frac):
+@pytest.mark.parametrize("S", [16, 32])
+def test_metadata_fraction_of_k(S):
+    frac = GOLDEN["meta_fraction_of_k"][str(S)]
     L = 4096
     n = L // S
     meta = bench.step_bytes([L], 1, 1, 1, page_size=S)["meta"]
