@@ -7,11 +7,14 @@ Workloads (each prints ONE JSON line):
 * ``longchat`` (default, the headline): one LongChat-7B-shaped layer -- 32
   heads, 32K context, 2048-token budget, fp16.  A "step" is one pass of the
   whole hot path: quest_estimate -> quest_topk_sparse_decode_attn (Top-K +
-  sparse attention + split merge), issued eagerly or replayed as a HIP graph
-  (the faster counts; both are reported).  Consecutive steps rotate over
-  several independent caches whose touched bytes (metadata + selected
-  pages) together exceed the 256 MB Infinity Cache, so every step reads its
-  bytes from HBM.
+  sparse attention + split merge).  Consecutive steps rotate over 16
+  independent caches whose touched bytes (metadata + selected pages, 1 GiB
+  per pass) are four times the 256 MB Infinity Cache, so every step reads
+  its bytes from HBM.  The value is the mean over >= 100 steps of one HIP
+  graph holding a step on each cache, replayed back to back (HIP events
+  around each replay; percentiles over the replays).  The same line carries
+  the ragged batch, the 32-layer GQA step and two sweep points under
+  ``extra`` (``--no-extra`` skips them).
 * ``gqa_multistep``: 32 layers of 32 q-heads / 8 kv-heads; every step
   appends one token per layer, runs dense attention on layers 0-1
   (quest_update_page_meta in append mode, then quest_decode_attn) and the
@@ -35,8 +38,11 @@ Inputs are seeded synthetic tensors drawn on the GPU and resident in HBM
 before timing starts.  The line carries the step time (the metric),
 effective GB/s on the algorithmic bytes, the dense-baseline time and
 speedup, the measured stream-read ceiling, a roofline object for the
-dominant call (HIP-event time on the launch stream) and, for the headline,
-a CPU-oracle baseline timed on a bounded sample of the same workload.
+dominant kernel (each kernel of the step timed alone, HIP events on the
+launch stream, algorithmic bytes of the step's byte model with the score,
+selection and partial round trips listed apart) and, for the headline, a
+CPU-oracle baseline timed on a bounded sample of the same workload (one
+thread, and every kv-head over one process per host core).
 
     python bench.py --pmc-summary DIR
 
@@ -67,36 +73,16 @@ METRIC = ("µs/decode step + effective HBM GB/s, 32 heads, 32K ctx, "
           "2048-token budget")
 CSRC = os.path.join(ROOT, "query_aware_kv_amd", "csrc")
 
-# The kernels each timed call launches, and the sources they compile from
-# (a change to any of them invalidates the recorded HBM traffic).
-CALLS = {
-    "quest_sparse_decode_attn": {
-        "kernels": ["attn_split_kernel", "attn_merge_kernel"],
-        "sources": ["attention.hip", "dev_attn.h", "dev_attn_mfma.h", "common.h",
-                    "launch.h"]},
-    "quest_estimate": {
-        "kernels": ["estimate_kernel"],
-        "sources": ["estimate.hip", "dev_estimate.h", "common.h", "launch.h"]},
-    "quest_topk_pages": {
-        "kernels": ["topk_kernel"],
-        "sources": ["topk.hip", "dev_topk.h", "common.h", "launch.h"]},
-    "quest_estimate_heads": {
-        "kernels": ["estimate_kernel"],
-        "sources": ["estimate.hip", "dev_estimate.h", "common.h", "launch.h"]},
-    "quest_append_estimate": {
-        "kernels": ["estimate_kernel"],
-        "sources": ["estimate.hip", "dev_estimate.h", "common.h", "launch.h"]},
-    "quest_decode_attn": {
-        "kernels": ["attn_split_kernel", "attn_merge_kernel"],
-        "sources": ["attention.hip", "dev_attn.h", "dev_attn_mfma.h", "common.h",
-                    "launch.h"]},
-    "quest_union_pages": {
-        "kernels": ["union_kernel"],
-        "sources": ["union.hip", "common.h", "launch.h"]},
-    "quest_topk_sparse_decode_attn": {
-        "kernels": ["topk_attn_kernel", "attn_merge_kernel"],
-        "sources": ["topk_attn.hip", "attention.hip", "dev_topk.h",
-                    "dev_attn.h", "dev_attn_mfma.h", "common.h", "launch.h"]},
+# The sources each kernel compiles from: a change to any of them makes the
+# recorded HBM traffic of that kernel stale (reported as null).
+_ATTN_SRC = ["dev_attn.h", "dev_attn_mfma.h", "common.h", "launch.h"]
+KERNELS = {
+    "estimate_kernel": ["estimate.hip", "dev_estimate.h", "common.h", "launch.h"],
+    "topk_kernel": ["topk.hip", "dev_topk.h", "common.h", "launch.h"],
+    "topk_attn_kernel": ["topk_attn.hip", "dev_topk.h"] + _ATTN_SRC,
+    "attn_split_kernel": ["attention.hip"] + _ATTN_SRC,
+    "attn_merge_kernel": ["attention.hip"] + _ATTN_SRC,
+    "union_kernel": ["union.hip", "common.h", "launch.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_longchat32k.md")
 
@@ -155,17 +141,19 @@ def sources_digest(names):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(call):
-    """HBM bytes per launch of `call` from the committed rocprofv3 counter
-    summary, or None if there is none or the call's sources changed since."""
+def recorded_traffic(kernel):
+    """(HBM bytes per launch, sources digest) of `kernel` from the committed
+    rocprofv3 counter summary, or (None, digest) if there is none or the
+    kernel's sources changed since the counters were taken."""
+    digest = sources_digest(KERNELS[kernel])
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
-        return None
-    m = re.search(r"^\| %s \| (\d+) \| ([0-9a-f]+) \|" % re.escape(call), text, re.M)
-    if not m or m.group(2) != sources_digest(CALLS[call]["sources"]):
-        return None
-    return int(m.group(1))
+        return None, digest
+    m = re.search(r"^\| %s \| (\d+) \| ([0-9a-f]+) \|" % re.escape(kernel), text, re.M)
+    if not m or m.group(2) != digest:
+        return None, digest
+    return int(m.group(1)), digest
 
 
 # ------------------------------------------------------------- GPU helpers
@@ -176,39 +164,6 @@ def pct(xs, p):
     return xs[i]
 
 
-class Timer:
-    """Wall-clock mean per step (synchronised at both ends) and per-step
-    HIP-event durations on the launch stream for percentiles."""
-
-    def __init__(self, torch):
-        self.torch = torch
-
-    def run(self, fn, n, w, rot, events=True):
-        torch = self.torch
-        stream = torch.cuda.current_stream()
-        for i in range(w):
-            fn(i % rot)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(n):
-            fn(i % rot)
-        torch.cuda.synchronize()
-        mean = (time.perf_counter() - t0) / n * 1e6
-        if not events:
-            return dict(mean=mean)
-        pairs = []
-        for i in range(n):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn(i % rot)
-            e1.record(stream)
-            pairs.append((e0, e1))
-        torch.cuda.synchronize()
-        ts = [a.elapsed_time(b) * 1e3 for a, b in pairs]
-        return dict(mean=mean, p10=pct(ts, 10), p50=pct(ts, 50), p90=pct(ts, 90))
-
-
 def capture(torch, fn):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -216,21 +171,62 @@ def capture(torch, fn):
     return g
 
 
-def call_us(torch, call, rot, reps):
-    """Device time of one call: HIP events on the launch stream around
-    replays of a graph holding one launch per cache, back to back."""
-    stream = torch.cuda.current_stream()
-    g = capture(torch, lambda: [call(i) for i in range(rot)])
-    g.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
+def graph_batch(torch, fn, rot, min_steps=100, min_replays=10, warm=2):
+    """The timing protocol of every figure in a line: one HIP graph holding
+    fn(0), ..., fn(rot - 1) -- one step (or call) on each of the rotating
+    caches, back to back -- replayed R >= max(min_replays, min_steps / rot)
+    times back to back after `warm` untimed replays.  HIP events on the
+    launch stream bracket every replay; the mean is over all R * rot steps,
+    the percentiles over the replays' per-step means.  Wall clock (host,
+    synchronised on both sides) is reported alongside."""
+    g = capture(torch, lambda: [fn(i) for i in range(rot)])
+    for _ in range(max(1, warm)):
         g.replay()
-    e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * rot)
+    R = max(min_replays, -(-min_steps // rot))
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(R):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e6 / (R * rot)
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 / rot for i in range(R)]
+    mean = ev[0].elapsed_time(ev[R]) * 1e3 / (R * rot)
+    del g
+    return dict(mean=mean, wall=wall, p10=pct(per, 10), p50=pct(per, 50),
+                p90=pct(per, 90), steps=R * rot, replays=R)
+
+
+def eager_us(torch, fn, rot, n, warm):
+    """Wall-clock µs per step of eager issue (the calls from Python through
+    ctypes, no graph), synchronised on both sides."""
+    for i in range(warm):
+        fn(i % rot)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        fn(i % rot)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / n * 1e6
+
+
+def one_graph_us(torch, fn, rot, n, warm):
+    """Wall-clock µs per step of one HIP graph per step, replayed one at a
+    time from the host."""
+    gs = [capture(torch, lambda i=i: fn(i)) for i in range(rot)]
+    for i in range(warm):
+        gs[i % rot].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        gs[i % rot].replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / n * 1e6
+    del gs
+    return us
 
 
 def stream_read_ceiling(torch, qa, gib=4, reps=10):
@@ -267,10 +263,11 @@ def make_layer(qa, synth, wl, layer=0, dev="cuda"):
     return c
 
 
-def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=True):
+def time_single_layer(args, torch, qa, synth, wls, with_dense=True, full=True):
     """Sparse step (and dense baseline) over rotating instances of one layer
-    geometry; per-call device times; algorithmic bytes from the selections
-    actually made."""
+    geometry, every figure by the back-to-back graph protocol
+    (graph_batch); each kernel of the step timed alone the same way;
+    algorithmic bytes from the selections actually made."""
     rot = len(wls)
     insts = [make_layer(qa, synth, wl) for wl in wls]
     torch.cuda.synchronize()
@@ -279,6 +276,8 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
     sm = 1.0 / math.sqrt(128)
     steps = [qa.SparseDecodeStep(kv, k, sm, select=args.select) for _ in range(rot)]
     denses = [qa.DenseDecode(kv, sm) for _ in range(rot)] if with_dense else []
+    min_steps = max(100, args.steps)
+    warm = max(1, -(-args.warmup // rot))
 
     def step_call(i, sts=steps):
         c = insts[i]
@@ -294,50 +293,43 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
         if with_dense:
             dense_call(i)
     torch.cuda.synchronize()
-    step_graphs = [capture(torch, lambda i=i: step_call(i)) for i in range(rot)]
-    tm = Timer(torch)
-    t_graph = tm.run(lambda i: step_graphs[i].replay(), args.steps, args.warmup,
-                     rot, events=percentiles)
-    t_eager = tm.run(step_call, args.steps, args.warmup, rot, events=False)
-
-    # One graph holding one step per cache, back to back (as a serving loop
-    # captures consecutive layers): no host work between steps.
-    def batch_us(sts):
-        g = capture(torch, lambda: [step_call(i, sts) for i in range(rot)])
-        t = tm.run(lambda i: g.replay(), max(1, args.steps // rot),
-                   max(1, args.warmup // rot), 1, events=False)
-        return t["mean"] / rot
-
-    t_batch = dict(mean=batch_us(steps))
-    # Warm (--warm), labelled apart: the first cache's step back to back, so
-    # that its bytes stay in the 256 MB Infinity Cache between steps.
-    t_warm = None
-    if args.warm:
-        g_warm = capture(torch, lambda: [step_call(0) for _ in range(rot)])
-        t_warm = tm.run(lambda i: g_warm.replay(), max(1, args.steps // rot),
-                        max(1, args.warmup // rot), 1, events=False)["mean"] / rot
-    # the other places the selection can run, timed the same way
+    t_batch = graph_batch(torch, step_call, rot, min_steps, warm=warm)
+    t_eager = t_graph1 = None
+    if full:                             # other ways of issuing, not the value
+        t_eager = eager_us(torch, step_call, rot, min(args.steps, 200), args.warmup)
+        t_graph1 = one_graph_us(torch, step_call, rot, min(args.steps, 200),
+                                args.warmup)
     by_select = {steps[0].select: round(t_batch["mean"], 3)}
-    for mode in ("attention", "separate"):
-        if mode in by_select:
-            continue
-        alt = [qa.SparseDecodeStep(kv, k, sm, select=mode) for _ in range(rot)]
-        for i in range(rot):
-            step_call(i, alt)
-        torch.cuda.synchronize()
-        by_select[mode] = round(batch_us(alt), 3)
-        del alt
+    if full:
+        for mode in ("attention", "separate"):
+            if mode in by_select:
+                continue
+            alt = [qa.SparseDecodeStep(kv, k, sm, select=mode) for _ in range(rot)]
+            for i in range(rot):
+                step_call(i, alt)
+            torch.cuda.synchronize()
+            by_select[mode] = round(graph_batch(torch, lambda i: step_call(i, alt),
+                                                rot, min_steps, warm=1)["mean"], 3)
+            del alt
     t_dense = None
     if with_dense:
-        dense_all = capture(torch, lambda: [dense_call(i) for i in range(rot)])
-        t_dense = tm.run(lambda i: dense_all.replay(), max(3, args.steps // (4 * rot)),
-                         1, 1, events=False)
-        t_dense = dict(mean=t_dense["mean"] / rot)
+        t_dense = graph_batch(torch, dense_call, rot, min_steps=2 * rot,
+                              min_replays=3, warm=1)
 
     def est(i):
         c, st = insts[i], steps[i]
         qa.quest_estimate(kv, c["q"], c["kmin"], c["kmax"], c["page_table"],
                           c["seq_lens"], st.scores)
+
+    def ta_splits(i):
+        c, st = insts[i], steps[i]
+        qa.quest_topk_sparse_decode_attn_splits(
+            kv, c["q"], c["k_pool"], c["v_pool"], c["page_table"], c["seq_lens"],
+            st.scores, k, 0, 0, sm, st.sel, st.out, st.workspace)
+
+    def merge(i):
+        st = steps[i]
+        qa.quest_merge_attn_splits(kv, k, st.workspace, st.out)
 
     def topk_attn(i):
         c, st = insts[i], steps[i]
@@ -361,17 +353,32 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
                                     c["page_table"], c["seq_lens"], st.sel, k,
                                     sm, st.out, st.workspace)
 
-    reps = max(10, args.steps // rot)
     mode = steps[0].select
     fits = kv.max_pages_per_seq <= qa.TOPK_ATTN_MAX_PAGES
-    us = {}
-    us["quest_estimate"] = call_us(torch, est, rot, reps)
-    us["quest_topk_pages"] = call_us(torch, topk_sep, rot, reps)
-    us["quest_sparse_decode_attn"] = call_us(torch, attn_sep, rot, reps)
-    if fits:
-        us["quest_topk_sparse_decode_attn"] = call_us(torch, topk_attn, rot, reps)
-        us["quest_topk_sparse_decode_attn_ex (2 sink + 2 local pages)"] = \
-            call_us(torch, topk_attn_forced, rot, reps)
+    ku = {}                              # per-kernel (per-call) device µs
+    ku["estimate_kernel"] = graph_batch(torch, est, rot, min_steps, warm=1)["mean"]
+    if mode == "attention":
+        ku["topk_attn_kernel"] = graph_batch(torch, ta_splits, rot, min_steps,
+                                             warm=1)["mean"]
+        ku["attn_merge_kernel"] = graph_batch(torch, merge, rot, min_steps,
+                                              warm=1)["mean"]
+    else:
+        ku["topk_kernel"] = graph_batch(torch, topk_sep, rot, min_steps, warm=1)["mean"]
+        # attn_split_kernel and its merge: one call, timed together
+        ku["attn_split_kernel+attn_merge_kernel"] = graph_batch(
+            torch, attn_sep, rot, min_steps, warm=1)["mean"]
+    other = {}
+    if full:
+        if mode == "attention":
+            other["quest_topk_pages"] = graph_batch(torch, topk_sep, rot, min_steps,
+                                                    warm=1)["mean"]
+            other["quest_sparse_decode_attn"] = graph_batch(torch, attn_sep, rot,
+                                                            min_steps, warm=1)["mean"]
+        if fits:
+            other["quest_topk_sparse_decode_attn"] = graph_batch(
+                torch, topk_attn, rot, min_steps, warm=1)["mean"]
+            other["quest_topk_sparse_decode_attn_ex (2 sink + 2 local pages)"] = \
+                graph_batch(torch, topk_attn_forced, rot, min_steps, warm=1)["mean"]
     for i in range(rot):                 # leave the plain selection in every step
         topk_sep(i)
     torch.cuda.synchronize()
@@ -382,43 +389,81 @@ def time_single_layer(args, torch, qa, synth, wls, with_dense=True, percentiles=
                         page_size=kv.page_size)
              for i in range(rot)]
     avg = {key: sum(b[key] for b in bstep) / rot for key in bstep[0]}
-    B = kv.batch
-    # per launch: what the call must read and write (its own outputs
-    # included), as the step's byte model counts them
-    score_bytes = kv.num_kv_heads * kv.max_pages_per_seq * 4 * B
-    sel_bytes = kv.num_kv_heads * k * 4 * B
-    est_bytes = avg["meta"] + avg["q"] + avg["table"] + score_bytes
-    kv_bytes = avg["kv"] + avg["q"] + avg["out"] + kv.num_kv_heads * k * 4 * B
-    nbytes = {"quest_estimate": est_bytes,
-              "quest_topk_pages": score_bytes + sel_bytes,
-              "quest_sparse_decode_attn": kv_bytes + sel_bytes,
-              "quest_topk_sparse_decode_attn": kv_bytes + score_bytes + sel_bytes}
-    step_calls = {"attention": ["quest_estimate", "quest_topk_sparse_decode_attn"],
-                  "separate": ["quest_estimate", "quest_topk_pages",
-                               "quest_sparse_decode_attn"]}[mode]
-    calls = {c: (us[c], nbytes[c]) for c in step_calls}
-    other = {c: round(v, 3) for c, v in us.items() if c not in calls}
+    kb = kernel_bytes(avg, kv, k)
     dbytes = sum(dense_bytes(l, kv.num_kv_heads, kv.num_q_heads, page_size=kv.page_size)
                  for l in lens_all) / rot
-    return dict(t_graph=t_graph, t_eager=t_eager, t_batch=t_batch, t_warm=t_warm,
-                t_dense=t_dense, bytes=avg, other_calls=other, by_select=by_select,
-                calls=calls, dense_bytes=dbytes, insts=insts, kv=kv, k_pages=k,
-                sm=sm)
+    return dict(t_batch=t_batch, t_eager=t_eager, t_graph1=t_graph1, t_dense=t_dense,
+                bytes=avg, kernel_us=ku, kernel_bytes=kb, other_us=other,
+                by_select=by_select, dense_bytes=dbytes, insts=insts, kv=kv,
+                k_pages=k, sm=sm, mode=mode)
 
 
-def roofline(calls, traffic_recorded=False):
-    """Roofline of the slowest call.  `traffic` is the recorded rocprofv3
-    HBM traffic (longchat layer only) while its sources are unchanged."""
-    dom = max(calls, key=lambda c: calls[c][0])
-    d_us, d_bytes = calls[dom]
-    achieved = d_bytes / (d_us * 1e-6) / 1e9
-    traffic = recorded_traffic(dom) if traffic_recorded else None
+def topk_attn_splits(rows, k):
+    """Workgroups per row of the Top-K + attention launch (its plan: 8 waves,
+    2 pages per wave if that still gives >= 256 workgroups, else 1)."""
+    ppw = 2 if rows * -(-k // 16) >= 256 else 1
+    return max(1, -(-k // (8 * ppw)))
+
+
+def kernel_bytes(avg, kv, k):
+    """Per kernel of the step, per launch: (algorithmic bytes, overhead
+    bytes).  Algorithmic bytes follow the step's byte model -- each page's
+    metadata, the kept pages' valid K/V, q, the output and the page-table
+    entries -- split over the kernels that must move them; the score and
+    selection round trips and the split partials are implementation
+    overhead, reported apart and not counted."""
+    B, Hq, Hkv = kv.batch, kv.num_q_heads, kv.num_kv_heads
+    scores = B * Hkv * kv.max_pages_per_seq * 4
+    sel = B * Hkv * k * 4
+    partials = B * Hq * topk_attn_splits(B * Hkv, k) * (128 + 2) * 4
+    return {
+        "estimate_kernel": (avg["meta"] + avg["q"] + avg["table"],
+                            {"scores_written": scores}),
+        "topk_attn_kernel": (avg["kv"] + avg["q"],
+                             {"scores_read": scores, "sel_written": sel,
+                              "kept_table_entries": sel, "partials_written": partials}),
+        "attn_merge_kernel": (avg["out"], {"partials_read": partials}),
+        "topk_kernel": (0, {"scores_read": scores, "sel_written": sel}),
+        "attn_split_kernel+attn_merge_kernel": (
+            avg["kv"] + avg["q"] + avg["out"],
+            {"sel_read": sel, "kept_table_entries": sel, "partials": 2 * partials}),
+    }
+
+
+def roofline(ku, kb, traffic_recorded=True):
+    """Roofline of the kernel with the most time per step: algorithmic bytes
+    per launch (the step's byte model, kernel_bytes) over its HIP-event
+    time, against the 8 TB/s HBM peak.  `traffic` is the rocprofv3 counter
+    figure recorded in profiles/ for that kernel while its sources are
+    unchanged (else null); it is not measured in this run."""
+    dom = max(ku, key=lambda n: ku[n])
+    us = ku[dom]
+    alg, over = kb[dom]
+    achieved = alg / (us * 1e-6) / 1e9
+    traffic, digest = recorded_traffic(dom) if (traffic_recorded and dom in KERNELS) \
+        else (None, None)
     return {"bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": f"{dom} [{' + '.join(CALLS[dom]['kernels'])}]",
-            "kernel_us": round(d_us, 3), "bytes_per_launch": int(d_bytes)}
+            "traffic_source": (f"recorded: {os.path.relpath(TRAFFIC_FILE, ROOT)} "
+                               f"(rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated), "
+                               f"sources digest {digest}" if traffic is not None else
+                               "null: no counter record for the current sources"),
+            "kernel": dom, "kernel_us": round(us, 3),
+            "bytes_per_launch": int(alg),
+            "overhead_bytes_per_launch": {k_: int(v) for k_, v in over.items()}}
+
+
+def protocol_note(r, rot):
+    tb = r["t_batch"]
+    return (f"value = mean µs per step over {tb['steps']} steps: {tb['replays']} "
+            f"back-to-back replays of one HIP graph holding one step on each of "
+            f"{rot} rotating caches (HIP events on the launch stream around every "
+            f"replay, untimed warm-up replays first); p10/p50/p90 over the "
+            f"replays' per-step means; every kernel and the dense baseline timed "
+            f"the same way; eager issue and one-graph-per-step are reported apart "
+            f"and are not the value")
 
 
 # ------------------------------------------------------------- workloads
@@ -428,8 +473,8 @@ def bench_longchat(args, torch, qa, synth):
     wls = [synth.longchat_layer_workload(seed=base.base_seed + 1000 * i)
            for i in range(args.rotate)]
     r = time_single_layer(args, torch, qa, synth, wls, with_dense=not args.no_dense)
-    tg, te, tb = r["t_graph"], r["t_eager"], r["t_batch"]
-    us = min(tg["mean"], te["mean"], tb["mean"])
+    tb = r["t_batch"]
+    us = tb["mean"]
     gbps = r["bytes"]["total"] / (us * 1e-6) / 1e9
     us_dense = r["t_dense"]["mean"] if r["t_dense"] else float("nan")
     ceiling = None if args.no_ceiling else stream_read_ceiling(torch, qa)
@@ -444,6 +489,9 @@ def bench_longchat(args, torch, qa, synth):
                    "q_heads": 32, "kv_heads": 32, "head_dim": 128,
                    "page_size": 16, "ctx": 32768, "budget_tokens": 2048,
                    "rotating_caches": args.rotate},
+        "timed_steps": tb["steps"],
+        "step_us_p10_p50_p90": [round(tb[p], 3) for p in ("p10", "p50", "p90")],
+        "wall_us_per_step": round(tb["wall"], 3),
         "effective_GBps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "stream_read_GBps": ceiling,
@@ -452,94 +500,100 @@ def bench_longchat(args, torch, qa, synth):
         "dense_us_per_step": round(us_dense, 3),
         "speedup_vs_dense": round(us_dense / us, 3),
         "dense_effective_GBps": round(r["dense_bytes"] / (us_dense * 1e-6) / 1e9, 1),
-        "timing": "value = the fastest of eager issue (the calls from Python "
-                  "through ctypes), one HIP graph per step, and one HIP graph "
-                  f"holding a step on each of the {args.rotate} rotating caches "
-                  "back to back (wall clock / steps); the dense baseline is "
-                  "timed the last way; percentiles from HIP events around each "
-                  "one-step graph replay; warm_* (with --warm) repeats one "
-                  "cache's step back to back (its bytes stay in the Infinity "
-                  "Cache), not the value",
-        "eager_us_per_step": round(te["mean"], 3),
-        "graph_us_per_step": round(tg["mean"], 3),
-        "graph_batch_us_per_step": round(tb["mean"], 3),
-        "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
-        "warm_graph_batch_us_per_step": None if r["t_warm"] is None else round(r["t_warm"], 3),
+        "timing": protocol_note(r, args.rotate),
+        "eager_us_per_step": round(r["t_eager"], 3),
+        "one_graph_per_step_us": round(r["t_graph1"], 3),
         "step_us_by_select": r["by_select"],
-        "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
-        "other_call_us": r["other_calls"],
-        "roofline": roofline(r["calls"], traffic_recorded=True),
+        "kernel_us": {n: round(v, 3) for n, v in r["kernel_us"].items()},
+        "other_call_us": {n: round(v, 3) for n, v in r["other_us"].items()},
+        "roofline": roofline(r["kernel_us"], r["kernel_bytes"]),
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds)
-        if args.cpu_all_cores:
+        if not args.no_cpu_all_cores:
             line["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(r, args.cpu_seconds)
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        line["extra"] = extra_workloads(args, torch, qa, synth)
     return line
 
 
-def bench_ragged(args, torch, qa, synth):
+def single_layer_line(r, rot):
+    """The figures every single-layer workload reports."""
+    tb = r["t_batch"]
+    us = tb["mean"]
+    us_dense = r["t_dense"]["mean"] if r["t_dense"] else None
+    d = {"us_per_step": round(us, 3),
+         "step_us_p10_p50_p90": [round(tb[p], 3) for p in ("p10", "p50", "p90")],
+         "timed_steps": tb["steps"], "rotating_caches": rot,
+         "bytes_per_step": int(r["bytes"]["total"]),
+         "effective_GBps": round(r["bytes"]["total"] / (us * 1e-6) / 1e9, 1),
+         "hbm_frac": round(r["bytes"]["total"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+         "kernel_us": {n: round(v, 3) for n, v in r["kernel_us"].items()},
+         "roofline": roofline(r["kernel_us"], r["kernel_bytes"])}
+    if us_dense:
+        d.update(dense_us_per_step=round(us_dense, 3),
+                 speedup_vs_dense=round(us_dense / us, 3),
+                 dense_effective_GBps=round(r["dense_bytes"] / (us_dense * 1e-6) / 1e9, 1))
+    return d
+
+
+def bench_ragged(args, torch, qa, synth, full=True):
     wl = synth.ragged_batch_workload()
-    r = time_single_layer(args, torch, qa, synth, [wl], with_dense=not args.no_dense)
-    tg, te, tb = r["t_graph"], r["t_eager"], r["t_batch"]
-    us = min(tg["mean"], te["mean"], tb["mean"])
-    gbps = r["bytes"]["total"] / (us * 1e-6) / 1e9
-    us_dense = r["t_dense"]["mean"] if r["t_dense"] else float("nan")
+    r = time_single_layer(args, torch, qa, synth, [wl],
+                          with_dense=not args.no_dense and full, full=full)
+    d = single_layer_line(r, 1)
+    d["config"] = {"workload": "ragged_batch_decode", "batch": wl.batch,
+                   "q_heads": 32, "kv_heads": 32, "ctx_min": min(wl.seq_lens),
+                   "ctx_max": max(wl.seq_lens), "budget_tokens": 2048,
+                   "dtype": "bf16", "select": r["mode"]}
+    if not full:
+        return d
+    us = d["us_per_step"]
     line = {
         "metric": "µs/decode step + effective HBM GB/s, batched ragged",
-        "value": round(us, 3), "unit": "us/step", "n_gpus": 1,
+        "value": us, "unit": "us/step", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 K/V/q; pool pages permuted)",
-        "config": {"workload": "ragged_batch_decode", "batch": wl.batch,
-                   "q_heads": 32, "kv_heads": 32, "ctx_min": min(wl.seq_lens),
-                   "ctx_max": max(wl.seq_lens), "budget_tokens": 2048},
-        "effective_GBps": round(gbps, 1),
-        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "bytes_per_step": int(r["bytes"]["total"]),
-        "dense_us_per_step": round(us_dense, 3),
-        "speedup_vs_dense": round(us_dense / us, 3),
-        "dense_effective_GBps": round(r["dense_bytes"] / (us_dense * 1e-6) / 1e9, 1),
-        "eager_us_per_step": round(te["mean"], 3),
-        "graph_us_per_step": round(tg["mean"], 3),
-        "graph_batch_us_per_step": round(tb["mean"], 3),
-        "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
+        "config": d.pop("config"),
+        "timing": protocol_note(r, 1) + " (one cache: its 1.6 GiB of touched "
+                  "bytes far exceed the Infinity Cache)",
+        "eager_us_per_step": round(r["t_eager"], 3),
+        "one_graph_per_step_us": round(r["t_graph1"], 3),
         "step_us_by_select": r["by_select"],
-        "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
-        "roofline": roofline(r["calls"]),
-        "gpu": torch.cuda.get_device_name(0),
-    }
+        "other_call_us": {n: round(v, 3) for n, v in r["other_us"].items()},
+        "gpu": torch.cuda.get_device_name(0)}
+    line.update(d)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline_ragged(r, args.cpu_seconds)
     return line
+
+
+def sweep_point(args, torch, qa, synth, ctx, budget, full=True):
+    # enough independent caches that the bytes one pass over them touches
+    # (metadata + selected pages) exceed the Infinity Cache
+    touched_mib = ctx / 1024 + min(budget, ctx) / 64
+    rot = min(64, max(2, math.ceil(768 / touched_mib)))
+    wls = [synth.sweep_workload(ctx, budget, seed=2 + 1000 * i) for i in range(rot)]
+    r = time_single_layer(args, torch, qa, synth, wls,
+                          with_dense=not args.no_dense, full=False)
+    d = single_layer_line(r, rot)
+    d.update(ctx=ctx, budget=budget)
+    del r
+    torch.cuda.empty_cache()
+    return d
 
 
 def bench_sweep(args, torch, qa, synth):
     points = []
     for ctx in synth.SWEEP_CTX:
         for budget in synth.SWEEP_BUDGET:
-            # enough independent caches that the bytes one pass over them
-            # touches (metadata + selected pages) exceed the Infinity Cache
-            touched_mib = ctx / 1024 + min(budget, ctx) / 64
-            rot = min(64, max(2, math.ceil(768 / touched_mib)))
-            wls = [synth.sweep_workload(ctx, budget, seed=2 + 1000 * i)
-                   for i in range(rot)]
-            r = time_single_layer(args, torch, qa, synth, wls,
-                                  with_dense=not args.no_dense, percentiles=False)
-            us = min(r["t_graph"]["mean"], r["t_eager"]["mean"], r["t_batch"]["mean"])
-            us_dense = r["t_dense"]["mean"] if r["t_dense"] else float("nan")
-            points.append({
-                "ctx": ctx, "budget": budget, "us_per_step": round(us, 3),
-                "effective_GBps": round(r["bytes"]["total"] / (us * 1e-6) / 1e9, 1),
-                "dense_us": round(us_dense, 3),
-                "speedup_vs_dense": round(us_dense / us, 3),
-                "call_us": {c: round(v[0], 3) for c, v in r["calls"].items()},
-                "other_call_us": r["other_calls"],
-                "roofline": roofline(r["calls"])})
+            points.append(sweep_point(args, torch, qa, synth, ctx, budget))
             print(json.dumps({"progress": points[-1]}), file=sys.stderr, flush=True)
-            del r
-            torch.cuda.empty_cache()
     at = [p for p in points if p["ctx"] == 32768 and p["budget"] == 2048][0]
     return {
         "metric": "µs/decode step over context x budget, 32 heads",
@@ -551,11 +605,13 @@ def bench_sweep(args, torch, qa, synth):
         "config": {"workload": "ctx_budget_sweep", "ctx": list(synth.SWEEP_CTX),
                    "budget_tokens": list(synth.SWEEP_BUDGET),
                    "value_at": "ctx 32768, budget 2048"},
+        "timing": "each point as the headline: back-to-back replays of one HIP "
+                  "graph over its rotating caches, >= 100 steps",
         "roofline": at["roofline"],
         "points": points, "gpu": torch.cuda.get_device_name(0)}
 
 
-def bench_gqa_multistep(args, torch, qa, synth):
+def bench_gqa_multistep(args, torch, qa, synth, full=True):
     wl = synth.gqa_multistep_workload()
     dev = "cuda"
     sm = 1.0 / math.sqrt(128)
@@ -600,17 +656,29 @@ def bench_gqa_multistep(args, torch, qa, synth):
     for s in range(min(args.warmup, nsteps)):
         one_step(s)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(nsteps):
-        one_step(s)
-    torch.cuda.synchronize()
-    us_eager = (time.perf_counter() - t0) / nsteps * 1e6
+    us_eager = None
+    if full:
+        t0 = time.perf_counter()
+        for s in range(nsteps):
+            one_step(s)
+        torch.cuda.synchronize()
+        us_eager = (time.perf_counter() - t0) / nsteps * 1e6
+    # the protocol: one graph per 32-layer step (128 of them, each appending
+    # its own token), replayed back to back in step order, events around each
     graphs = [capture(torch, lambda s=s: one_step(s)) for s in range(nsteps)]
+    for s in range(min(args.warmup, nsteps)):
+        graphs[s].replay()
     torch.cuda.synchronize()
-    tm = Timer(torch)
-    tg = tm.run(lambda s: graphs[s].replay(), nsteps, min(args.warmup, nsteps),
-                nsteps)
-    us = min(us_eager, tg["mean"])
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
+    ev[0].record(stream)
+    for s in range(nsteps):
+        graphs[s].replay()
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[s].elapsed_time(ev[s + 1]) * 1e3 for s in range(nsteps)]
+    us = ev[0].elapsed_time(ev[nsteps]) * 1e3 / nsteps
+    del graphs
 
     # bytes per step (final lengths, selections of the last replayed step)
     B = 1
@@ -623,14 +691,14 @@ def bench_gqa_multistep(args, torch, qa, synth):
     total = sparse_b + dense_b + app_b
     all_dense = wl.layers * dense_bytes([L0 + nsteps], 8, 32) + app_b
 
-    # the layers' calls at the last step, one by one (a graph of one call
-    # per layer, back to back, so that each reads its bytes from HBM); the
-    # roofline is that of the call with the most time per 32-layer step
+    # the layers' kernels at the last step, one by one: a graph of one call
+    # per layer over every sparse (or dense) layer, back to back, so that
+    # each reads its bytes from HBM (30 sparse layers: 0.5 GB); the roofline
+    # is that of the kernel with the most time per 32-layer step
     s_l = nsteps - 1
-    sparse_l = layers[wl.dense_layers:wl.dense_layers + 8]
+    sparse_l = layers[wl.dense_layers:]
     dense_l = layers[:wl.dense_layers]
     Lf = L0 + nsteps
-    mp = sparse_l[0]["kv"].max_pages_per_seq
 
     def ae(i):
         sp = sparse_l[i]
@@ -642,9 +710,13 @@ def bench_gqa_multistep(args, torch, qa, synth):
     def ta(i):
         sp = sparse_l[i]
         c, st = sp["c"], sp["step"]
-        qa.quest_topk_sparse_decode_attn(sp["kv"], sp["q"][s_l], c["k_pool"], c["v_pool"],
-                                         c["page_table"], lens[s_l], st.scores, k, sm,
-                                         st.sel, st.out, st.workspace)
+        qa.quest_topk_sparse_decode_attn_splits(
+            sp["kv"], sp["q"][s_l], c["k_pool"], c["v_pool"], c["page_table"],
+            lens[s_l], st.scores, k, 0, 0, sm, st.sel, st.out, st.workspace)
+
+    def mg(i):
+        sp = sparse_l[i]
+        qa.quest_merge_attn_splits(sp["kv"], k, sp["step"].workspace, sp["step"].out)
 
     def da(i):
         de = dense_l[i]
@@ -652,46 +724,57 @@ def bench_gqa_multistep(args, torch, qa, synth):
         qa.quest_decode_attn(de["kv"], de["q"][s_l], c["k_pool"], c["v_pool"],
                              c["page_table"], lens[s_l], sm, d_.out, d_.workspace)
 
-    reps = max(10, args.steps // 8)
-    t_calls = {"quest_append_estimate": call_us(torch, ae, len(sparse_l), reps),
-               "quest_topk_sparse_decode_attn": call_us(torch, ta, len(sparse_l), reps),
-               "quest_decode_attn": call_us(torch, da, len(dense_l), reps)}
+    ns = len(sparse_l)
+    ku = {"estimate_kernel (append)": graph_batch(torch, ae, ns, 100, warm=1)["mean"],
+          "topk_attn_kernel": graph_batch(torch, ta, ns, 100, warm=1)["mean"],
+          "attn_merge_kernel": graph_batch(torch, mg, ns, 100, warm=1)["mean"],
+          "attn_split_kernel+attn_merge_kernel (dense)":
+              graph_batch(torch, da, len(dense_l), 20, min_replays=5, warm=1)["mean"]}
     sb = step_bytes([Lf], 8, 32, k, sel=sparse_l[0]["step"].sel.cpu().numpy())
-    b_calls = {
-        "quest_append_estimate": sb["meta"] + sb["q"] + sb["table"] + 8 * mp * 4 +
-                                 append_bytes(1, 8),
-        "quest_topk_sparse_decode_attn": sb["kv"] + sb["q"] + sb["out"] + 8 * mp * 4 +
-                                         8 * k * 4,
-        "quest_decode_attn": dense_bytes([Lf], 8, 32)}
-    per_step = {"quest_append_estimate": wl.layers - wl.dense_layers,
-                "quest_topk_sparse_decode_attn": wl.layers - wl.dense_layers,
-                "quest_decode_attn": wl.dense_layers}
-    dom = max(t_calls, key=lambda c_: t_calls[c_] * per_step[c_])
+    mp = sparse_l[0]["kv"].max_pages_per_seq
+    kb = kernel_bytes(sb, sparse_l[0]["kv"], k)
+    kb["estimate_kernel (append)"] = (sb["meta"] + sb["q"] + sb["table"] + append_bytes(1, 8),
+                                      {"scores_written": 8 * mp * 4})
+    kb["attn_split_kernel+attn_merge_kernel (dense)"] = (dense_bytes([Lf], 8, 32), {})
+    per_step = {"estimate_kernel (append)": wl.layers - wl.dense_layers,
+                "topk_attn_kernel": wl.layers - wl.dense_layers,
+                "attn_merge_kernel": wl.layers - wl.dense_layers,
+                "attn_split_kernel+attn_merge_kernel (dense)": wl.dense_layers}
+    dom = max(ku, key=lambda c_: ku[c_] * per_step[c_])
+    rl = roofline({dom: ku[dom]}, {dom: kb[dom]}, traffic_recorded=False)
+    d = {"us_per_step": round(us, 3),
+         "step_us_p10_p50_p90": [round(pct(per, q_), 3) for q_ in (10, 50, 90)],
+         "timed_steps": nsteps,
+         "bytes_per_step": int(total),
+         "effective_GBps": round(total / (us * 1e-6) / 1e9, 1),
+         "hbm_frac": round(total / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+         "all_dense_bytes_per_step": int(all_dense),
+         "launches_per_step": wl.dense_layers * 3 + (wl.layers - wl.dense_layers) * 3,
+         "layer_kernel_us": {c_: round(v, 3) for c_, v in ku.items()},
+         "roofline": rl,
+         "config": {"workload": "gqa_multistep_decode", "layers": wl.layers,
+                    "q_heads": 32, "kv_heads": 8, "ctx_start": L0,
+                    "appended_steps": nsteps, "budget_tokens": wl.budget_tokens,
+                    "dense_layers": wl.dense_layers}}
+    if not full:
+        return d
     line = {
         "metric": "µs per 32-layer decode step, GQA 32/8, 32K ctx, "
                   "2048-token budget, layers 0-1 dense",
-        "value": round(us, 3), "unit": "us/step", "n_gpus": 1,
+        "value": d["us_per_step"], "unit": "us/step", "n_gpus": 1,
         "steps": nsteps, "warmup": min(args.warmup, nsteps),
         "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded N(0,1) fp16, 4 outlier channels x8 per "
                 "(layer, kv-head); one appended token per layer per step)",
-        "config": {"workload": "gqa_multistep_decode", "layers": wl.layers,
-                   "q_heads": 32, "kv_heads": 8, "ctx_start": L0,
-                   "appended_steps": nsteps, "budget_tokens": wl.budget_tokens,
-                   "dense_layers": wl.dense_layers},
-        "effective_GBps": round(total / (us * 1e-6) / 1e9, 1),
-        "hbm_frac": round(total / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-        "bytes_per_step": int(total),
-        "all_dense_bytes_per_step": int(all_dense),
+        "timing": "value = mean µs per 32-layer step over the 128 appended "
+                  "steps: one HIP graph per step, replayed back to back in step "
+                  "order, HIP events around each replay; eager issue reported "
+                  "apart",
         "eager_us_per_step": round(us_eager, 3),
-        "graph_us_per_step": round(tg["mean"], 3),
-        "graph_step_us_p10_p50_p90": [round(tg[p], 3) for p in ("p10", "p50", "p90")],
-        "launches_per_step": wl.dense_layers * 3 + (wl.layers - wl.dense_layers) * 3,
-        "layer_call_us": {c_: round(v, 3) for c_, v in t_calls.items()},
-        "roofline": roofline({dom: (t_calls[dom], b_calls[dom])}),
         "gpu": torch.cuda.get_device_name(0),
     }
+    line.update(d)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline_multistep(layers, wl, args.cpu_seconds)
     return line
@@ -722,15 +805,14 @@ def bench_gqa_union(args, torch, qa, synth):
         for i in range(rot):
             call(steps, i)
         torch.cuda.synchronize()
-        g = capture(torch, lambda steps=steps: [call(steps, i) for i in range(rot)])
-        t = Timer(torch).run(lambda i: g.replay(), max(2, args.steps // rot), 2, 1,
-                             events=False)
+        t = graph_batch(torch, lambda i, steps=steps: call(steps, i), rot,
+                        max(100, args.steps), warm=1)
         lens = [int(x) for x in insts[0]["seq_lens"].cpu()]
         b = [step_bytes(lens, kv.num_kv_heads, kv.num_q_heads, k,
                         sel=steps[i].sel.cpu().numpy())["total"] for i in range(rot)]
         kept = [float((steps[i].sel >= 0).sum()) / (kv.batch * kv.num_kv_heads)
                 for i in range(rot)]
-        res[name] = dict(us=t["mean"] / rot, bytes=sum(b) / rot,
+        res[name] = dict(us=t["mean"], bytes=sum(b) / rot,
                          pages=sum(kept) / rot)
     u, sm_ = res["union"], res["sum"]
 
@@ -755,19 +837,26 @@ def bench_gqa_union(args, torch, qa, synth):
                                     c["page_table"], c["seq_lens"], st.sel, G * k,
                                     sm, st.out, st.workspace)
 
-    reps = max(10, args.steps // rot)
-    t_calls = {name: call_us(torch, f, rot, reps) for name, f in (
+    t_calls = {name: graph_batch(torch, f, rot, 100, warm=1)["mean"] for name, f in (
         ("quest_estimate_heads", e_heads), ("quest_topk_pages", tk_heads),
         ("quest_union_pages", un), ("quest_sparse_decode_attn", att))}
     lens = [int(x) for x in insts[0]["seq_lens"].cpu()]
     Hq, Hkv, mp = kv.num_q_heads, kv.num_kv_heads, kv.max_pages_per_seq
     sb = step_bytes(lens, Hkv, Hq, k, sel=unions[0].sel.cpu().numpy())
+    # per call (one kernel each, but the attention call: split + merge)
+    names = {"quest_estimate_heads": "estimate_kernel (per head)",
+             "quest_topk_pages": "topk_kernel",
+             "quest_union_pages": "union_kernel",
+             "quest_sparse_decode_attn": "attn_split_kernel+attn_merge_kernel"}
     b_calls = {
-        "quest_estimate_heads": sb["meta"] + sb["q"] + sb["table"] + Hq * mp * 4,
-        "quest_topk_pages": Hq * mp * 4 + Hq * k * 4,
-        "quest_union_pages": Hq * k * 4 + Hkv * G * k * 4,
-        "quest_sparse_decode_attn": sb["kv"] + sb["q"] + sb["out"] + Hkv * G * k * 4}
-    calls = {c_: (t_calls[c_], b_calls[c_]) for c_ in t_calls}
+        "quest_estimate_heads": (sb["meta"] + sb["q"] + sb["table"],
+                                 {"scores_written": Hq * mp * 4}),
+        "quest_topk_pages": (0, {"scores_read": Hq * mp * 4, "sel_written": Hq * k * 4}),
+        "quest_union_pages": (0, {"sel_read": Hq * k * 4, "union_written": Hkv * G * k * 4}),
+        "quest_sparse_decode_attn": (sb["kv"] + sb["q"] + sb["out"],
+                                     {"sel_read": Hkv * G * k * 4})}
+    ku = {names[c_]: t_calls[c_] for c_ in t_calls}
+    kb = {names[c_]: b_calls[c_] for c_ in b_calls}
     return {
         "metric": "µs/decode step, GQA 32/8 layer, per-head Top-K + union vs "
                   "group-sum Top-K",
@@ -787,8 +876,8 @@ def bench_gqa_union(args, torch, qa, synth):
                       "effective_GBps": round(sm_["bytes"] / (sm_["us"] * 1e-6) / 1e9, 1),
                       "pages_per_kv_head": round(sm_["pages"], 1)},
         "union_pages_over_k": round(u["pages"] / k, 3),
-        "union_call_us": {c_: round(v[0], 3) for c_, v in calls.items()},
-        "roofline": roofline(calls),
+        "union_call_us": {c_: round(v, 3) for c_, v in t_calls.items()},
+        "roofline": roofline(ku, kb, traffic_recorded=False),
         "group": G, "gpu": torch.cuda.get_device_name(0)}
 
 
@@ -807,8 +896,8 @@ def bench_page32(args, torch, qa, synth):
                                        page_size=S, name=f"p{S}_ctx{ctx}")
                    for i in range(rot)]
             r = time_single_layer(args, torch, qa, synth, wls,
-                                  with_dense=not args.no_dense, percentiles=False)
-            us = min(r["t_graph"]["mean"], r["t_eager"]["mean"], r["t_batch"]["mean"])
+                                  with_dense=not args.no_dense, full=False)
+            us = r["t_batch"]["mean"]
             c, kv = r["insts"][0], r["kv"]
             # prefill: rebuild every box of the prompt vs writing its K once
             kmin, kmax = qa.alloc_meta(kv)
@@ -840,8 +929,8 @@ def bench_page32(args, torch, qa, synth):
                 "effective_GBps": round(r["bytes"]["total"] / (us * 1e-6) / 1e9, 1),
                 "meta_bytes_per_step": int(r["bytes"]["meta"]),
                 "dense_us": round(r["t_dense"]["mean"], 3) if r["t_dense"] else None,
-                "call_us": {k_: round(v[0], 3) for k_, v in r["calls"].items()},
-                "roofline": roofline(r["calls"]),
+                "kernel_us": {k_: round(v, 3) for k_, v in r["kernel_us"].items()},
+                "roofline": roofline(r["kernel_us"], r["kernel_bytes"]),
                 "prefill_meta_build_us": round(meta_us, 2),
                 "prefill_meta_GBps": round(meta_bytes / (meta_us * 1e-6) / 1e9, 1),
                 "prefill_k_write_us": round(kwrite_us, 2),
@@ -897,12 +986,8 @@ def bench_host_kv(args, torch, qa, synth):
         step_call(i)
         dense_call(i)
     torch.cuda.synchronize()
-    g_step = capture(torch, lambda: [step_call(i) for i in range(rot)])
-    g_dense = capture(torch, lambda: [dense_call(i) for i in range(rot)])
-    tm = Timer(torch)
-    us = tm.run(lambda i: g_step.replay(), max(2, args.steps // (4 * rot)), 2, 1,
-                events=False)["mean"] / rot
-    us_dense = tm.run(lambda i: g_dense.replay(), 3, 1, 1, events=False)["mean"] / rot
+    us = graph_batch(torch, step_call, rot, 10, min_replays=3, warm=1)["mean"]
+    us_dense = graph_batch(torch, dense_call, rot, 2, min_replays=2, warm=1)["mean"]
     lens = [int(x) for x in insts[0]["seq_lens"].cpu()]
     b = step_bytes(lens, kv.num_kv_heads, kv.num_q_heads, k,
                    sel=steps[0].sel.cpu().numpy())
@@ -950,6 +1035,26 @@ def bench_host_kv(args, torch, qa, synth):
         "gpu": torch.cuda.get_device_name(0)}
 
 
+def extra_workloads(args, torch, qa, synth):
+    """The other workloads of the pages at their real sizes, each timed by
+    the same protocol (no CPU leg): the ragged batch, the 32-layer GQA step
+    and two sweep points.  Each carries its bytes and its roofline."""
+    ex = {}
+    for name, fn in (
+            ("sweep_32k_2048", lambda: sweep_point(args, torch, qa, synth, 32768, 2048)),
+            ("sweep_128k_256", lambda: sweep_point(args, torch, qa, synth, 131072, 256)),
+            ("ragged_batch", lambda: bench_ragged(args, torch, qa, synth, full=False)),
+            ("gqa_multistep", lambda: bench_gqa_multistep(args, torch, qa, synth,
+                                                          full=False))):
+        t0 = time.perf_counter()
+        ex[name] = fn()
+        ex[name]["bench_seconds"] = round(time.perf_counter() - t0, 1)
+        print(json.dumps({"progress": name, "us_per_step": ex[name]["us_per_step"]}),
+              file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    return ex
+
+
 # ------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(gpu, budget_s):
@@ -982,7 +1087,7 @@ def cpu_baseline(gpu, budget_s):
                 break
     per_step_us = el / reps * (gpu["kv"].num_q_heads / len(heads)) * 1e6
     return {"value": round(per_step_us, 1), "unit": "us/step", "cores": 1,
-            "kind": "oracle",
+            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": (f"{reps} oracle decode steps over {len(heads)} of 32 heads "
                        f"of one 32K-context layer (estimate + Top-K + sparse "
                        f"attention, float64, 1 thread), {el:.1f} s, scaled x"
@@ -1199,11 +1304,10 @@ def pmc_summary(d, copy_mib):
         b = (fetch[k] * f_scale + write[k] * w_scale) * 1024
         per_kernel[k] = b
         out.append(f"| {k} | {nf[k]} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.0f} |")
-    calls = ["", "| call | HBM bytes per launch | sources digest |", "|---|---|---|"]
-    for call, spec in CALLS.items():
-        if all(k in per_kernel for k in spec["kernels"]):
-            b = sum(per_kernel[k] for k in spec["kernels"])
-            calls.append(f"| {call} | {b:.0f} | {sources_digest(spec['sources'])} |")
+    calls = ["", "| kernel | HBM bytes per launch | sources digest |", "|---|---|---|"]
+    for kern, srcs in KERNELS.items():
+        if kern in per_kernel:
+            calls.append(f"| {kern} | {per_kernel[kern]:.0f} | {sources_digest(srcs)} |")
     head = [f"Copy calibration ({copy_mib} MiB read + {copy_mib} MiB written "
             f"by one device copy): FETCH_SIZE reads {cfetch['copy']:.1f} KiB "
             f"(scale x{f_scale:.4f}), WRITE_SIZE {cwrite['copy']:.1f} KiB "
@@ -1222,16 +1326,17 @@ def main():
     ap.add_argument("--select", default="auto",
                     choices=["auto", "attention", "separate"],
                     help="where the sparse step runs its Top-K (SparseDecodeStep)")
-    ap.add_argument("--rotate", type=int, default=8,
-                    help="independent caches the steps cycle through")
+    ap.add_argument("--rotate", type=int, default=16,
+                    help="independent caches the steps cycle through (16: "
+                         "1 GiB of touched bytes per pass, 4x the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--warm", action="store_true",
-                    help="also time one cache's step back to back (bytes held "
-                         "in the Infinity Cache), reported apart from the value")
-    ap.add_argument("--cpu-all-cores", action="store_true",
-                    help="also time the oracle on every kv-head with one "
+    ap.add_argument("--no-cpu-all-cores", action="store_true",
+                    help="skip the oracle timed on every kv-head with one "
                          "process per host core (headline workload)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="headline only: skip the ragged batch, the 32-layer "
+                         "GQA step and the sweep points")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

@@ -261,6 +261,39 @@ QUEST_API quest_status quest_topk_sparse_decode_attn_ex(
     size_t workspace_bytes, void* stream);
 
 /*
+ * quest_topk_sparse_decode_attn_ex in its two launches, for callers that
+ * time them apart or put other work between them.  This call is the first:
+ * the same Top-K and attention (sel_pages bit for bit as _ex), stopping
+ * before the split merge -- each workgroup's partial result (running max,
+ * softmax denominator, unnormalised output) stays in `workspace`, except
+ * when the plan has a single split per row, in which case `out` is written
+ * here directly.  quest_merge_attn_splits with the same kv, k_pages and
+ * workspace then completes `out` ([Q] Summary, exact attention: the online
+ * softmax merge is the last step of the same sum).  Arguments, limits and
+ * errors as quest_topk_sparse_decode_attn_ex; the workspace must not be
+ * reused between the two calls.
+ */
+QUEST_API quest_status quest_topk_sparse_decode_attn_splits(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const float* scores, int32_t k_pages, int32_t n_sink, int32_t n_local,
+    float sm_scale, int32_t* sel_pages, float* out, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/*
+ * The second launch of quest_topk_sparse_decode_attn_ex: merges the split
+ * partials that quest_topk_sparse_decode_attn_splits left in `workspace`
+ * (same kv and k_pages) into out [batch][Hq][128] (float32); does nothing
+ * when that plan has a single split (out is already written).  Same
+ * workspace size rule; k_pages and max_pages_per_seq <= 8192.
+ */
+QUEST_API quest_status quest_merge_attn_splits(const quest_paged_kv* kv,
+                                               int32_t k_pages,
+                                               const void* workspace,
+                                               size_t workspace_bytes,
+                                               float* out, void* stream);
+
+/*
  * Dense decode attention over all L_b tokens (the in-library baseline).
  * "The Memory Bandwidth Bottleneck of Long-Context Decoding" in [G]:
  *   out[b][h] = softmax(sm_scale * q K^T) V over every token of request b.

@@ -324,13 +324,12 @@ QUEST_API quest_status quest_sparse_decode_attn(
                        stream, fn);
 }
 
-QUEST_API quest_status quest_topk_sparse_decode_attn_ex(
+static quest_status run_topk_attention(
     const quest_paged_kv* kv, const void* q, const void* k_pool,
     const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
     const float* scores, int32_t k_pages, int32_t n_sink, int32_t n_local,
     float sm_scale, int32_t* sel_pages, float* out, void* workspace,
-    size_t workspace_bytes, void* stream) {
-  const char* fn = "quest_topk_sparse_decode_attn_ex";
+    size_t workspace_bytes, void* stream, bool merge, const char* fn) {
   quest_status s = check_attention_common(kv, q, k_pool, v_pool, page_table,
                                           seq_lens, sm_scale, out, fn);
   if (s != QUEST_OK) return s;
@@ -351,7 +350,60 @@ QUEST_API quest_status quest_topk_sparse_decode_attn_ex(
   return hip_status(quest::launch_topk_attention(
                         *kv, q, k_pool, v_pool, page_table, seq_lens, scores,
                         k_pages, n_sink, n_local, sm_scale, sel_pages, out,
-                        workspace, static_cast<hipStream_t>(stream)),
+                        workspace, static_cast<hipStream_t>(stream), merge),
+                    fn);
+}
+
+QUEST_API quest_status quest_topk_sparse_decode_attn_ex(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const float* scores, int32_t k_pages, int32_t n_sink, int32_t n_local,
+    float sm_scale, int32_t* sel_pages, float* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return run_topk_attention(kv, q, k_pool, v_pool, page_table, seq_lens, scores,
+                            k_pages, n_sink, n_local, sm_scale, sel_pages, out,
+                            workspace, workspace_bytes, stream, true,
+                            "quest_topk_sparse_decode_attn_ex");
+}
+
+QUEST_API quest_status quest_topk_sparse_decode_attn_splits(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const float* scores, int32_t k_pages, int32_t n_sink, int32_t n_local,
+    float sm_scale, int32_t* sel_pages, float* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return run_topk_attention(kv, q, k_pool, v_pool, page_table, seq_lens, scores,
+                            k_pages, n_sink, n_local, sm_scale, sel_pages, out,
+                            workspace, workspace_bytes, stream, false,
+                            "quest_topk_sparse_decode_attn_splits");
+}
+
+QUEST_API quest_status quest_merge_attn_splits(const quest_paged_kv* kv,
+                                               int32_t k_pages,
+                                               const void* workspace,
+                                               size_t workspace_bytes,
+                                               float* out, void* stream) {
+  const char* fn = "quest_merge_attn_splits";
+  quest_status s = check_kv(kv, fn);
+  if (s != QUEST_OK) return s;
+  if ((s = check_group(kv, fn)) != QUEST_OK) return s;
+  REQUIRE_PTR(out, aligned4(out));
+  if (k_pages < 1)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  if (kv->max_pages_per_seq > quest::kTopkAttnMaxPages || k_pages > quest::kTopkAttnMaxPages)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: max_pages_per_seq and k_pages must be <= %d",
+                fn, quest::kTopkAttnMaxPages);
+  const size_t need = quest::attention_workspace_bytes(*kv, k_pages);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(QUEST_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu",
+                  fn, need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (!aligned16(workspace))
+      return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: `workspace` is misaligned", fn);
+  }
+  return hip_status(quest::launch_topk_attention_merge(
+                        *kv, k_pages, const_cast<void*>(workspace), out,
+                        static_cast<hipStream_t>(stream)),
                     fn);
 }
 

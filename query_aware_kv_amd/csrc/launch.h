@@ -73,13 +73,20 @@ constexpr int kTopkAttnMaxPages = 8192;
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink,
                              hipStream_t stream);
 
+// merge = false: leave the split partials in the workspace (out is written
+// only when the plan has a single split); launch_topk_attention_merge then
+// combines them.
 hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
                                  const void* k_pool, const void* v_pool,
                                  const int32_t* page_table,
                                  const int32_t* seq_lens, const float* scores,
                                  int k_pages, int n_sink, int n_local,
                                  float sm_scale, int32_t* sel, float* out,
-                                 void* workspace, hipStream_t stream);
+                                 void* workspace, hipStream_t stream,
+                                 bool merge = true);
+hipError_t launch_topk_attention_merge(const quest_paged_kv& kv, int k_pages,
+                                       void* workspace, float* out,
+                                       hipStream_t stream);
 
 // Fused step (estimate -> Top-K -> attention in one launch).
 constexpr int kStepMaxPages = 8192;

@@ -264,6 +264,9 @@ step_kernel(StepArgs a) {
     if (left == gridDim.x - 1) {  // last one out: ready the queue for the next call
       a.ctrl->ticket = 0;
       a.ctrl->exited = 0;
+      // a stalled wait of this call must not cut short the waits of the
+      // next one: every wait ends at once while `stalls` is non-zero
+      a.ctrl->stalls = 0;
     }
   }
 }

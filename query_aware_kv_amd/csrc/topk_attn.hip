@@ -206,21 +206,50 @@ void dispatch_g(int G, int ppw, const quest_paged_kv& kv, const void* q,
 
 }  // namespace
 
+namespace {
+
+// The 8-wave plan, and where its partials live in the caller's workspace.
+struct TaLayout {
+  AttnPlan pl;
+  float* ws_o;
+  float* ws_ml;
+};
+
+bool ta_layout(const quest_paged_kv& kv, int k_pages, void* workspace, TaLayout& t) {
+  t.pl = attention_plan(kv, k_pages, kTaWaves);
+  // the caller's workspace holds the partials of the 4-wave plan, which
+  // never has fewer splits (see attention_plan); refuse rather than overrun
+  if (t.pl.nsplit > attention_plan(kv, k_pages).nsplit) return false;
+  const size_t slots = (size_t)kv.batch * kv.num_q_heads * t.pl.nsplit;
+  t.ws_o = static_cast<float*>(workspace);
+  t.ws_ml = t.ws_o ? t.ws_o + attention_ml_offset(slots) : nullptr;
+  return true;
+}
+
+}  // namespace
+
+hipError_t launch_topk_attention_merge(const quest_paged_kv& kv, int k_pages,
+                                       void* workspace, float* out,
+                                       hipStream_t stream) {
+  TaLayout t;
+  if (!ta_layout(kv, k_pages, workspace, t)) return hipErrorInvalidValue;
+  if (t.pl.nsplit > 1) launch_merge(kv, t.ws_o, t.ws_ml, t.pl.nsplit, out, stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
                                  const void* k_pool, const void* v_pool,
                                  const int32_t* page_table,
                                  const int32_t* seq_lens, const float* scores,
                                  int k_pages, int n_sink, int n_local,
                                  float sm_scale, int32_t* sel, float* out,
-                                 void* workspace, hipStream_t stream) {
+                                 void* workspace, hipStream_t stream, bool merge) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
-  const AttnPlan pl = attention_plan(kv, k_pages, kTaWaves);
-  // the caller's workspace holds the partials of the 4-wave plan, which
-  // never has fewer splits (see attention_plan); refuse rather than overrun
-  if (pl.nsplit > attention_plan(kv, k_pages).nsplit) return hipErrorInvalidValue;
-  const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_ml = ws_o ? ws_o + attention_ml_offset(slots) : nullptr;
+  TaLayout t;
+  if (!ta_layout(kv, k_pages, workspace, t)) return hipErrorInvalidValue;
+  const AttnPlan pl = t.pl;
+  float* ws_o = t.ws_o;
+  float* ws_ml = t.ws_ml;
   const float qscale = sm_scale * kLog2e;
   const int mp = kv.max_pages_per_seq;
 #define QUEST_TA_D(TT, KK, SS)                                                       \
@@ -240,7 +269,7 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
     else { if (s32) QUEST_TA_D(DType::BF16, 16, 2); else QUEST_TA_D(DType::BF16, 16, 1); }
   }
 #undef QUEST_TA_D
-  if (pl.nsplit > 1) launch_merge(kv, ws_o, ws_ml, pl.nsplit, out, stream);
+  if (merge && pl.nsplit > 1) launch_merge(kv, ws_o, ws_ml, pl.nsplit, out, stream);
   return hipGetLastError();
 }
 

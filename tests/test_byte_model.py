@@ -72,3 +72,35 @@ def test_gqa_reads_kv_once_per_kv_head():
     assert b["kv"] == 8 * 128 * 16 * 2 * 128 * 2
     assert b["meta"] == 8 * 2048 * 512
     assert b["q"] == 32 * 128 * 2 and b["out"] == 32 * 128 * 4
+
+
+def test_kernel_bytes_split_the_step_model():
+    """The per-kernel algorithmic bytes of the roofline add up to the step's
+    byte model (q counted once per kernel that reads it), and the round trips
+    the model leaves out are listed apart."""
+    import query_aware_kv_amd as qa
+    kv = qa.paged_kv(1, 32, 32, 2048, 2048, __import__("torch").float16)
+    avg = bench.step_bytes([32768], 32, 32, 128)
+    kb = bench.kernel_bytes(avg, kv, 128)
+    est, ta, mg = (kb[n][0] for n in ("estimate_kernel", "topk_attn_kernel",
+                                      "attn_merge_kernel"))
+    assert est + ta + mg == avg["total"] + avg["q"]
+    assert ta == 32 * 128 * 8192 + avg["q"]          # kept K/V + q
+    over = kb["topk_attn_kernel"][1]
+    assert over["scores_read"] == 32 * 2048 * 4 and over["sel_written"] == 32 * 128 * 4
+    # 8 splits of 16 pages per row at 32 rows: 32 heads x 8 partials
+    assert over["partials_written"] == 32 * 8 * 130 * 4
+    assert bench.topk_attn_splits(8, 128) == 16      # 8 rows: one page per wave
+
+
+def test_roofline_takes_the_slowest_kernel():
+    ku = {"estimate_kernel": 8.0, "topk_attn_kernel": 12.0, "attn_merge_kernel": 1.5}
+    kb = {"estimate_kernel": (33_570_816, {}),
+          "topk_attn_kernel": (33_562_624, {"scores_read": 262144}),
+          "attn_merge_kernel": (16384, {})}
+    r = bench.roofline(ku, kb, traffic_recorded=False)
+    assert r["kernel"] == "topk_attn_kernel" and r["kernel_us"] == 12.0
+    assert abs(r["achieved"] - 33_562_624 / 12e-6 / 1e9) < 0.1
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
+    assert r["overhead_bytes_per_launch"] == {"scores_read": 262144}
+    assert r["traffic"] is None

@@ -104,6 +104,33 @@ def test_longchat_layer_32k_budget_2048():
         assert plant <= set(sel[0, g].tolist()), g
 
 
+def test_longchat_dense_32k_against_oracle():
+    """The in-library dense baseline at the headline's size and in the
+    benchmark's launch configuration (quest_decode_attn on the LongChat
+    layer: one query head per kv-head, fp16, 32K tokens, 128 splits of 16
+    pages per head merged in one launch) against the oracle's textbook
+    attention over every token of sampled heads."""
+    wl = synth.longchat_layer_workload()
+    C.say(f"[case] dense {wl.name}: 32 heads, ctx 32768")
+    c = build(wl)
+    kv = c["kv"]
+    # pin the launch plan: 128 splits per head (partials o[128] + (M, den))
+    slots = 32 * 128
+    assert qa.quest_workspace_size(kv, kv.max_pages_per_seq) == \
+        slots * 128 * 4 + slots * 2 * 4
+    out = qa.DenseDecode(kv, SM)(c["q"], c["k_pool"], c["v_pool"],
+                                 c["page_table"], c["seq_lens"])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    heads = [3, 28]
+    pt = c["page_table"].cpu().numpy().astype(np.int64)
+    lens = c["seq_lens"].cpu().numpy().astype(np.int64)
+    ref = O.dense_attention(C.to64(c["q"][:, heads]), C.to64(c["k_pool"][:, heads]),
+                            C.to64(c["v_pool"][:, heads]), pt, lens, SM, 16)
+    worst = C.assert_attention_close(got[:, heads], ref)
+    C.say(f"  dense attention max err {worst:.2e}")
+
+
 @pytest.mark.parametrize("ctx,budget", [(4096, 4096), (16384, 256),
                                         (65536, 1024), (131072, 4096)])
 def test_sweep_point(ctx, budget):
@@ -156,10 +183,15 @@ def test_page32_layer_128k():
     C.say(f"  sampled attention max err {worst:.2e}")
 
 
-def test_gqa_multistep_three_layers():
+@pytest.mark.parametrize("path", ["calls", "append_step"])
+def test_gqa_multistep_three_layers(path):
     """Layers 0-1 dense, layer 2 sparse (GQA 32/8, group score = sum of the 4
-    query heads' bounds), three appended decode steps at 32K, against the
-    oracle's layer step on two sampled kv-heads."""
+    query heads' bounds), three appended decode steps at 32K (the first
+    append opens a new page), against the oracle's layer step on two
+    sampled kv-heads.  "calls": the append by quest_update_page_meta, then
+    the step; "append_step": the benchmark's own path -- the append folded
+    into the bounds launch (quest_append_estimate), then the Top-K +
+    attention call."""
     wl = synth.gqa_multistep_workload(layers=3, steps=3)
     G = wl.group
     heads = [1, 6]
@@ -188,14 +220,19 @@ def test_gqa_multistep_three_layers():
             c, kv = st["c"], st["kv"]
             q = synth.draw_query(wl, layer, "cuda", step=step)
             k_new, v_new = synth.draw_append_token(wl, layer, step, "cuda")
-            qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], st["kmin"],
-                                      st["kmax"], c["page_table"], lens,
-                                      k_new=k_new, v_new=v_new)
+            if layer < wl.dense_layers or path == "calls":
+                qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], st["kmin"],
+                                          st["kmax"], c["page_table"], lens,
+                                          k_new=k_new, v_new=v_new)
             if layer < wl.dense_layers:
                 out = st["dense"](q, c["k_pool"], c["v_pool"], c["page_table"], lens)
-            else:
+            elif path == "calls":
                 out = st["step"](q, c["k_pool"], c["v_pool"], st["kmin"],
                                   st["kmax"], c["page_table"], lens)
+            else:
+                out = st["step"].append_step(q, c["k_pool"], c["v_pool"], st["kmin"],
+                                             st["kmax"], c["page_table"], lens,
+                                             k_new, v_new)
             torch.cuda.synchronize()
             o = st["o"]
             s_o, sel_o, out_o = O.layer_step(

@@ -283,10 +283,12 @@ def test_full_budget_sparse_equals_dense(name):
 
 
 def test_step_is_deterministic():
+    """100 repeats of the step give the same scores, selection and output
+    bit for bit (no atomics, fixed split and merge order)."""
     wl, c = make("gqa4_f16")
     kmin, kmax = C.gpu_meta(c)
     first = C.run_gpu_step(c, wl.k_pages, kmin, kmax, SM)
-    for _ in range(5):
+    for _ in range(100):
         again = C.run_gpu_step(c, wl.k_pages, kmin, kmax, SM)
         for a, b in zip(first, again):
             assert np.array_equal(a, b, equal_nan=True)
@@ -361,6 +363,35 @@ def test_topk_attn_equals_separate_calls(name, k_extra):
     assert int((a.sel == -777).sum()) == 0
     assert torch.equal(a.sel, b.sel)
     C.assert_same_up_to_split_order(a.out, b.out)
+
+
+@pytest.mark.parametrize("k_extra", [None, 1, 5])
+@pytest.mark.parametrize("name", ["tiny_ref", "mha_ragged_f16", "gqa4_f16",
+                                  "gqa8_f16", "with_empty_request"])
+def test_topk_attn_splits_then_merge_equals_one_call(name, k_extra):
+    """quest_topk_sparse_decode_attn_splits followed by
+    quest_merge_attn_splits launch the same two kernels as
+    quest_topk_sparse_decode_attn_ex: sel_pages and out bit for bit (also
+    when the plan has a single split, where the first call writes out and
+    the merge does nothing), with forced pages too."""
+    wl, c = make(name)
+    k = wl.k_pages if k_extra is None else k_extra
+    kv = c["kv"]
+    kmin, kmax = C.gpu_meta(c)
+    for n_sink, n_local in ((0, 0), (1, min(2, k - 1))):
+        a = qa.SparseDecodeStep(kv, k, SM, select="attention", n_sink=n_sink,
+                                n_local=n_local)
+        a(c["q"], c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"], c["seq_lens"])
+        sel = torch.full_like(a.sel, -777)
+        out = torch.full_like(a.out, float("nan"))
+        ws = qa.alloc_workspace(kv, k)
+        qa.quest_topk_sparse_decode_attn_splits(
+            kv, c["q"], c["k_pool"], c["v_pool"], c["page_table"], c["seq_lens"],
+            a.scores, k, n_sink, n_local, SM, sel, out, ws)
+        qa.quest_merge_attn_splits(kv, k, ws, out)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, a.sel)
+        assert torch.equal(out.view(torch.int32), a.out.view(torch.int32))
 
 
 @pytest.mark.parametrize("select", ["attention", "separate"])
