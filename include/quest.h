@@ -294,6 +294,27 @@ QUEST_API quest_status quest_merge_attn_splits(const quest_paged_kv* kv,
                                                float* out, void* stream);
 
 /*
+ * quest_topk_sparse_decode_attn_ex without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The split partials
+ * go to a scratch array inside the library, 8 MiB (8388608 bytes) per GPU,
+ * held from the library's load until the process ends; the entry point
+ * itself calls no hipMalloc, hipFree or other allocating routine.  Outputs
+ * (sel_pages, out) are bit-identical to quest_topk_sparse_decode_attn_ex.
+ * Geometries whose partials exceed the scratch (quest_workspace_size(kv,
+ * k_pages) > 8 MiB) are refused with QUEST_ERR_UNSUPPORTED before any
+ * launch.  Every call on one GPU shares that GPU's scratch and leaves its
+ * partials there: calls that may overlap on one GPU (other streams, other
+ * host threads) race and must not be issued.  Other arguments, limits and
+ * errors as quest_topk_sparse_decode_attn_ex.
+ */
+QUEST_API quest_status quest_topk_sparse_decode_attn_noalloc(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const float* scores, int32_t k_pages, int32_t n_sink, int32_t n_local,
+    float sm_scale, int32_t* sel_pages, float* out, void* stream);
+
+/*
  * Dense decode attention over all L_b tokens (the in-library baseline).
  * "The Memory Bandwidth Bottleneck of Long-Context Decoding" in [G]:
  *   out[b][h] = softmax(sm_scale * q K^T) V over every token of request b.

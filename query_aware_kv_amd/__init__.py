@@ -24,6 +24,7 @@ from ._abi import (  # noqa: F401
     quest_stream_read_probe, quest_topk_pages, quest_topk_pages_ex,
     quest_topk_sparse_decode_attn, quest_topk_sparse_decode_attn_ex,
     quest_topk_sparse_decode_attn_splits, quest_merge_attn_splits,
+    quest_topk_sparse_decode_attn_noalloc,
     quest_update_page_meta,
     quest_workspace_size,
 )

@@ -94,6 +94,8 @@ def _load():
                                                  ctypes.c_float, P, P, P,
                                                  ctypes.c_size_t, P],
         "quest_merge_attn_splits": [KV, I, P, ctypes.c_size_t, P, P],
+        "quest_topk_sparse_decode_attn_noalloc": [KV, P, P, P, P, P, P, I, I, I,
+                                                  ctypes.c_float, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -410,6 +412,28 @@ def quest_topk_sparse_decode_attn_splits(kv: PagedKV, q, k_pool, v_pool,
         _ptr(sel_pages, "sel_pages", i32, (kv.batch, kv.num_kv_heads, k_pages)),
         _ptr(out, "out", torch.float32, (kv.batch, kv.num_q_heads, kv.head_dim)),
         _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes),
+        _stream(stream)))
+
+
+def quest_topk_sparse_decode_attn_noalloc(kv: PagedKV, q, k_pool, v_pool,
+                                          page_table, seq_lens, scores,
+                                          k_pages: int, n_sink: int, n_local: int,
+                                          sm_scale: float, sel_pages, out,
+                                          stream=None) -> None:
+    dt = kv.torch_dtype
+    i32 = torch.int32
+    _check(LIB.quest_topk_sparse_decode_attn_noalloc(
+        ctypes.byref(kv),
+        _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
+        _ptr(seq_lens, "seq_lens", i32, (kv.batch,)),
+        _ptr(scores, "scores", torch.float32,
+             (kv.batch, kv.num_kv_heads, kv.max_pages_per_seq)),
+        int(k_pages), int(n_sink), int(n_local), float(sm_scale),
+        _ptr(sel_pages, "sel_pages", i32, (kv.batch, kv.num_kv_heads, k_pages)),
+        _ptr(out, "out", torch.float32, (kv.batch, kv.num_q_heads, kv.head_dim)),
         _stream(stream)))
 
 

@@ -378,6 +378,35 @@ QUEST_API quest_status quest_topk_sparse_decode_attn_splits(
                             "quest_topk_sparse_decode_attn_splits");
 }
 
+QUEST_API quest_status quest_topk_sparse_decode_attn_noalloc(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const float* scores, int32_t k_pages, int32_t n_sink, int32_t n_local,
+    float sm_scale, int32_t* sel_pages, float* out, void* stream) {
+  const char* fn = "quest_topk_sparse_decode_attn_noalloc";
+  quest_status s = check_attention_common(kv, q, k_pool, v_pool, page_table,
+                                          seq_lens, sm_scale, out, fn);
+  if (s != QUEST_OK) return s;
+  REQUIRE_PTR(scores, aligned4(scores));
+  REQUIRE_PTR(sel_pages, aligned4(sel_pages));
+  if ((s = check_topk_counts(k_pages, n_sink, n_local, fn)) != QUEST_OK) return s;
+  if (kv->max_pages_per_seq > quest::kTopkAttnMaxPages || k_pages > quest::kTopkAttnMaxPages)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: max_pages_per_seq and k_pages must be <= %d",
+                fn, quest::kTopkAttnMaxPages);
+  const size_t need = quest::attention_workspace_bytes(*kv, k_pages);
+  if (need > quest::kNoAllocScratchBytes)
+    return fail(QUEST_ERR_UNSUPPORTED,
+                "%s: this geometry needs %zu bytes of split scratch; the "
+                "allocation-free entry point holds %zu bytes per GPU (use "
+                "quest_topk_sparse_decode_attn_ex with a workspace)",
+                fn, need, quest::kNoAllocScratchBytes);
+  return hip_status(quest::launch_topk_attention_noalloc(
+                        *kv, q, k_pool, v_pool, page_table, seq_lens, scores,
+                        k_pages, n_sink, n_local, sm_scale, sel_pages, out,
+                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 QUEST_API quest_status quest_merge_attn_splits(const quest_paged_kv* kv,
                                                int32_t k_pages,
                                                const void* workspace,

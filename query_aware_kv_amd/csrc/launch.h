@@ -87,6 +87,16 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
 hipError_t launch_topk_attention_merge(const quest_paged_kv& kv, int k_pages,
                                        void* workspace, float* out,
                                        hipStream_t stream);
+// The same launches with the partials in the library's per-GPU scratch
+// array (topk_attn.hip) instead of a caller workspace: no allocation.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+hipError_t launch_topk_attention_noalloc(const quest_paged_kv& kv, const void* q,
+                                         const void* k_pool, const void* v_pool,
+                                         const int32_t* page_table,
+                                         const int32_t* seq_lens, const float* scores,
+                                         int k_pages, int n_sink, int n_local,
+                                         float sm_scale, int32_t* sel, float* out,
+                                         hipStream_t stream);
 
 // Fused step (estimate -> Top-K -> attention in one launch).
 constexpr int kStepMaxPages = 8192;

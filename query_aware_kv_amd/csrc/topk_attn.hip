@@ -16,6 +16,8 @@
 // Workgroups have 8 waves (one slice of 8 * PPW pages): the selection is
 // repeated once per workgroup, so half as many workgroups as with 4 waves
 // halves that repeated work while the same number of waves stream K/V.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "dev_attn.h"
@@ -206,7 +208,40 @@ void dispatch_g(int G, int ppw, const quest_paged_kv& kv, const void* q,
 
 }  // namespace
 
+// Scratch of quest_topk_sparse_decode_attn_noalloc: room for the split
+// partials of one call, a file-scope device array (each GPU that loads the
+// library holds its own copy until the process ends).  Host code must not
+// pass this name to a kernel -- on the host it is only a stand-in -- but the
+// device address that hipGetSymbolAddress returns for the current GPU.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];  // per GPU, set once
+std::mutex g_scratch_mu;
+
+// The current GPU's address of `scratch`, looked up on the first call on
+// that GPU (with the GPU current) and kept.
+hipError_t scratch_address(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return hipSuccess;
+}
 
 // The 8-wave plan, and where its partials live in the caller's workspace.
 struct TaLayout {
@@ -227,6 +262,23 @@ bool ta_layout(const quest_paged_kv& kv, int k_pages, void* workspace, TaLayout&
 }
 
 }  // namespace
+
+hipError_t launch_topk_attention_noalloc(const quest_paged_kv& kv, const void* q,
+                                         const void* k_pool, const void* v_pool,
+                                         const int32_t* page_table,
+                                         const int32_t* seq_lens, const float* scores,
+                                         int k_pages, int n_sink, int n_local,
+                                         float sm_scale, int32_t* sel, float* out,
+                                         hipStream_t stream) {
+  if (attention_workspace_bytes(kv, k_pages) > kNoAllocScratchBytes)
+    return hipErrorInvalidValue;  // the caller checks first
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_topk_attention(kv, q, k_pool, v_pool, page_table, seq_lens, scores,
+                               k_pages, n_sink, n_local, sm_scale, sel, out, ws,
+                               stream, true);
+}
 
 hipError_t launch_topk_attention_merge(const quest_paged_kv& kv, int k_pages,
                                        void* workspace, float* out,

@@ -306,3 +306,22 @@ def test_paged_kv_like_reads_the_geometry_off_the_tensors():
         qa.paged_kv_like(q, k_pool, pt[:2])            # batch disagrees
     with pytest.raises(ValueError):
         qa.paged_kv_like(q.float(), k_pool.float(), pt)  # no float32 caches
+
+
+def test_noalloc_refuses_geometries_past_its_scratch():
+    """The allocation-free entry point holds 8 MiB of split scratch per GPU:
+    a geometry that needs more is refused on the host, before any HIP call
+    (2048 rows x 1024 kept pages: 64 MiB of partials)."""
+    k = kv(batch=64, num_pool_pages=16, max_pages_per_seq=1024)
+    st, need = ws_size(k, 1024)
+    assert st == 0 and need > 8 << 20
+    P = ctypes.c_void_p
+    st = qa.LIB.quest_topk_sparse_decode_attn_noalloc(
+        ctypes.byref(k), *[P(FAKE)] * 6, 1024, 0, 0, 0.088, P(FAKE), P(FAKE), None)
+    assert st == _abi.QUEST_ERR_UNSUPPORTED
+    msg = qa.LIB.quest_last_error().decode()
+    assert "scratch" in msg and str(8 << 20) in msg
+    # bad counts are still argument errors
+    st = qa.LIB.quest_topk_sparse_decode_attn_noalloc(
+        ctypes.byref(kv()), *[P(FAKE)] * 6, 0, 0, 0, 0.088, P(FAKE), P(FAKE), None)
+    assert st == _abi.QUEST_ERR_INVALID_ARGUMENT
