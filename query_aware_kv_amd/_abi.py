@@ -14,7 +14,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libquest.so")
+# QUEST_LIB names another build of the same library (the host-sanitized one
+# the ABI tests run against); by default the in-tree build.
+LIB_PATH = os.environ.get("QUEST_LIB") or os.path.join(_HERE, "libquest.so")
 
 QUEST_OK = 0
 QUEST_ERR_INVALID_ARGUMENT = 1

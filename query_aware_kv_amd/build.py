@@ -37,9 +37,17 @@ SOURCES = ["api.cpp", "meta.hip", "estimate.hip", "topk.hip", "attention.hip",
            "union.hip"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src),
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for the CPU-only
+# build the ABI tests run against (device code is built as usual).
+SANITIZE_HOST = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                 "-Xarch_host -fno-omit-frame-pointer -Xarch_host -g").split()
+BUILD_SAN = os.path.join(PKG, "_build_san")
+LIB_SAN = os.path.join(BUILD_SAN, "libquest_san.so")
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *COMMON_FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src),
            "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -66,6 +74,37 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    """libquest_san.so: the same sources with host code under ASan + UBSan
+    (load it with the sanitizer runtime preloaded, QUEST_LIB pointing at
+    it).  For the host-side ABI tests only: no kernel is launched there."""
+    if os.path.isdir(BUILD_SAN):
+        shutil.rmtree(BUILD_SAN)
+    os.makedirs(BUILD_SAN)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s_: _compile(s_, BUILD_SAN, SANITIZE_HOST), SOURCES))
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *SANITIZE_HOST,
+           "-shared-libsan", *objs, "-o", LIB_SAN]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {LIB_SAN}")
+    return LIB_SAN
+
+
+def sanitizer_runtime() -> str:
+    """The shared ASan runtime of hipcc's clang (to preload)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin",
+                         "clang")
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitized" in sys.argv:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -565,7 +565,13 @@ QUEST_API quest_status quest_stream_read_probe(const void* buf, size_t bytes,
 }
 
 QUEST_API const char* quest_status_string(quest_status status) {
-  switch (status) {
+  // Callers across the C ABI may pass any int: read the argument's bytes as
+  // an int rather than as the enum (a value outside the enumerators' range
+  // is undefined behaviour for a C++ enum).
+  int code = 0;
+  static_assert(sizeof(code) == sizeof(status), "quest_status is int-sized");
+  std::memcpy(&code, &status, sizeof(code));
+  switch (code) {
     case QUEST_OK: return "ok";
     case QUEST_ERR_INVALID_ARGUMENT: return "invalid argument";
     case QUEST_ERR_UNSUPPORTED: return "unsupported shape or dtype";
