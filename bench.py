@@ -1315,6 +1315,29 @@ def pmc_summary(d, copy_mib):
     return "\n".join(head + out + calls) + "\n"
 
 
+def trace_summary(d):
+    """Markdown: per-kernel dispatch count, mean and median duration (ns)
+    and grid from rocprofv3 --kernel-trace CSVs under d."""
+    rows = {}
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            n = row["Kernel_Name"]
+            m = re.search(r"quest::\(anonymous namespace\)::(\w+)(<[^(]*>)?", n)
+            if not m:
+                continue
+            key = (m.group(1) + (m.group(2) or ""),
+                   f"{row.get('Grid_Size_X', row.get('Grid_Size', '?'))}x"
+                   f"{row.get('Grid_Size_Y', '1')}/{row.get('Workgroup_Size_X', '?')}")
+            dur = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+            rows.setdefault(key, []).append(dur)
+    out = ["| kernel | grid (threads x, y / workgroup) | dispatches | mean ns | median ns |",
+           "|---|---|---|---|---|"]
+    for (k, grid), v in sorted(rows.items(), key=lambda kv: -statistics.mean(kv[1])):
+        out.append(f"| `{k}` | {grid} | {len(v)} | {statistics.mean(v):.0f} | "
+                   f"{statistics.median(v):.0f} |")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1344,9 +1367,14 @@ def main():
                          "(calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="only summarise rocprofv3 counter CSVs under DIR")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="only summarise rocprofv3 --kernel-trace CSVs under DIR")
     ap.add_argument("--copy-mib", type=int, default=512,
                     help="size the --copy-probe runs used (for --pmc-summary)")
     args = ap.parse_args()
+    if args.trace_summary:
+        sys.stdout.write(trace_summary(args.trace_summary))
+        return
     if args.pmc_summary:
         sys.stdout.write(pmc_summary(args.pmc_summary, args.copy_mib))
         return
