@@ -8,7 +8,8 @@
 // Scores become order-preserving uint32 keys (-0 folded onto +0 first, so
 // equal numbers get equal keys), kept in VGPRs: KPT per thread, in segments
 // of SEG consecutive pages -- thread t holds pages SEG*t .. SEG*t+SEG-1 of
-// each stretch of SEG*BLOCK pages.  SEG = 4 (the default) spreads a row just
+// each stretch of SEG*BLOCK pages -- and optionally a short tail of TAIL
+// pages per thread after the last stretch (topk_page).  SEG = 4 (the default) spreads a row just
 // longer than 4*BLOCK pages over every wave, which the latency-bound
 // launches want; SEG = KPT (one run per thread) needs one placement scan
 // instead of KPT/4, which the many-row launches that share the CUs want.
@@ -38,9 +39,16 @@ struct TopkSmem {
   uint32_t prefix, need, count;
 };
 
-// Page of this thread's key i: segment i / SEG, position i % SEG.
-template <int BLOCK, int SEG>
+// Page of this thread's key i.  The first KPT - TAIL keys lie in segments
+// of SEG consecutive pages (segment i / SEG, position i % SEG); the last
+// TAIL keys are a run of TAIL consecutive pages per thread after every
+// segment: pages SK*BLOCK + TAIL*t .. +TAIL-1 for thread t, SK = KPT - TAIL.
+// A tail extends a row by TAIL*BLOCK pages at a fraction of the cost of a
+// whole further segment (rows just past 2048 pages: 5 keys per thread
+// instead of 8).
+template <int BLOCK, int SEG, int SK = 0, int TAIL = 0>
 __device__ __forceinline__ int topk_page(int i) {
+  if (TAIL > 0 && i >= SK) return SK * BLOCK + (int)threadIdx.x * TAIL + (i - SK);
   return (i / SEG) * (BLOCK * SEG) + (int)threadIdx.x * SEG + i % SEG;
 }
 
@@ -71,26 +79,31 @@ __device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t x) {
 // the row, so they go out back to back; entries past `limit` hold anything
 // and are never used (they are not pages of the row).  A 16-byte-aligned
 // row whose length is a multiple of 4 is read with 16-byte loads.
-template <int BLOCK, int KPT, int SEG = kTopkSeg>
+// (TAIL: see topk_page; the tail keys are read one 4-byte load each.)
+template <int BLOCK, int KPT, int SEG = kTopkSeg, int TAIL = 0>
 __device__ __forceinline__ void topk_load(const float* __restrict__ s, int limit,
                                           float (&v)[KPT]) {
-  static_assert(SEG % 4 == 0 && KPT % SEG == 0 && KPT / SEG <= kTopkMaxSegs,
-                "whole 16-byte pieces and segments");
+  constexpr int SK = KPT - TAIL;
+  static_assert(SEG % 4 == 0 && SK % SEG == 0 && SK / SEG + (TAIL > 0) <= kTopkMaxSegs &&
+                    TAIL >= 0 && TAIL < SEG,
+                "whole 16-byte pieces and segments, a tail shorter than a segment");
   const bool vec = (reinterpret_cast<uintptr_t>(s) & 15u) == 0 && (limit & 3) == 0 &&
                    limit >= 4;
   if (vec) {  // row-uniform
 #pragma unroll
-    for (int i = 0; i < KPT; i += 4) {
-      const int b = min(topk_page<BLOCK, SEG>(i), limit - 4);  // each piece wholly in or out
+    for (int i = 0; i < SK; i += 4) {
+      const int b = min(topk_page<BLOCK, SEG, SK, TAIL>(i), limit - 4);  // each piece wholly in or out
       const float4 x = *reinterpret_cast<const float4*>(s + b);
       v[i] = x.x;
       v[i + 1] = x.y;
       v[i + 2] = x.z;
       v[i + 3] = x.w;
     }
+#pragma unroll
+    for (int i = SK; i < KPT; ++i) v[i] = s[min(topk_page<BLOCK, SEG, SK, TAIL>(i), limit - 1)];
   } else if (limit > 0) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) v[i] = s[min(topk_page<BLOCK, SEG>(i), limit - 1)];
+    for (int i = 0; i < KPT; ++i) v[i] = s[min(topk_page<BLOCK, SEG, SK, TAIL>(i), limit - 1)];
   } else {  // an empty row: nothing to read
 #pragma unroll
     for (int i = 0; i < KPT; ++i) v[i] = 0.f;
@@ -126,7 +139,7 @@ __device__ __forceinline__ void topk_load_table(const int32_t* __restrict__ pt_r
 // Forced pages take no part in the radix select: it picks k - n_sink -
 // n_local among the others, and the placement scan counts forced pages as
 // kept, so the list stays ascending.
-template <int BLOCK, int KPT, int SEG = kTopkSeg>
+template <int BLOCK, int KPT, int SEG = kTopkSeg, int TAIL = 0>
 __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
                          int n_sink, int n_local,
                          int32_t* __restrict__ out,
@@ -134,6 +147,7 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
                          int32_t* __restrict__ phys, TopkSmem<BLOCK>& sm,
                          int w_lo = 0, int w_hi = 0x7fffffff) {
   constexpr int NW = BLOCK / kWave;
+  constexpr int SK = KPT - TAIL;
   static_assert(NW >= 2, "one wave scans while the others clear");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   w_hi = min(w_hi, k);
@@ -145,7 +159,7 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
     if (phys) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
-        const int p = topk_page<BLOCK, SEG>(i);
+        const int p = topk_page<BLOCK, SEG, SK, TAIL>(i);
         if (p < n && p >= w_lo && p < w_hi) phys[p - w_lo] = (*ent)[i];
       }
     }
@@ -159,7 +173,7 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
   uint32_t kmn = 0xffffffffu, kmx = 0u;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const int p = topk_page<BLOCK, SEG>(i);
+    const int p = topk_page<BLOCK, SEG, SK, TAIL>(i);
     forced[i] = p < n && (p < n_sink || p >= local0);
     cand[i] = p < n && !forced[i];
     key[i] = cand[i] ? score_key(v[i]) : 0u;
@@ -235,8 +249,12 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
   // Kept: forced pages, competing keys whose decided bits exceed the
   // threshold's, and the first `need` (in page order) whose decided bits
   // equal them.  "gt" counts the first two kinds.  Pages are ordered by
-  // segment, then thread, then position: one packed count per segment.
-  constexpr int NSEG = KPT / SEG;
+  // segment, then thread, then position: one packed count per segment (the
+  // tail, if any, is the last segment, TAIL keys long).
+  constexpr int NFULL = SK / SEG;
+  constexpr int NSEG = NFULL + (TAIL > 0 ? 1 : 0);
+  auto seg_len = [](int sg) { return sg < NFULL ? SEG : TAIL; };
+  auto seg_key = [](int sg, int e) { return sg < NFULL ? sg * SEG + e : SK + e; };
   const uint32_t thr = shift >= 32 ? 0u : (prefix >> shift);
   uint32_t packed[NSEG], incl[NSEG];
 #pragma unroll
@@ -244,7 +262,8 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < SEG; ++e) {
-      const int i = sg * SEG + e;
+      if (e >= seg_len(sg)) break;
+      const int i = seg_key(sg, e);
       const uint32_t v = key[i] >> shift;
       gt += forced[i] || (pick && cand[i] && v > thr);
       eq += pick && cand[i] && v == thr;
@@ -266,8 +285,9 @@ __device__ __forceinline__ void topk_row(const float (&v)[KPT], int n, int k,
     uint32_t gt_before = before >> 16, eq_before = before & 0xffffu;
 #pragma unroll
     for (int e = 0; e < SEG; ++e) {
-      const int i = sg * SEG + e;
-      const int page = topk_page<BLOCK, SEG>(i);
+      if (e >= seg_len(sg)) break;
+      const int i = seg_key(sg, e);
+      const int page = topk_page<BLOCK, SEG, SK, TAIL>(i);
       if (page >= n) continue;
       const uint32_t v = key[i] >> shift;
       uint32_t slot = 0xffffffffu;

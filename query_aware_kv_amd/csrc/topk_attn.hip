@@ -31,7 +31,7 @@ namespace {
 constexpr int kTaWaves = 8;
 constexpr int kTaThreads = kTaWaves * kWave;
 
-template <DType T, int G, int KPT, int PPW, int SUB>
+template <DType T, int G, int KPT, int PPW, int SUB, int TAIL>
 __global__ void __launch_bounds__(kTaThreads)
 topk_attn_kernel(const uint16_t* __restrict__ q,
                  const uint16_t* __restrict__ k_pool,
@@ -57,7 +57,8 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
 
   // Scores, the length and q are independent loads.
   float v[KPT];
-  topk_load<kTaThreads, KPT>(scores + (int64_t)unit * max_pages, max_pages, v);
+  topk_load<kTaThreads, KPT, kTopkSeg, TAIL>(scores + (int64_t)unit * max_pages, max_pages,
+                                             v);
   const int L = seq_lens[b];
   // q: packed words of one head (VALU path), the MFMA operand for a group
   AttnQ<G> qf;
@@ -69,8 +70,8 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
   constexpr int S = SUB * kTileRows;
   const int n = pages_of(L, S, max_pages);
   const int s0 = split * kTaWaves * PPW;
-  topk_row<kTaThreads, KPT>(v, n, k, n_sink, n_local, kept, nullptr, nullptr, sm.topk,
-                            s0, s0 + kTaWaves * PPW);
+  topk_row<kTaThreads, KPT, kTopkSeg, TAIL>(v, n, k, n_sink, n_local, kept, nullptr, nullptr,
+                                            sm.topk, s0, s0 + kTaWaves * PPW);
   __syncthreads();
 
   // This workgroup's slice of the list: publish it, then attend over it.
@@ -166,28 +167,28 @@ topk_attn_kernel(const uint16_t* __restrict__ q,
   }
 }
 
-template <DType T, int G, int KPT, int PPW, int SUB>
+template <DType T, int G, int KPT, int PPW, int SUB, int TAIL>
 void launch_t(const quest_paged_kv& kv, const void* q, const void* k_pool,
               const void* v_pool, const int32_t* page_table,
               const int32_t* seq_lens, const float* scores, int k, int n_sink,
               int n_local, float qscale, int32_t* sel, float* out, float* ws_o,
               float* ws_ml, int nsplit, hipStream_t stream) {
   dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
-  topk_attn_kernel<T, G, KPT, PPW, SUB><<<grid, kTaThreads, 0, stream>>>(
+  topk_attn_kernel<T, G, KPT, PPW, SUB, TAIL><<<grid, kTaThreads, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), page_table, seq_lens, scores, k,
       n_sink, n_local, kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages, qscale, sel, out,
       ws_o, ws_ml);
 }
 
-template <DType T, int KPT, int SUB>
+template <DType T, int KPT, int SUB, int TAIL = 0>
 void dispatch_g(int G, int ppw, const quest_paged_kv& kv, const void* q,
                 const void* k_pool, const void* v_pool, const int32_t* page_table,
                 const int32_t* seq_lens, const float* scores, int k, int n_sink,
                 int n_local, float qscale, int32_t* sel, float* out, float* ws_o,
                 float* ws_ml, int nsplit, hipStream_t s) {
 #define QUEST_TA(GG, PP)                                                         \
-  launch_t<T, GG, KPT, PP, SUB>(kv, q, k_pool, v_pool, page_table, seq_lens, scores, \
+  launch_t<T, GG, KPT, PP, SUB, TAIL>(kv, q, k_pool, v_pool, page_table, seq_lens, scores, \
                            k, n_sink, n_local, qscale, sel, out, ws_o, ws_ml,    \
                            nsplit, s)
   // ppw never exceeds the plan's limit for SUB: only those variants are built
@@ -304,22 +305,23 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
   float* ws_ml = t.ws_ml;
   const float qscale = sm_scale * kLog2e;
   const int mp = kv.max_pages_per_seq;
-#define QUEST_TA_D(TT, KK, SS)                                                       \
-  dispatch_g<TT, KK, SS>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,    \
-                         scores, k_pages, n_sink, n_local, qscale, sel, out, ws_o,  \
-                         ws_ml, pl.nsplit, stream)
+#define QUEST_TA_D(TT, KK, SS, TL)                                                   \
+  dispatch_g<TT, KK, SS, TL>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens, \
+                             scores, k_pages, n_sink, n_local, qscale, sel, out,     \
+                             ws_o, ws_ml, pl.nsplit, stream)
   const bool s32 = kv.page_size == 32;
-  // scores per thread: the fewest (a multiple of 4) that cover the row
-  // (fewer VGPRs, shorter load and select)
-  if (kv.dtype == QUEST_F16) {
-    if (mp <= 2048) { if (s32) QUEST_TA_D(DType::F16, 4, 2); else QUEST_TA_D(DType::F16, 4, 1); }
-    else if (mp <= 4096) { if (s32) QUEST_TA_D(DType::F16, 8, 2); else QUEST_TA_D(DType::F16, 8, 1); }
-    else { if (s32) QUEST_TA_D(DType::F16, 16, 2); else QUEST_TA_D(DType::F16, 16, 1); }
-  } else {
-    if (mp <= 2048) { if (s32) QUEST_TA_D(DType::BF16, 4, 2); else QUEST_TA_D(DType::BF16, 4, 1); }
-    else if (mp <= 4096) { if (s32) QUEST_TA_D(DType::BF16, 8, 2); else QUEST_TA_D(DType::BF16, 8, 1); }
-    else { if (s32) QUEST_TA_D(DType::BF16, 16, 2); else QUEST_TA_D(DType::BF16, 16, 1); }
-  }
+  // scores per thread: the fewest that cover the row (fewer VGPRs, a shorter
+  // load and selection): 4, 4 + a tail of 1 (rows of up to 2560 pages: the
+  // 32K contexts that have grown a few pages), 8 or 16
+  auto by_len = [&](auto tt) {
+    constexpr DType TT = decltype(tt)::value;
+    if (mp <= 2048) { if (s32) QUEST_TA_D(TT, 4, 2, 0); else QUEST_TA_D(TT, 4, 1, 0); }
+    else if (mp <= 2560) { if (s32) QUEST_TA_D(TT, 5, 2, 1); else QUEST_TA_D(TT, 5, 1, 1); }
+    else if (mp <= 4096) { if (s32) QUEST_TA_D(TT, 8, 2, 0); else QUEST_TA_D(TT, 8, 1, 0); }
+    else { if (s32) QUEST_TA_D(TT, 16, 2, 0); else QUEST_TA_D(TT, 16, 1, 0); }
+  };
+  if (kv.dtype == QUEST_F16) by_len(std::integral_constant<DType, DType::F16>{});
+  else by_len(std::integral_constant<DType, DType::BF16>{});
 #undef QUEST_TA_D
   if (merge && pl.nsplit > 1) launch_merge(kv, ws_o, ws_ml, pl.nsplit, out, stream);
   return hipGetLastError();

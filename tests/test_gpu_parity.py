@@ -425,16 +425,17 @@ def test_graph_replay_matches_eager(select):
 
 
 @pytest.mark.parametrize("mp,rows", [(2056, 12), (2056, 300), (4104, 12), (1027, 300),
-                                     (2048, 300)])
+                                     (2048, 300), (2560, 12), (2561, 12), (2560, 300)])
 def test_topk_segment_boundaries(mp, rows):
     """Rows whose length crosses the 4-page segments of the selection's key
-    layout (1024, 2048 and 4096 pages and just past them), with few rows
-    (the 8-wave launch, keys in segments of 4) and many (the 4-wave one,
-    keys in runs): bit-exact against the oracle, every score kind."""
+    layout (1024, 2048 and 4096 pages and just past them) and the one-key
+    tail after 2048 pages (rows of up to 2560), with few rows (the 8-wave
+    launch, keys in segments of 4) and many (the 4-wave one, keys in runs):
+    bit-exact against the oracle, every score kind."""
     k = 128
     g = np.random.default_rng(mp * 7 + rows)
-    edges = [n for n in (1023, 1024, 1025, 1028, 2047, 2048, 2049, 2052, 2056, 4095,
-                         4096, 4097, 4100, 4104) if n <= mp]
+    edges = [n for n in (1023, 1024, 1025, 1028, 2047, 2048, 2049, 2052, 2056, 2559,
+                         2560, 2561, 4095, 4096, 4097, 4100, 4104) if n <= mp]
     n_list = (edges * (rows // len(edges) + 1))[:rows]
     n_list[-1] = int(g.integers(1, mp + 1))
     C.say(f"[case] topk segments mp={mp} rows={rows}")
@@ -450,14 +451,15 @@ def test_topk_segment_boundaries(mp, rows):
         assert np.array_equal(got[r, 0], ref), f"row {r} n={n_list[r]}"
 
 
-@pytest.mark.parametrize("mp", [2056, 4104])
+@pytest.mark.parametrize("mp", [2056, 2560, 2561, 4104])
 def test_topk_attn_selection_segment_boundaries(mp):
     """The selection inside the attention launch (quest_topk_sparse_decode_attn,
-    keys in segments of 4) at lengths around the segment boundaries: its
-    sel_pages output bit-exact against the oracle."""
-    rows, k = 10, 128
-    edges = [n for n in (2047, 2048, 2049, 2052, 2056, 4096, 4097, 4104, 1, 129)
-             if n <= mp]
+    keys in segments of 4, with a one-key tail for rows of up to 2560 pages)
+    at lengths around the segment boundaries: its sel_pages output bit-exact
+    against the oracle."""
+    rows, k = 12, 128
+    edges = [n for n in (2047, 2048, 2049, 2052, 2056, 2559, 2560, 2561, 4096, 4097,
+                         4104, 1, 129) if n <= mp]
     n_list = (edges * 2)[:rows]
     C.say(f"[case] topk_attn segments mp={mp} n={n_list}")
     s = _topk_case(rows, n_list, mp, k, seed=mp + 11)
