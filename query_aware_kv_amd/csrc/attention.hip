@@ -34,95 +34,110 @@ attn_split_kernel(const uint16_t* __restrict__ q,
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int c = lane & 15, r = lane >> 4;
 
-  // List entries, then their table entries: neither waits for the length
-  // (both are in bounds on their own); the length only masks afterwards.
-  // The loads are unconditional, from indices clamped into the row (slots
-  // past the end read a valid entry and discard it), so each group goes
-  // out back to back with one wait.
-  const int i0 = (split * kAttnWaves + wid) * PPW;
-  int jr[PPW];
-  int64_t pp[PPW];
-#pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
-    const int i = i0 + pi;
-    if (sel) {
-      const int e = sel[(int64_t)unit * list_len + min(i, list_len - 1)];
-      jr[pi] = i < list_len ? e : -1;
-    } else {
-      jr[pi] = i < max_pages ? i : -1;
-    }
-  }
-#pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) {
-    const bool in_row = jr[pi] >= 0 && jr[pi] < max_pages;
-    const int64_t e = page_table[(int64_t)b * max_pages + (in_row ? jr[pi] : 0)];
-    pp[pi] = in_row ? e : -1;
-  }
+  // The workgroup's entries: a balanced contiguous range of the list --
+  // sel_pages[b][g][..] (entries -1 skipped) or 0..max_pages-1 -- walked in
+  // chunks of kAttnWaves * PPW entries, wave w taking PPW consecutive ones
+  // of each chunk.  The sparse plan gives every workgroup one chunk; the
+  // dense plan sizes the ranges so that the grid fits the GPU in one round.
+  const int64_t lo = (int64_t)split * list_len / nsplit;
+  const int64_t hi = (int64_t)(split + 1) * list_len / nsplit;
   const int L = seq_lens[b];
   constexpr int S = SUB * kTileRows;
-  const int n = pages_of(L, S, max_pages);
-  int pj[PPW];
-#pragma unroll
-  for (int pi = 0; pi < PPW; ++pi)
-    pj[pi] = (jr[pi] >= 0 && jr[pi] < n && pp[pi] >= 0 && pp[pi] < num_pool_pages)
-                 ? jr[pi] : -1;
-  // valid tokens of tile s of page pi (<= 0: absent); uniform over the wave
-  auto tile_valid = [&](int pi, int s) {
-    return pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
-  };
-  // The tile loads sit in one branch that depends on every page's table
-  // entry, so all of them are in before the first tile load and no wait
-  // separates the pages' loads.
-  bool any = false;
-#pragma unroll
-  for (int pi = 0; pi < PPW; ++pi) any |= pj[pi] >= 0;
-  uint4 kx[PPW][SUB][4], vx[PPW][SUB][4];
-  if constexpr (G >= 2) {
-    // a query group: both products on the matrix cores (dev_attn_mfma.h)
-    uint4 qb[4];
+  // q: packed words of one head (VALU path), the MFMA operand for a group
+  AttnQ<G> qf;
+  uint4 qb[4];
+  if constexpr (G >= 2)
     mfma_load_q<G>(q, (int64_t)unit * G, lane, qb);
-    if (any) {
-#pragma unroll
-      for (int pi = 0; pi < PPW; ++pi)
-#pragma unroll
-        for (int s = 0; s < SUB; ++s)
-          if (tile_valid(pi, s) > 0)
-            mfma_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), lane,
-                           kx[pi][s], vx[pi][s]);
-    }
-    MfmaAttnState st;
-    mfma_attn_init(st);
-#pragma unroll
-    for (int pi = 0; pi < PPW; ++pi)
-#pragma unroll
-      for (int s = 0; s < SUB; ++s) {
-        const int v = tile_valid(pi, s);
-        if (v > 0) mfma_attn_page<T>(st, qb, kx[pi][s], vx[pi][s], v, qscale, lane);
-      }
-    mfma_attn_stage_wave(st, sm, wid, lane);
-  } else {
-    AttnQ<G> qf;
+  else
     attn_load_q<T, G>(q, (int64_t)unit * G, c, qscale, qf);
-    if (any) {
+  MfmaAttnState mst;
+  AttnState<G> vst;
+  if constexpr (G >= 2) mfma_attn_init(mst);
+  else attn_init(vst);
+  for (int64_t c0 = lo; c0 < hi; c0 += kAttnWaves * PPW) {
+    // List entries, then their table entries: neither waits for the length
+    // (both are in bounds on their own); the length only masks afterwards.
+    // The loads are unconditional, from indices clamped into the row (slots
+    // past the end read a valid entry and discard it), so each group goes
+    // out back to back with one wait.
+    const int64_t i0 = c0 + wid * PPW;
+    int jr[PPW];
+    int64_t pp[PPW];
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi) {
+      const int64_t i = i0 + pi;
+      if (sel) {
+        const int e = sel[(int64_t)unit * list_len + min(i, (int64_t)list_len - 1)];
+        jr[pi] = i < hi ? e : -1;
+      } else {
+        jr[pi] = i < hi ? (int)i : -1;
+      }
+    }
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi) {
+      const bool in_row = jr[pi] >= 0 && jr[pi] < max_pages;
+      const int64_t e = page_table[(int64_t)b * max_pages + (in_row ? jr[pi] : 0)];
+      pp[pi] = in_row ? e : -1;
+    }
+    const int n = pages_of(L, S, max_pages);
+    int pj[PPW];
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi)
+      pj[pi] = (jr[pi] >= 0 && jr[pi] < n && pp[pi] >= 0 && pp[pi] < num_pool_pages)
+                   ? jr[pi] : -1;
+    // valid tokens of tile s of page pi (<= 0: absent); uniform over the wave
+    auto tile_valid = [&](int pi, int s) {
+      return pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
+    };
+    // The tile loads sit in one branch that depends on every page's table
+    // entry, so all of them are in before the first tile load and no wait
+    // separates the pages' loads.
+    bool any = false;
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi) any |= pj[pi] >= 0;
+    uint4 kx[PPW][SUB][4], vx[PPW][SUB][4];
+    if constexpr (G >= 2) {
+      // a query group: both products on the matrix cores (dev_attn_mfma.h)
+      if (any) {
+#pragma unroll
+        for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+          for (int s = 0; s < SUB; ++s)
+            if (tile_valid(pi, s) > 0)
+              mfma_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), lane,
+                             kx[pi][s], vx[pi][s]);
+      }
 #pragma unroll
       for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
-        for (int s = 0; s < SUB; ++s)
-          if (tile_valid(pi, s) > 0)
-            attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
-                           kx[pi][s], vx[pi][s]);
-    }
-    AttnState<G> st;
-    attn_init(st);
+        for (int s = 0; s < SUB; ++s) {
+          const int v = tile_valid(pi, s);
+          if (v > 0) mfma_attn_page<T>(mst, qb, kx[pi][s], vx[pi][s], v, qscale, lane);
+        }
+    } else {
+      if (any) {
 #pragma unroll
-    for (int pi = 0; pi < PPW; ++pi)
+        for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
-      for (int s = 0; s < SUB; ++s) {
-        const int v = tile_valid(pi, s);
-        if (v > 0) attn_page<T, G>(st, qf, kx[pi][s], vx[pi][s], v, r);
+          for (int s = 0; s < SUB; ++s)
+            if (tile_valid(pi, s) > 0)
+              attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
+                             kx[pi][s], vx[pi][s]);
       }
-    attn_combine_rows(st);
-    attn_stage_wave(st, sm, wid, r, c);
+#pragma unroll
+      for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+          const int v = tile_valid(pi, s);
+          if (v > 0) attn_page<T, G>(vst, qf, kx[pi][s], vx[pi][s], v, r);
+        }
+    }
+  }
+  if constexpr (G >= 2) {
+    mfma_attn_stage_wave(mst, sm, wid, lane);
+  } else {
+    attn_combine_rows(vst);
+    attn_stage_wave(vst, sm, wid, r, c);
   }
   __syncthreads();
 
@@ -156,6 +171,43 @@ attn_merge_kernel(const float* __restrict__ ws_o,
   const int64_t qh = blockIdx.x;
   merge_splits(ws_o + qh * nsplit * kHeadDim, ws_ml + qh * nsplit * 2, nsplit,
                out + qh * kHeadDim, sm);
+}
+
+// Many splits (the dense plan's): 8 groups of 128 threads, group u folding
+// splits u, u + 8, ... of every channel, 16 per memory round trip (so up to
+// 128 splits take one), then the groups meet in LDS.
+constexpr int kMergeWideMin = 32;
+constexpr int kMergeGroups = 8;
+constexpr int kMergeWideThreads = kMergeGroups * kHeadDim;
+
+__global__ void __launch_bounds__(kMergeWideThreads)
+attn_merge_wide_kernel(const float* __restrict__ ws_o,
+                       const float* __restrict__ ws_ml, int nsplit,
+                       float* __restrict__ out) {
+  __shared__ float sm_m[kMergeGroups][kHeadDim], sm_num[kMergeGroups][kHeadDim],
+      sm_den[kMergeGroups][kHeadDim];
+  const int64_t qh = blockIdx.x;
+  const int ch = threadIdx.x & (kHeadDim - 1), grp = threadIdx.x / kHeadDim;
+  float mr = -INFINITY, num = 0.f, den = 0.f;
+  merge_strided<16>(ws_o + qh * nsplit * kHeadDim, ws_ml + qh * nsplit * 2, nsplit, grp,
+                    kMergeGroups, ch, mr, num, den);
+  sm_m[grp][ch] = mr;
+  sm_num[grp][ch] = num;
+  sm_den[grp][ch] = den;
+  __syncthreads();
+  if (grp == 0) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kMergeGroups; ++u) M = fmaxf(M, sm_m[u][ch]);
+    float d = 0.f, nm = 0.f;
+#pragma unroll
+    for (int u = 0; u < kMergeGroups; ++u) {
+      const float w = exp2_or_zero(sm_m[u][ch], M);
+      d += sm_den[u][ch] * w;
+      nm += sm_num[u][ch] * w;
+    }
+    out[qh * kHeadDim + ch] = d > 0.f ? nm / d : 0.f;
+  }
 }
 
 // Pages per wave the registers allow: at most 4 16-token tiles per wave,
@@ -195,6 +247,23 @@ AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves) {
   return {ppw, nsplit < 1 ? 1 : nsplit};
 }
 
+// Dense plan: the whole row split into balanced ranges, walked in chunks of
+// 8 pages (4 waves x 2 pages) by workgroups that all fit the GPU at once
+// (about 4 per CU at this kernel's register use, 1024 in all), so that no
+// second round of a few workgroups runs alone at the end; rows of many
+// requests get one workgroup each and no merge.
+AttnPlan dense_plan(const quest_paged_kv& kv) {
+  constexpr int64_t kTargetWgs = 1024;
+  constexpr int kDensePpw = 2;
+  const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
+  const int64_t chunks = (kv.max_pages_per_seq + kAttnWaves * kDensePpw - 1) /
+                         (kAttnWaves * kDensePpw);
+  int64_t ns = kTargetWgs / units;
+  if (ns > chunks) ns = chunks;
+  if (ns > 65535) ns = 65535;
+  return {kDensePpw, (int)(ns < 1 ? 1 : ns)};
+}
+
 // Workspace: [partial o: slots x 128 floats][partial (M, den): slots x 2],
 // the second part 256-byte aligned.
 size_t attention_ml_offset(size_t slots) {
@@ -204,8 +273,12 @@ size_t attention_ml_offset(size_t slots) {
 void launch_merge(const quest_paged_kv& kv, const float* ws_o,
                   const float* ws_ml, int nsplit, float* out,
                   hipStream_t stream) {
-  attn_merge_kernel<<<kv.batch * kv.num_q_heads, 256, 0, stream>>>(
-      ws_o, ws_ml, nsplit, out);
+  if (nsplit > kMergeWideMin)
+    attn_merge_wide_kernel<<<kv.batch * kv.num_q_heads, kMergeWideThreads, 0, stream>>>(
+        ws_o, ws_ml, nsplit, out);
+  else
+    attn_merge_kernel<<<kv.batch * kv.num_q_heads, 256, 0, stream>>>(ws_o, ws_ml, nsplit,
+                                                                     out);
 }
 
 namespace {
@@ -255,11 +328,24 @@ bool attention_supported(int group) {
   return group == 1 || group == 2 || group == 4 || group == 8;
 }
 
-size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len) {
-  const Plan pl = attention_plan(kv, list_len);
-  if (pl.nsplit == 1) return 0;
-  const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
+// Bytes of the partials of `nsplit` splits per row (0 for one split: the
+// workgroups write the output themselves).
+static size_t partial_bytes(const quest_paged_kv& kv, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const size_t slots = (size_t)kv.batch * kv.num_q_heads * nsplit;
   return (attention_ml_offset(slots) + slots * 2) * sizeof(float);
+}
+
+// The sparse plan for list_len entries; a list as long as the row
+// (list_len >= max_pages_per_seq, the size quest_decode_attn is asked with)
+// also covers the dense plan.
+size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len) {
+  size_t need = partial_bytes(kv, attention_plan(kv, list_len).nsplit);
+  if (list_len >= kv.max_pages_per_seq) {
+    const size_t d = partial_bytes(kv, dense_plan(kv).nsplit);
+    if (d > need) need = d;
+  }
+  return need;
 }
 
 hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
@@ -268,7 +354,7 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
                             const int32_t* sel, int list_len, float sm_scale,
                             float* out, void* workspace, hipStream_t stream) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
-  const Plan pl = attention_plan(kv, list_len);
+  const Plan pl = sel ? attention_plan(kv, list_len) : dense_plan(kv);
   const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = ws_o ? ws_o + attention_ml_offset(slots) : nullptr;

@@ -256,6 +256,48 @@ __device__ __forceinline__ void merge_half(const float* __restrict__ o,
   }
 }
 
+// Fold the splits s = first, first + stride, ... of channel ch into a
+// running (max, num, den), CHUNK splits per memory round trip, every load of
+// a chunk issued from a clamped split index and masked afterwards.
+template <int CHUNK>
+__device__ __forceinline__ void merge_strided(const float* __restrict__ o,
+                                              const float* __restrict__ ml, int nsplit,
+                                              int first, int stride, int ch, float& mr,
+                                              float& num, float& den) {
+  for (int s0 = first; s0 < nsplit; s0 += stride * CHUNK) {
+    float w[CHUNK], l[CHUNK], x[CHUNK];
+#pragma unroll
+    for (int u = 0; u < CHUNK; ++u) {
+      const int sc = min(s0 + stride * u, nsplit - 1);
+      const float2 m_l = *reinterpret_cast<const float2*>(ml + 2 * sc);
+      w[u] = m_l.x;
+      l[u] = m_l.y;
+      x[u] = o[(int64_t)sc * kHeadDim + ch];
+    }
+#pragma unroll
+    for (int u = 0; u < CHUNK; ++u) {
+      if (s0 + stride * u >= nsplit) {
+        w[u] = -INFINITY;
+        l[u] = 0.f;
+        x[u] = 0.f;
+      }
+    }
+    float mc = mr;
+#pragma unroll
+    for (int u = 0; u < CHUNK; ++u) mc = fmaxf(mc, w[u]);
+    const float sc = exp2_or_zero(mr, mc);
+    num *= sc;
+    den *= sc;
+#pragma unroll
+    for (int u = 0; u < CHUNK; ++u) {
+      const float e = exp2_or_zero(w[u], mc);
+      num += x[u] * e;
+      den += l[u] * e;
+    }
+    mr = mc;
+  }
+}
+
 // Merge nsplit partials of one (request, query head) into out_row[128] with
 // a 256-thread workgroup: partial s is (o[s*128 .. +128], ml[2s] = M,
 // ml[2s+1] = den).  Thread (half, ch) folds channel ch of the splits of its

@@ -107,17 +107,14 @@ def test_longchat_layer_32k_budget_2048():
 def test_longchat_dense_32k_against_oracle():
     """The in-library dense baseline at the headline's size and in the
     benchmark's launch configuration (quest_decode_attn on the LongChat
-    layer: one query head per kv-head, fp16, 32K tokens, 128 splits of 16
-    pages per head merged in one launch) against the oracle's textbook
-    attention over every token of sampled heads."""
+    layer: one query head per kv-head, fp16, 32K tokens, 32 workgroups per
+    head each walking 64 pages in chunks of 8, merged in one launch)
+    against the oracle's textbook attention over every token of sampled
+    heads."""
     wl = synth.longchat_layer_workload()
     C.say(f"[case] dense {wl.name}: 32 heads, ctx 32768")
     c = build(wl)
     kv = c["kv"]
-    # pin the launch plan: 128 splits per head (partials o[128] + (M, den))
-    slots = 32 * 128
-    assert qa.quest_workspace_size(kv, kv.max_pages_per_seq) == \
-        slots * 128 * 4 + slots * 2 * 4
     out = qa.DenseDecode(kv, SM)(c["q"], c["k_pool"], c["v_pool"],
                                  c["page_table"], c["seq_lens"])
     torch.cuda.synchronize()
@@ -168,6 +165,28 @@ def test_gqa8_bf16_layer_32k():
     worst = check_units(c, step, [(0, [0]), (0, [3])], wl.k_pages, wl.group,
                         check_meta=meta)
     C.say(f"  sampled attention max err {worst:.2e}")
+
+
+def test_gqa_dense_layer_many_splits():
+    """The dense call on a GQA layer of the multi-step workload's final size
+    (32 / 8 heads, 32896 tokens = 2056 pages): 128 workgroups per kv-head,
+    uneven 16- and 17-page ranges, merged by the wide merge (more than 32
+    splits), against the oracle on sampled heads."""
+    wl = synth.Workload("gqa_dense_2056", 1, 32, 8, (32896,), 2048, "f16",
+                        outliers=4, base_seed=73)
+    C.say(f"[case] {wl.name}: Hq 32 / Hkv 8, ctx 32896, dense")
+    c = build(wl)
+    out = qa.DenseDecode(c["kv"], SM)(c["q"], c["k_pool"], c["v_pool"],
+                                      c["page_table"], c["seq_lens"])
+    torch.cuda.synchronize()
+    heads = [2, 7]
+    qh = [g * 4 + r for g in heads for r in range(4)]
+    pt = c["page_table"].cpu().numpy().astype(np.int64)
+    lens = c["seq_lens"].cpu().numpy().astype(np.int64)
+    ref = O.dense_attention(C.to64(c["q"][:, qh]), C.to64(c["k_pool"][:, heads]),
+                            C.to64(c["v_pool"][:, heads]), pt, lens, SM, 16)
+    worst = C.assert_attention_close(out.cpu().numpy().astype(np.float64)[:, qh], ref)
+    C.say(f"  dense attention max err {worst:.2e}")
 
 
 def test_page32_layer_128k():
