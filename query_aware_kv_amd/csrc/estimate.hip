@@ -6,14 +6,18 @@
 // Work mapping: a 16-lane DPP row owns one kv-head g of one request and walks
 // blocks of 4 consecutive pages, prefetching the next block's page ids while
 // it scores the current one.  Rows of one wave take consecutive kv-heads,
-// whose metadata sit next to each other in the pool.
+// whose metadata sit next to each other in the pool.  When the kv-heads come
+// in fours, the waves of a workgroup take the same four kv-heads over
+// consecutive blocks: a wave still reads 1 KiB runs of bounds, and the
+// workgroup's 16-byte score stores fill whole 64- or 128-byte pieces of each
+// score row instead of pieces that 4 or 8 workgroups on different XCDs share.
 #include "dev_estimate.h"
 #include "launch.h"
 
 namespace quest {
 namespace {
 
-constexpr int kRowsPerBlock = 16;  // 256 threads
+constexpr int kRowsPerBlock = 16;  // 256 threads when kv-heads do not come in fours
 
 // Extra arguments of the append mode (null otherwise).
 struct EstAppend {
@@ -28,8 +32,10 @@ struct EstAppend {
 // APPEND: first append token L_b - 1 (k_new / v_new) to its page and box,
 // as quest_update_page_meta's append mode; the row that owns that page
 // does it and scores the page with the updated box.
+// quads: Hkv / 4 for the four-head mapping (workgroups of blockDim.x / 64
+// waves), else 0.
 template <DType T, int G, bool PER_HEAD, bool APPEND>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 estimate_kernel(const uint16_t* __restrict__ q,
                 uint16_t* __restrict__ kmin,
                 uint16_t* __restrict__ kmax,
@@ -37,13 +43,23 @@ estimate_kernel(const uint16_t* __restrict__ q,
                 const int32_t* __restrict__ seq_lens,
                 float* __restrict__ scores, int Hkv, int max_pages,
                 int rows_per_head, int num_pool_pages, int page_size,
-                EstAppend ap) {
+                int quads, EstAppend ap) {
   const int b = blockIdx.y;
-  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
-  if (row >= rows_per_head * Hkv) return;  // whole 16-lane rows exit together
-  const int g = row % Hkv;
-  const int jb0 = row / Hkv;
+  int g, jb0;
+  if (quads > 0) {
+    // wave w: kv-heads 4 (x mod quads) .. +3, one per row, of first block
+    // (x / quads) * waves + w
+    const int waves = blockDim.x >> 6;
+    jb0 = (int)(blockIdx.x / quads) * waves + (int)(threadIdx.x >> 6);
+    g = (int)(blockIdx.x % quads) * 4 + (int)((threadIdx.x >> 4) & 3);
+    if (jb0 >= rows_per_head) return;  // whole waves exit together
+  } else {
+    const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+    if (row >= rows_per_head * Hkv) return;  // whole 16-lane rows exit together
+    g = row % Hkv;
+    jb0 = row / Hkv;
+  }
   const int32_t* pt_row = page_table + (int64_t)b * max_pages;
   float* srow = scores + ((int64_t)b * Hkv + g) * (PER_HEAD ? G : 1) * max_pages;
   // The length, the first table entries and q are independent loads.
@@ -114,14 +130,24 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
   int64_t rph = target_rows / ((int64_t)Hkv * kv.batch);
   if (rph < 1) rph = 1;
   if (rph > blocks_per_head) rph = blocks_per_head;
+  // Four-head mapping: 8 waves per workgroup (a full 128-byte line of 8
+  // blocks' scores per kv-head) while that leaves at least 256 workgroups
+  // and a row has more than 4 blocks, else 4.  A row that walks several blocks strides by a multiple of the
+  // waves, so that every step of the workgroup covers aligned blocks.
+  const int quads = Hkv % 4 == 0 ? Hkv / 4 : 0;
+  int waves = 8;
+  if (quads > 0 && (rph <= 4 || (int64_t)quads * ((rph + 7) / 8) * kv.batch < 256)) waves = 4;
+  if (quads > 0 && rph < blocks_per_head && rph >= waves) rph -= rph % waves;
   const int64_t rows = rph * Hkv;
-  dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock),
+  dim3 grid(quads > 0 ? (unsigned)(quads * ((rph + waves - 1) / waves))
+                      : (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock),
             (unsigned)kv.batch);
-  estimate_kernel<T, G, PER_HEAD, APPEND><<<grid, 256, 0, stream>>>(
+  const int threads = quads > 0 ? waves * kWave : kRowsPerBlock * 16;
+  estimate_kernel<T, G, PER_HEAD, APPEND><<<grid, threads, 0, stream>>>(
       static_cast<const uint16_t*>(q),
       static_cast<uint16_t*>(const_cast<void*>(kmin)),
       static_cast<uint16_t*>(const_cast<void*>(kmax)), page_table, seq_lens, scores,
-      Hkv, kv.max_pages_per_seq, (int)rph, kv.num_pool_pages, kv.page_size, ap);
+      Hkv, kv.max_pages_per_seq, (int)rph, kv.num_pool_pages, kv.page_size, quads, ap);
 }
 
 template <DType T, bool PER_HEAD, bool APPEND>
