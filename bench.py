@@ -84,7 +84,13 @@ KERNELS = {
     "attn_merge_kernel": ["attention.hip"] + _ATTN_SRC,
     "union_kernel": ["union.hip", "common.h", "launch.h"],
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_longchat32k.md")
+# rocprofv3 counter summaries, one per workload; a line reports the record
+# of its own workload only
+TRAFFIC_FILES = {
+    "longchat": os.path.join(ROOT, "profiles", "hbm_traffic_longchat32k.md"),
+    "ragged": os.path.join(ROOT, "profiles", "kernels_ragged_batch.md"),
+    "gqa_multistep": os.path.join(ROOT, "profiles", "kernels_gqa_multistep.md"),
+}
 
 
 # ------------------------------------------------------------- byte model
@@ -141,13 +147,13 @@ def sources_digest(names):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel):
+def recorded_traffic(kernel, path):
     """(HBM bytes per launch, sources digest) of `kernel` from the committed
-    rocprofv3 counter summary, or (None, digest) if there is none or the
-    kernel's sources changed since the counters were taken."""
+    rocprofv3 counter summary at `path`, or (None, digest) if there is none
+    or the kernel's sources changed since the counters were taken."""
     digest = sources_digest(KERNELS[kernel])
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None, digest
     m = re.search(r"^\| %s \| (\d+) \| ([0-9a-f]+) \|" % re.escape(kernel), text, re.M)
@@ -430,26 +436,28 @@ def kernel_bytes(avg, kv, k):
     }
 
 
-def roofline(ku, kb, traffic_recorded=True):
+def roofline(ku, kb, traffic_file=None):
     """Roofline of the kernel with the most time per step: algorithmic bytes
     per launch (the step's byte model, kernel_bytes) over its HIP-event
     time, against the 8 TB/s HBM peak.  `traffic` is the rocprofv3 counter
-    figure recorded in profiles/ for that kernel while its sources are
-    unchanged (else null); it is not measured in this run."""
+    figure that `traffic_file` (the same workload's summary in profiles/)
+    records for that kernel while its sources are unchanged, else null; it
+    is not measured in this run."""
     dom = max(ku, key=lambda n: ku[n])
     us = ku[dom]
     alg, over = kb[dom]
     achieved = alg / (us * 1e-6) / 1e9
-    traffic, digest = recorded_traffic(dom) if (traffic_recorded and dom in KERNELS) \
-        else (None, None)
+    traffic, digest = recorded_traffic(dom, traffic_file) \
+        if (traffic_file and dom in KERNELS) else (None, None)
     return {"bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "traffic_source": (f"recorded: {os.path.relpath(TRAFFIC_FILE, ROOT)} "
+            "traffic_source": (f"recorded: {os.path.relpath(traffic_file, ROOT)} "
                                f"(rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated), "
                                f"sources digest {digest}" if traffic is not None else
-                               "null: no counter record for the current sources"),
+                               "null: no counter record of this workload for the "
+                               "current sources"),
             "kernel": dom, "kernel_us": round(us, 3),
             "bytes_per_launch": int(alg),
             "overhead_bytes_per_launch": {k_: int(v) for k_, v in over.items()}}
@@ -506,7 +514,7 @@ def bench_longchat(args, torch, qa, synth):
         "step_us_by_select": r["by_select"],
         "kernel_us": {n: round(v, 3) for n, v in r["kernel_us"].items()},
         "other_call_us": {n: round(v, 3) for n, v in r["other_us"].items()},
-        "roofline": roofline(r["kernel_us"], r["kernel_bytes"]),
+        "roofline": roofline(r["kernel_us"], r["kernel_bytes"], TRAFFIC_FILES["longchat"]),
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu:
@@ -520,7 +528,7 @@ def bench_longchat(args, torch, qa, synth):
     return line
 
 
-def single_layer_line(r, rot):
+def single_layer_line(r, rot, traffic_file=None):
     """The figures every single-layer workload reports."""
     tb = r["t_batch"]
     us = tb["mean"]
@@ -532,7 +540,7 @@ def single_layer_line(r, rot):
          "effective_GBps": round(r["bytes"]["total"] / (us * 1e-6) / 1e9, 1),
          "hbm_frac": round(r["bytes"]["total"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
          "kernel_us": {n: round(v, 3) for n, v in r["kernel_us"].items()},
-         "roofline": roofline(r["kernel_us"], r["kernel_bytes"])}
+         "roofline": roofline(r["kernel_us"], r["kernel_bytes"], traffic_file)}
     if us_dense:
         d.update(dense_us_per_step=round(us_dense, 3),
                  speedup_vs_dense=round(us_dense / us, 3),
@@ -544,7 +552,7 @@ def bench_ragged(args, torch, qa, synth, full=True):
     wl = synth.ragged_batch_workload()
     r = time_single_layer(args, torch, qa, synth, [wl],
                           with_dense=not args.no_dense and full, full=full)
-    d = single_layer_line(r, 1)
+    d = single_layer_line(r, 1, TRAFFIC_FILES["ragged"])
     d["config"] = {"workload": "ragged_batch_decode", "batch": wl.batch,
                    "q_heads": 32, "kv_heads": 32, "ctx_min": min(wl.seq_lens),
                    "ctx_max": max(wl.seq_lens), "budget_tokens": 2048,
@@ -741,7 +749,7 @@ def bench_gqa_multistep(args, torch, qa, synth, full=True):
                 "attn_merge_kernel": wl.layers - wl.dense_layers,
                 "attn_split_kernel+attn_merge_kernel (dense)": wl.dense_layers}
     dom = max(ku, key=lambda c_: ku[c_] * per_step[c_])
-    rl = roofline({dom: ku[dom]}, {dom: kb[dom]}, traffic_recorded=False)
+    rl = roofline({dom: ku[dom]}, {dom: kb[dom]}, TRAFFIC_FILES["gqa_multistep"])
     d = {"us_per_step": round(us, 3),
          "step_us_p10_p50_p90": [round(pct(per, q_), 3) for q_ in (10, 50, 90)],
          "timed_steps": nsteps,
@@ -877,7 +885,7 @@ def bench_gqa_union(args, torch, qa, synth):
                       "pages_per_kv_head": round(sm_["pages"], 1)},
         "union_pages_over_k": round(u["pages"] / k, 3),
         "union_call_us": {c_: round(v, 3) for c_, v in t_calls.items()},
-        "roofline": roofline(ku, kb, traffic_recorded=False),
+        "roofline": roofline(ku, kb),
         "group": G, "gpu": torch.cuda.get_device_name(0)}
 
 

@@ -98,9 +98,26 @@ def test_roofline_takes_the_slowest_kernel():
     kb = {"estimate_kernel": (33_570_816, {}),
           "topk_attn_kernel": (33_562_624, {"scores_read": 262144}),
           "attn_merge_kernel": (16384, {})}
-    r = bench.roofline(ku, kb, traffic_recorded=False)
+    r = bench.roofline(ku, kb)
     assert r["kernel"] == "topk_attn_kernel" and r["kernel_us"] == 12.0
     assert abs(r["achieved"] - 33_562_624 / 12e-6 / 1e9) < 0.1
     assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
     assert r["overhead_bytes_per_launch"] == {"scores_read": 262144}
     assert r["traffic"] is None
+
+
+def test_recorded_traffic_needs_its_workload_file_and_current_sources(tmp_path):
+    digest = bench.sources_digest(bench.KERNELS["topk_attn_kernel"])
+    f = tmp_path / "traffic.md"
+    f.write_text("| kernel | HBM bytes per launch | sources digest |\n|---|---|---|\n"
+                 f"| topk_attn_kernel | 36000000 | {digest} |\n"
+                 "| estimate_kernel | 34000000 | 0000000000000000 |\n")
+    assert bench.recorded_traffic("topk_attn_kernel", str(f)) == (36000000, digest)
+    # a digest of other sources: no record
+    assert bench.recorded_traffic("estimate_kernel", str(f))[0] is None
+    assert bench.recorded_traffic("topk_attn_kernel", str(tmp_path / "none.md"))[0] is None
+    ku = {"topk_attn_kernel": 12.0}
+    kb = {"topk_attn_kernel": (33_562_624, {})}
+    r = bench.roofline(ku, kb, str(f))
+    assert r["traffic"] == 36000000 and digest in r["traffic_source"]
+    assert bench.roofline(ku, kb)["traffic"] is None
