@@ -447,8 +447,14 @@ def roofline(ku, kb, traffic_file=None):
     us = ku[dom]
     alg, over = kb[dom]
     achieved = alg / (us * 1e-6) / 1e9
-    traffic, digest = recorded_traffic(dom, traffic_file) \
-        if (traffic_file and dom in KERNELS) else (None, None)
+    # a call of several kernels ("a+b"): the sum of their records
+    parts = [p_.strip() for p_ in dom.split("+")]
+    traffic, digest = None, None
+    if traffic_file and all(p_ in KERNELS for p_ in parts):
+        recs = [recorded_traffic(p_, traffic_file) for p_ in parts]
+        digest = ",".join(r_[1] for r_ in recs)
+        if all(r_[0] is not None for r_ in recs):
+            traffic = sum(r_[0] for r_ in recs)
     return {"bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -121,3 +121,15 @@ def test_recorded_traffic_needs_its_workload_file_and_current_sources(tmp_path):
     r = bench.roofline(ku, kb, str(f))
     assert r["traffic"] == 36000000 and digest in r["traffic_source"]
     assert bench.roofline(ku, kb)["traffic"] is None
+
+
+def test_recorded_traffic_of_a_two_kernel_call_is_the_sum(tmp_path):
+    d1 = bench.sources_digest(bench.KERNELS["attn_split_kernel"])
+    d2 = bench.sources_digest(bench.KERNELS["attn_merge_kernel"])
+    f = tmp_path / "traffic.md"
+    f.write_text(f"| attn_split_kernel | 1000 | {d1} |\n| attn_merge_kernel | 24 | {d2} |\n")
+    ku = {"attn_split_kernel+attn_merge_kernel": 10.0}
+    kb = {"attn_split_kernel+attn_merge_kernel": (1000, {})}
+    assert bench.roofline(ku, kb, str(f))["traffic"] == 1024
+    f.write_text(f"| attn_split_kernel | 1000 | {d1} |\n")
+    assert bench.roofline(ku, kb, str(f))["traffic"] is None
