@@ -1329,6 +1329,28 @@ def pmc_summary(d, copy_mib):
     return "\n".join(head + out + calls) + "\n"
 
 
+def counter_table(d):
+    """Markdown: the median of each counter per kernel and grid over its
+    dispatches, from rocprofv3 --pmc CSVs under d (raw counts, uncalibrated)."""
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            m = re.search(r"quest::\(anonymous namespace\)::(\w+)(<[^(]*>)?", row["Kernel_Name"])
+            if not m:
+                continue
+            key = (m.group(1) + (m.group(2) or ""), row.get("Grid_Size", "?"))
+            vals.setdefault(key, {}).setdefault(row["Counter_Name"], []).append(
+                float(row["Counter_Value"]))
+    names = sorted({c for v in vals.values() for c in v})
+    out = ["| kernel | grid | dispatches | " + " | ".join(names) + " |",
+           "|---|---|---|" + "---|" * len(names)]
+    for (k, grid), v in sorted(vals.items()):
+        n = max(len(x) for x in v.values())
+        out.append(f"| `{k}` | {grid} | {n} | " + " | ".join(
+            f"{statistics.median(v[c]):.0f}" if c in v else "" for c in names) + " |")
+    return "\n".join(out) + "\n"
+
+
 def trace_summary(d):
     """Markdown: per-kernel dispatch count, mean and median duration (ns)
     and grid from rocprofv3 --kernel-trace CSVs under d."""
@@ -1383,6 +1405,8 @@ def main():
                     help="only summarise rocprofv3 counter CSVs under DIR")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="only summarise rocprofv3 --kernel-trace CSVs under DIR")
+    ap.add_argument("--counter-table", metavar="DIR",
+                    help="only tabulate rocprofv3 --pmc counters under DIR per kernel")
     ap.add_argument("--copy-mib", type=int, default=512,
                     help="size the --copy-probe runs used (for --pmc-summary)")
     args = ap.parse_args()
@@ -1391,6 +1415,9 @@ def main():
         return
     if args.pmc_summary:
         sys.stdout.write(pmc_summary(args.pmc_summary, args.copy_mib))
+        return
+    if args.counter_table:
+        sys.stdout.write(counter_table(args.counter_table))
         return
     if args.copy_probe:
         import torch
