@@ -7,6 +7,7 @@
 // arithmetic (PPW * 8 KiB in flight per wave).  The four waves meet in LDS;
 // with one split per row the workgroup writes the output directly, otherwise
 // a partial (o[128], M, den) per query head, which the merge kernel combines.
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -223,17 +224,24 @@ using Plan = AttnPlan;
 
 }  // namespace
 
+namespace {
+int64_t dense_resident(const quest_paged_kv& kv, int ppw);
+}  // namespace
+
 // Pages per wave: as many as the registers allow while the grid keeps at
-// least ~4096 waves (16 per CU) to spread the loads over all 256 CUs.  The
-// 8-wave Top-K + attention workgroups repeat the row's selection each, so
-// fewer, fuller ones pay there: at least 256 of them (2048 waves), with at
-// most 2 pages per wave (4 made the kernel slower through its registers).
-// Measured on the 32-head layers: 8 splits of 2 pages per wave beat 16 of
-// one at budgets up to 2048 tokens.  The 8-wave split count never exceeds
-// the 4-wave one (PPW 4 for 4 waves needs units * ceil(L/16) >= 1024, which
-// gives 8 waves PPW 2 and the same count; PPW 2 for 4 waves gives 8 waves
-// PPW 2 and half the count), so quest_workspace_size, planned for
-// kAttnWaves, covers every plan.
+// least ~4096 waves (16 per CU) to spread the loads over all 256 CUs -- or,
+// for kernels of which fewer workgroups fit the GPU at once (query groups:
+// 2 per CU at 2 pages per wave), at least as many workgroups as fit.  A grid
+// between one and two resident rounds is cut to one round of balanced
+// ranges instead of leaving a partial second round (a GQA layer's union
+// lists: 17.4 -> 15.5 us, 512 workgroups of 2 pages per wave where there
+// were 1024 of one).  The 8-wave Top-K + attention workgroups repeat the
+// row's selection each, so fewer, fuller ones pay there: at least 256 of
+// them (2048 waves), with at most 2 pages per wave (4 made the kernel slower
+// through its registers).  Measured on the 32-head layers: 8 splits of 2
+// pages per wave beat 16 of one at budgets up to 2048 tokens.
+// quest_workspace_size covers the 4-wave and the 8-wave plan of a list (and,
+// for whole rows, the dense plan).
 AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves) {
   const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
   const bool topk_wg = waves == 8;
@@ -242,9 +250,16 @@ AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves) {
   int ppw = 1;
   for (int cand = min(cap, max_ppw(kv.page_size / kTileRows)); cand > 1; cand /= 2) {
     const int64_t ns = (list_len + waves * cand - 1) / (waves * cand);
-    if (units * ns >= min_wgs) { ppw = cand; break; }
+    const int64_t need =
+        topk_wg ? min_wgs : std::min<int64_t>(min_wgs, dense_resident(kv, cand));
+    if (units * ns >= need) { ppw = cand; break; }
   }
-  const int nsplit = (list_len + waves * ppw - 1) / (waves * ppw);
+  int nsplit = (list_len + waves * ppw - 1) / (waves * ppw);
+  if (!topk_wg) {
+    const int64_t res = dense_resident(kv, ppw);
+    if (units * nsplit > res && units * nsplit < 2 * res)
+      nsplit = (int)(res / units > 0 ? res / units : 1);
+  }
   return {ppw, nsplit < 1 ? 1 : nsplit};
 }
 
@@ -396,11 +411,13 @@ static size_t partial_bytes(const quest_paged_kv& kv, int nsplit) {
   return (attention_ml_offset(slots) + slots * 2) * sizeof(float);
 }
 
-// The sparse plan for list_len entries; a list as long as the row
-// (list_len >= max_pages_per_seq, the size quest_decode_attn is asked with)
-// also covers the dense plan.
+// The sparse plans (4-wave attention, 8-wave Top-K + attention) for
+// list_len entries; a list as long as the row (list_len >= max_pages_per_seq,
+// the size quest_decode_attn is asked with) also covers the dense plan.
 size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len) {
   size_t need = partial_bytes(kv, attention_plan(kv, list_len).nsplit);
+  const size_t t = partial_bytes(kv, attention_plan(kv, list_len, 8).nsplit);
+  if (t > need) need = t;
   if (list_len >= kv.max_pages_per_seq) {
     const size_t d = partial_bytes(kv, dense_plan(kv).nsplit);
     if (d > need) need = d;

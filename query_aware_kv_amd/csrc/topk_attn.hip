@@ -253,9 +253,8 @@ struct TaLayout {
 
 bool ta_layout(const quest_paged_kv& kv, int k_pages, void* workspace, TaLayout& t) {
   t.pl = attention_plan(kv, k_pages, kTaWaves);
-  // the caller's workspace holds the partials of the 4-wave plan, which
-  // never has fewer splits (see attention_plan); refuse rather than overrun
-  if (t.pl.nsplit > attention_plan(kv, k_pages).nsplit) return false;
+  // the caller's workspace (attention_workspace_bytes, checked by every
+  // entry point) holds the partials of this plan
   const size_t slots = (size_t)kv.batch * kv.num_q_heads * t.pl.nsplit;
   t.ws_o = static_cast<float*>(workspace);
   t.ws_ml = t.ws_o ? t.ws_o + attention_ml_offset(slots) : nullptr;
