@@ -45,10 +45,15 @@ CPU-oracle baseline timed on a bounded sample of the same workload (one
 thread, and every kv-head over one process per host core).
 
     python bench.py --pmc-summary DIR
+    python bench.py --trace-summary DIR
+    python bench.py --counter-table DIR
 
-turns the CSV output of rocprofv3 FETCH_SIZE / WRITE_SIZE runs (DIR/fetch,
-DIR/write, and DIR/cfetch, DIR/cwrite over ``--copy-probe``) into the
-per-call HBM traffic summary kept under profiles/.
+turn rocprofv3 CSV output into the summaries kept under profiles/: the
+calibrated HBM traffic per kernel from FETCH_SIZE / WRITE_SIZE runs
+(DIR/fetch, DIR/write, and DIR/cfetch, DIR/cwrite over ``--copy-probe``),
+recorded with a digest of each kernel's sources and read back as the
+``roofline.traffic`` of the same workload's line; per-kernel durations
+from a --kernel-trace run; any other counters per kernel.
 """
 from __future__ import annotations
 
