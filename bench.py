@@ -33,6 +33,8 @@ Workloads (each prints ONE JSON line):
 * ``host_kv``: the longchat layer with K/V in pinned host memory (metadata
   in HBM): only the kept pages cross the host link; its roofline is the
   link's measured read ceiling.
+* ``head_groups``: the longchat layer split into 1, 2 or 4 head groups whose
+  chains run one after another or as parallel branches of one HIP graph.
 
 Inputs are seeded synthetic tensors drawn on the GPU and resident in HBM
 before timing starts.  The line carries the step time (the metric),
@@ -973,6 +975,81 @@ def bench_page32(args, torch, qa, synth):
         "points": rows, "gpu": torch.cuda.get_device_name(0)}
 
 
+def bench_head_groups(args, torch, qa, synth):
+    """The LongChat layer split into 1, 2 or 4 head groups, each group an
+    estimate -> Top-K + attention chain over its own caches (32 / groups
+    heads each, so the bytes per step equal the headline's).  The chains run
+    one after another on one stream ("serial") or as parallel branches of
+    one HIP graph, one default-priority stream per group ("parallel"): does
+    overlapping one group's selection and K/V stream with another group's
+    bounds pay?  Same protocol as the headline (back-to-back graph replays
+    over rotating caches, >= --steps steps)."""
+    import dataclasses
+    rot = 8
+    variants = args.hg_variants.split(",")
+    side = [torch.cuda.Stream() for _ in range(4)]   # default priority
+    sm = 1.0 / math.sqrt(128)
+    out = {}
+    for ng in (1, 2, 4):
+        hk = 32 // ng
+        caches = []
+        for r in range(rot):
+            grp = []
+            for gi in range(ng):
+                wl = dataclasses.replace(synth.longchat_layer_workload(seed=1 + 1000 * r + 97 * gi),
+                                         num_q_heads=hk, num_kv_heads=hk,
+                                         name=f"head_groups{ng}_{r}_{gi}")
+                c = make_layer(qa, synth, wl)
+                grp.append((c, qa.SparseDecodeStep(c["kv"], wl.k_pages, sm, select="attention")))
+            caches.append(grp)
+
+        def chain(c, st):
+            st(c["q"], c["k_pool"], c["v_pool"], c["kmin"], c["kmax"], c["page_table"],
+               c["seq_lens"])
+
+        def serial(i):
+            for c, st in caches[i]:
+                chain(c, st)
+
+        def parallel(i):
+            main = torch.cuda.current_stream()
+            for j, (c, st) in enumerate(caches[i]):
+                side[j].wait_stream(main)
+                with torch.cuda.stream(side[j]):
+                    chain(c, st)
+            for j in range(len(caches[i])):
+                main.wait_stream(side[j])
+
+        for i in range(rot):
+            serial(i)
+        torch.cuda.synchronize()
+        for v, fn in (("serial", serial), ("parallel", parallel)):
+            if v not in variants or (v == "parallel" and ng == 1):
+                continue
+            t = graph_batch(torch, fn, rot, max(args.steps, 100))
+            out[f"{v}_{ng}_groups"] = {
+                "us_per_step": round(t["mean"], 3),
+                "step_us_p10_p50_p90": [round(t[p_], 3) for p_ in ("p10", "p50", "p90")],
+                "timed_steps": t["steps"]}
+            print(json.dumps({"progress": f"{v}_{ng}_groups", "us_per_step": t["mean"]}),
+                  file=sys.stderr, flush=True)
+        del caches
+        torch.cuda.empty_cache()
+    one = out.get("serial_1_groups", {}).get("us_per_step")
+    return {
+        "metric": "µs/decode step, LongChat layer (32 heads, 32K ctx, 2048-token "
+                  "budget) as 1, 2 or 4 head groups, serial or parallel graph branches",
+        "value": one, "unit": "us/step", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (as longchat; each head group its own caches)",
+        "config": {"workload": "longchat_head_groups", "groups": [1, 2, 4],
+                   "rotating_caches": rot, "variants": variants},
+        "timing": "each variant: back-to-back replays of one HIP graph holding one "
+                  "step on each rotating cache, HIP events around each replay",
+        "results": out, "gpu": torch.cuda.get_device_name(0)}
+
+
 def bench_host_kv(args, torch, qa, synth):
     """The LongChat layer with its K/V pools in pinned host memory: metadata,
     scores and selection stay in HBM, and attention reads only the kept
@@ -1356,10 +1433,14 @@ def counter_table(d):
     return "\n".join(out) + "\n"
 
 
+STEP_KERNELS = ("estimate_kernel", "topk_kernel", "topk_attn_kernel", "attn_split_kernel",
+                "attn_merge_kernel", "attn_merge_wide_kernel")
+
+
 def trace_summary(d):
     """Markdown: per-kernel dispatch count, mean and median duration (ns)
     and grid from rocprofv3 --kernel-trace CSVs under d."""
-    rows = {}
+    rows, spans = {}, []
     for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
         for row in csv.DictReader(open(f)):
             n = row["Kernel_Name"]
@@ -1369,13 +1450,33 @@ def trace_summary(d):
             key = (m.group(1) + (m.group(2) or ""),
                    f"{row.get('Grid_Size_X', row.get('Grid_Size', '?'))}x"
                    f"{row.get('Grid_Size_Y', '1')}/{row.get('Workgroup_Size_X', '?')}")
-            dur = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
-            rows.setdefault(key, []).append(dur)
+            t0, t1 = int(row["Start_Timestamp"]), int(row["End_Timestamp"])
+            rows.setdefault(key, []).append(t1 - t0)
+            if m.group(1) in STEP_KERNELS:
+                spans.append((t0, t1))
     out = ["| kernel | grid (threads x, y / workgroup) | dispatches | mean ns | median ns |",
            "|---|---|---|---|---|"]
     for (k, grid), v in sorted(rows.items(), key=lambda kv: -statistics.mean(kv[1])):
         out.append(f"| `{k}` | {grid} | {len(v)} | {statistics.mean(v):.0f} | "
                    f"{statistics.median(v):.0f} |")
+    # concurrency of the step kernels: the sum of their durations over the
+    # union of their busy intervals (1.0: never two at once)
+    iv = sorted(spans)
+    busy, cur_s, cur_e = 0, None, None
+    for a, b in iv:
+        if cur_e is None or a > cur_e:
+            if cur_e is not None:
+                busy += cur_e - cur_s
+            cur_s, cur_e = a, b
+        else:
+            cur_e = max(cur_e, b)
+    if cur_e is not None:
+        busy += cur_e - cur_s
+    total = sum(b - a for a, b in iv)
+    if busy:
+        out += ["", f"Step kernels (estimate, Top-K, attention, merge): {total / 1e3:.1f} us "
+                f"of durations over {busy / 1e3:.1f} us busy, concurrency "
+                f"{total / busy:.2f}."]
     return "\n".join(out) + "\n"
 
 
@@ -1386,7 +1487,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="longchat",
                     choices=["longchat", "gqa_multistep", "ragged", "sweep",
-                             "gqa_union", "page32", "host_kv"])
+                             "gqa_union", "page32", "host_kv", "head_groups"])
     ap.add_argument("--select", default="auto",
                     choices=["auto", "attention", "separate"],
                     help="where the sparse step runs its Top-K (SparseDecodeStep)")
@@ -1410,6 +1511,8 @@ def main():
                     help="only summarise rocprofv3 counter CSVs under DIR")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="only summarise rocprofv3 --kernel-trace CSVs under DIR")
+    ap.add_argument("--hg-variants", default="serial,parallel",
+                    help="head_groups workload: which issue orders to time")
     ap.add_argument("--counter-table", metavar="DIR",
                     help="only tabulate rocprofv3 --pmc counters under DIR per kernel")
     ap.add_argument("--copy-mib", type=int, default=512,
@@ -1448,7 +1551,7 @@ def main():
     fn = {"longchat": bench_longchat, "gqa_multistep": bench_gqa_multistep,
           "ragged": bench_ragged, "sweep": bench_sweep,
           "gqa_union": bench_gqa_union, "page32": bench_page32,
-          "host_kv": bench_host_kv}[args.workload]
+          "host_kv": bench_host_kv, "head_groups": bench_head_groups}[args.workload]
     print(json.dumps(fn(args, torch, qa, synth)), flush=True)
 
 
