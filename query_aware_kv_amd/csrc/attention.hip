@@ -225,6 +225,8 @@ using Plan = AttnPlan;
 }  // namespace
 
 namespace {
+// workgroups of the attention instance with `ppw` pages per wave that the
+// current GPU holds at once (defined below)
 int64_t dense_resident(const quest_paged_kv& kv, int ppw);
 }  // namespace
 
@@ -292,6 +294,8 @@ int64_t resident_wgs() {
   return n;
 }
 
+// The same for the instance a plan of `ppw` pages per wave launches (4 only
+// for 16-token pages: max_ppw).
 int64_t dense_resident(const quest_paged_kv& kv, int ppw) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
   auto by_g = [&](auto tt, auto ss) -> int64_t {
@@ -299,7 +303,10 @@ int64_t dense_resident(const quest_paged_kv& kv, int ppw) {
     constexpr int SS = decltype(ss)::value;
     auto pick = [&](auto gg) -> int64_t {
       constexpr int GG = decltype(gg)::value;
-      return ppw == 2 ? resident_wgs<TT, GG, 2, SS>() : resident_wgs<TT, GG, 1, SS>();
+      if constexpr (SS == 1) {
+        if (ppw >= 4) return resident_wgs<TT, GG, 4, SS>();
+      }
+      return ppw >= 2 ? resident_wgs<TT, GG, 2, SS>() : resident_wgs<TT, GG, 1, SS>();
     };
     if (G == 1) return pick(std::integral_constant<int, 1>{});
     if (G == 2) return pick(std::integral_constant<int, 2>{});

@@ -132,8 +132,11 @@ void launch_t(const quest_paged_kv& kv, const void* q, const void* kmin,
   if (rph > blocks_per_head) rph = blocks_per_head;
   // Four-head mapping: 8 waves per workgroup (a full 128-byte line of 8
   // blocks' scores per kv-head) while that leaves at least 256 workgroups
-  // and a row has more than 4 blocks, else 4.  A row that walks several blocks strides by a multiple of the
-  // waves, so that every step of the workgroup covers aligned blocks.
+  // and a row has more than 4 blocks, else 4.  A row that walks several
+  // blocks strides by a multiple of the waves, so that every step of the
+  // workgroup covers aligned blocks.  Measured on the 32-head LongChat
+  // layer: 8.56 us against 9.44 us with 16 kv-heads of one block per
+  // 4-wave workgroup, and 9.59 us with 16 waves.
   const int quads = Hkv % 4 == 0 ? Hkv / 4 : 0;
   int waves = 8;
   if (quads > 0 && (rph <= 4 || (int64_t)quads * ((rph + 7) / 8) * kv.batch < 256)) waves = 4;
