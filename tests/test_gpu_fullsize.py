@@ -167,14 +167,16 @@ def test_gqa8_bf16_layer_32k():
     C.say(f"  sampled attention max err {worst:.2e}")
 
 
-def test_gqa_dense_layer_many_splits():
+@pytest.mark.parametrize("S", [16, 32])
+def test_gqa_dense_layer_many_splits(S):
     """The dense call on a GQA layer of the multi-step workload's final size
-    (32 / 8 heads, 32896 tokens = 2056 pages): 128 workgroups per kv-head,
-    uneven 16- and 17-page ranges, merged by the wide merge (more than 32
-    splits), against the oracle on sampled heads."""
-    wl = synth.Workload("gqa_dense_2056", 1, 32, 8, (32896,), 2048, "f16",
-                        outliers=4, base_seed=73)
-    C.say(f"[case] {wl.name}: Hq 32 / Hkv 8, ctx 32896, dense")
+    (32 / 8 heads, 32896 tokens: 2056 16-token or 1028 32-token pages): as
+    many workgroups as the GPU holds at once (96 or 64 per kv-head at this
+    kernel's occupancy), uneven page ranges, merged by the wide merge (more
+    than 32 splits), against the oracle on sampled heads."""
+    wl = synth.Workload(f"gqa_dense_{S}", 1, 32, 8, (32896,), 2048, "f16",
+                        page_size=S, outliers=4, base_seed=73)
+    C.say(f"[case] {wl.name}: Hq 32 / Hkv 8, ctx 32896, {S}-token pages, dense")
     c = build(wl)
     out = qa.DenseDecode(c["kv"], SM)(c["q"], c["k_pool"], c["v_pool"],
                                       c["page_table"], c["seq_lens"])
@@ -184,7 +186,7 @@ def test_gqa_dense_layer_many_splits():
     pt = c["page_table"].cpu().numpy().astype(np.int64)
     lens = c["seq_lens"].cpu().numpy().astype(np.int64)
     ref = O.dense_attention(C.to64(c["q"][:, qh]), C.to64(c["k_pool"][:, heads]),
-                            C.to64(c["v_pool"][:, heads]), pt, lens, SM, 16)
+                            C.to64(c["v_pool"][:, heads]), pt, lens, SM, S)
     worst = C.assert_attention_close(out.cpu().numpy().astype(np.float64)[:, qh], ref)
     C.say(f"  dense attention max err {worst:.2e}")
 
