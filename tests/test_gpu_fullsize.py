@@ -191,6 +191,41 @@ def test_gqa_dense_layer_many_splits(S):
     C.say(f"  dense attention max err {worst:.2e}")
 
 
+def test_union_layer_32k_against_oracle():
+    """The union rule ("Guide to Quest", Best Practices 2) on the bench's
+    GQA layer (32 / 8 heads, 32K, 2048-token budget): per-head bounds,
+    per-head Top-K, the union and the attention over it (8 rows of up to
+    512 entries: 2 pages per wave, 64 splits, the wide merge), against the
+    oracle on two sampled kv-heads."""
+    wl = synth.Workload("gqa_union_32k", 1, 32, 8, (32768,), 2048, "f16",
+                        outliers=4, base_seed=74)
+    C.say(f"[case] {wl.name}: Hq 32 / Hkv 8, ctx 32768, union of per-head Top-K")
+    c = build(wl)
+    kv, k, G = c["kv"], wl.k_pages, 4
+    kmin, kmax = C.gpu_meta(c)
+    st = qa.UnionDecodeStep(kv, k, SM)
+    out = st(c["q"], c["k_pool"], c["v_pool"], kmin, kmax, c["page_table"], c["seq_lens"])
+    torch.cuda.synchronize()
+    heads = [1, 6]
+    qh = [g * G + r for g in heads for r in range(G)]
+    pt = c["page_table"].cpu().numpy().astype(np.int64)
+    lens = c["seq_lens"].cpu().numpy().astype(np.int64)
+    q = C.to64(c["q"][:, qh])
+    kp, vp = C.to64(c["k_pool"][:, heads]), C.to64(c["v_pool"][:, heads])
+    omin, omax = O.page_meta(kp, pt, lens, 16)
+    s_ora = O.estimate_heads(q, omin, omax, pt, lens, 16, kv.max_pages_per_seq)
+    C.assert_scores_close(st.scores.cpu().numpy().astype(np.float64)[:, qh], s_ora, lens)
+    sel_heads = st.sel_heads.cpu().numpy().astype(np.int64)[:, qh]
+    C.assert_sets_match(sel_heads, s_ora, lens, k)
+    sel = st.sel.cpu().numpy().astype(np.int64)[:, heads]
+    assert np.array_equal(sel, O.union_pages(sel_heads, G))
+    kept = [int((sel[0, i] >= 0).sum()) for i in range(len(heads))]
+    C.say(f"  union keeps {kept} pages of {G * k} slots")
+    ref = O.sparse_attention(q, kp, vp, pt, lens, sel, SM, 16)
+    worst = C.assert_attention_close(out.cpu().numpy().astype(np.float64)[:, qh], ref)
+    C.say(f"  union attention max err {worst:.2e}")
+
+
 def test_page32_layer_128k():
     """32-token pages at 128K context with a 2048-token budget (64 pages of
     4096 per head), 32 heads, fp16."""
