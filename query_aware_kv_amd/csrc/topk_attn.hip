@@ -251,14 +251,15 @@ struct TaLayout {
   float* ws_ml;
 };
 
-bool ta_layout(const quest_paged_kv& kv, int k_pages, void* workspace, TaLayout& t) {
+TaLayout ta_layout(const quest_paged_kv& kv, int k_pages, void* workspace) {
+  TaLayout t;
   t.pl = attention_plan(kv, k_pages, kTaWaves);
   // the caller's workspace (attention_workspace_bytes, checked by every
   // entry point) holds the partials of this plan
   const size_t slots = (size_t)kv.batch * kv.num_q_heads * t.pl.nsplit;
   t.ws_o = static_cast<float*>(workspace);
   t.ws_ml = t.ws_o ? t.ws_o + attention_ml_offset(slots) : nullptr;
-  return true;
+  return t;
 }
 
 }  // namespace
@@ -283,8 +284,7 @@ hipError_t launch_topk_attention_noalloc(const quest_paged_kv& kv, const void* q
 hipError_t launch_topk_attention_merge(const quest_paged_kv& kv, int k_pages,
                                        void* workspace, float* out,
                                        hipStream_t stream) {
-  TaLayout t;
-  if (!ta_layout(kv, k_pages, workspace, t)) return hipErrorInvalidValue;
+  const TaLayout t = ta_layout(kv, k_pages, workspace);
   if (t.pl.nsplit > 1) launch_merge(kv, t.ws_o, t.ws_ml, t.pl.nsplit, out, stream);
   return hipGetLastError();
 }
@@ -297,8 +297,7 @@ hipError_t launch_topk_attention(const quest_paged_kv& kv, const void* q,
                                  float sm_scale, int32_t* sel, float* out,
                                  void* workspace, hipStream_t stream, bool merge) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
-  TaLayout t;
-  if (!ta_layout(kv, k_pages, workspace, t)) return hipErrorInvalidValue;
+  const TaLayout t = ta_layout(kv, k_pages, workspace);
   const AttnPlan pl = t.pl;
   float* ws_o = t.ws_o;
   float* ws_ml = t.ws_ml;

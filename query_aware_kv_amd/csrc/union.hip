@@ -16,8 +16,8 @@ constexpr int kUnionThreads = 256;
 constexpr int kUnionWords = kTopkMaxPages / 32;  // bitmap of up to 32768 pages
 
 __global__ void __launch_bounds__(kUnionThreads)
-union_kernel(const int32_t* __restrict__ sel_heads, int G, int k, int Hkv,
-             int max_pages, int32_t* __restrict__ sel_union) {
+union_kernel(const int32_t* __restrict__ sel_heads, int G, int k, int max_pages,
+             int32_t* __restrict__ sel_union) {
   __shared__ uint32_t bm[kUnionWords];
   __shared__ uint32_t wsum[kUnionThreads / kWave];
   const int unit = blockIdx.x;  // b * Hkv + g
@@ -62,7 +62,7 @@ hipError_t launch_union(const quest_paged_kv& kv, const int32_t* sel_heads,
                         int k_pages, int32_t* sel_union, hipStream_t stream) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
   union_kernel<<<kv.batch * kv.num_kv_heads, kUnionThreads, 0, stream>>>(
-      sel_heads, G, k_pages, kv.num_kv_heads, kv.max_pages_per_seq, sel_union);
+      sel_heads, G, k_pages, kv.max_pages_per_seq, sel_union);
   return hipGetLastError();
 }
 
