@@ -660,12 +660,10 @@ def bench_gqa_multistep(args, torch, qa, synth, full=True):
     def one_step(s):
         for layer, st in enumerate(layers):
             c, kv = st["c"], st["kv"]
-            if layer < wl.dense_layers:
-                qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], c["kmin"],
-                                          c["kmax"], c["page_table"], lens[s],
-                                          k_new=st["k_new"][s], v_new=st["v_new"][s])
-                st["dense"](st["q"][s], c["k_pool"], c["v_pool"],
-                            c["page_table"], lens[s])
+            if layer < wl.dense_layers:   # the append rides on the attention launch
+                st["dense"].append_step(st["q"][s], c["k_pool"], c["v_pool"],
+                                        c["kmin"], c["kmax"], c["page_table"],
+                                        lens[s], st["k_new"][s], st["v_new"][s])
             else:   # the append rides on the estimate launch
                 st["step"].append_step(st["q"][s], c["k_pool"], c["v_pool"],
                                        c["kmin"], c["kmax"], c["page_table"],
@@ -742,8 +740,10 @@ def bench_gqa_multistep(args, torch, qa, synth, full=True):
     def da(i):
         de = dense_l[i]
         c, d_ = de["c"], de["dense"]
-        qa.quest_decode_attn(de["kv"], de["q"][s_l], c["k_pool"], c["v_pool"],
-                             c["page_table"], lens[s_l], sm, d_.out, d_.workspace)
+        qa.quest_append_decode_attn(de["kv"], c["k_pool"], c["v_pool"], c["kmin"],
+                                    c["kmax"], c["page_table"], lens[s_l],
+                                    de["k_new"][s_l], de["v_new"][s_l], de["q"][s_l],
+                                    sm, d_.out, d_.workspace)
 
     ns = len(sparse_l)
     ku = {"estimate_kernel (append)": graph_batch(torch, ae, ns, 100, warm=1)["mean"],
@@ -756,7 +756,8 @@ def bench_gqa_multistep(args, torch, qa, synth, full=True):
     kb = kernel_bytes(sb, sparse_l[0]["kv"], k)
     kb["estimate_kernel (append)"] = (sb["meta"] + sb["q"] + sb["table"] + append_bytes(1, 8),
                                       {"scores_written": 8 * mp * 4})
-    kb["attn_split_kernel+attn_merge_kernel (dense)"] = (dense_bytes([Lf], 8, 32), {})
+    kb["attn_split_kernel+attn_merge_kernel (dense)"] = (dense_bytes([Lf], 8, 32)
+                                                         + append_bytes(1, 8), {})
     per_step = {"estimate_kernel (append)": wl.layers - wl.dense_layers,
                 "topk_attn_kernel": wl.layers - wl.dense_layers,
                 "attn_merge_kernel": wl.layers - wl.dense_layers,
@@ -770,7 +771,7 @@ def bench_gqa_multistep(args, torch, qa, synth, full=True):
          "effective_GBps": round(total / (us * 1e-6) / 1e9, 1),
          "hbm_frac": round(total / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
          "all_dense_bytes_per_step": int(all_dense),
-         "launches_per_step": wl.dense_layers * 3 + (wl.layers - wl.dense_layers) * 3,
+         "launches_per_step": wl.dense_layers * 2 + (wl.layers - wl.dense_layers) * 3,
          "layer_kernel_us": {c_: round(v, 3) for c_, v in ku.items()},
          "roofline": rl,
          "config": {"workload": "gqa_multistep_decode", "layers": wl.layers,

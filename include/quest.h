@@ -139,7 +139,9 @@ QUEST_API quest_status quest_estimate(
  * box in kmin / kmax -- [G] §1, the box forms as its page forms), and the
  * scores are those of the updated boxes.  Requests with L_b = 0 append
  * nothing.  The decode step of one layer becomes this call plus
- * quest_topk_sparse_decode_attn.
+ * quest_topk_sparse_decode_attn.  The page a request appends into must be
+ * its own: no other request's row may list it (its box and slot are
+ * written while the other rows are read).
  */
 QUEST_API quest_status quest_append_estimate(
     const quest_paged_kv* kv, void* k_pool, void* v_pool, void* kmin, void* kmax,
@@ -326,6 +328,25 @@ QUEST_API quest_status quest_decode_attn(
     const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
     float sm_scale, float* out, void* workspace, size_t workspace_bytes,
     void* stream);
+
+/*
+ * quest_update_page_meta in append mode followed by quest_decode_attn, in
+ * one launch (+ the split merge), with the same results bit for bit: each
+ * request appends token L_b - 1 (k_new / v_new [batch][Hkv][d], written
+ * into k_pool / v_pool at slot (L_b - 1) % S of logical page (L_b - 1) / S
+ * and folded into that page's box in kmin / kmax -- [G] §1, the box forms
+ * as its page forms), and the attention runs over all L_b tokens, the new
+ * one included ([G] attention equation).  Requests with L_b = 0 append
+ * nothing.  The decode step of a dense layer becomes this one call.  The
+ * workspace must hold quest_workspace_size(kv, max_pages_per_seq) bytes.
+ * As in quest_append_estimate, the page a request appends into must be its
+ * own: no other request's row may list it.
+ */
+QUEST_API quest_status quest_append_decode_attn(
+    const quest_paged_kv* kv, void* k_pool, void* v_pool, void* kmin, void* kmax,
+    const int32_t* page_table, const int32_t* seq_lens, const void* k_new,
+    const void* v_new, const void* q, float sm_scale, float* out, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 /*
  * One whole sparse decode step -- quest_estimate, quest_topk_pages and

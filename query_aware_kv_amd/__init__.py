@@ -20,7 +20,8 @@ from ._abi import (  # noqa: F401
     QUEST_ERR_WORKSPACE_TOO_SMALL, paged_kv, paged_kv_like,
     quest_decode_attn, quest_estimate, quest_sparse_decode_attn,
     quest_sparse_decode_step, quest_step_workspace_size,
-    quest_append_estimate, quest_estimate_heads, quest_union_pages,
+    quest_append_estimate, quest_append_decode_attn, quest_estimate_heads,
+    quest_union_pages,
     quest_stream_read_probe, quest_topk_pages, quest_topk_pages_ex,
     quest_topk_sparse_decode_attn, quest_topk_sparse_decode_attn_ex,
     quest_topk_sparse_decode_attn_splits, quest_merge_attn_splits,
@@ -221,4 +222,13 @@ class DenseDecode:
                  stream=None) -> torch.Tensor:
         quest_decode_attn(self.kv, q, k_pool, v_pool, page_table, seq_lens,
                           self.sm_scale, self.out, self.workspace, stream)
+        return self.out
+
+    def append_step(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_lens,
+                    k_new, v_new, stream=None) -> torch.Tensor:
+        """Append the step's token (seq_lens already count it) and attend
+        over every token, in one launch (quest_append_decode_attn)."""
+        quest_append_decode_attn(self.kv, k_pool, v_pool, kmin, kmax, page_table,
+                                 seq_lens, k_new, v_new, q, self.sm_scale, self.out,
+                                 self.workspace, stream)
         return self.out

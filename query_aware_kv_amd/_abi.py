@@ -88,6 +88,8 @@ def _load():
         "quest_topk_pages_ex": [KV, P, P, I, I, I, P, P],
         "quest_estimate_heads": [KV, P, P, P, P, P, P, P],
         "quest_append_estimate": [KV, P, P, P, P, P, P, P, P, P, P, P],
+        "quest_append_decode_attn": [KV, P, P, P, P, P, P, P, P, P, ctypes.c_float,
+                                     P, P, ctypes.c_size_t, P],
         "quest_union_pages": [KV, P, I, P, P],
         "quest_topk_sparse_decode_attn_ex": [KV, P, P, P, P, P, P, I, I, I,
                                              ctypes.c_float, P, P, P,
@@ -474,6 +476,29 @@ def quest_union_pages(kv: PagedKV, sel_heads, k_pages: int, sel_union,
         int(k_pages),
         _ptr(sel_union, "sel_union", torch.int32,
              (kv.batch, kv.num_kv_heads, G * k_pages)),
+        _stream(stream)))
+
+
+def quest_append_decode_attn(kv: PagedKV, k_pool, v_pool, kmin, kmax, page_table,
+                             seq_lens, k_new, v_new, q, sm_scale: float, out,
+                             workspace, stream=None) -> None:
+    dt = kv.torch_dtype
+    i32 = torch.int32
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.quest_append_decode_attn(
+        ctypes.byref(kv),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(kmin, "kmin", dt, _meta_shape(kv)),
+        _ptr(kmax, "kmax", dt, _meta_shape(kv)),
+        _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
+        _ptr(seq_lens, "seq_lens", i32, (kv.batch,)),
+        _ptr(k_new, "k_new", dt, (kv.batch, kv.num_kv_heads, kv.head_dim)),
+        _ptr(v_new, "v_new", dt, (kv.batch, kv.num_kv_heads, kv.head_dim)),
+        _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
+        float(sm_scale),
+        _ptr(out, "out", torch.float32, (kv.batch, kv.num_q_heads, kv.head_dim)),
+        _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes),
         _stream(stream)))
 
 

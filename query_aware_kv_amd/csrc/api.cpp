@@ -129,7 +129,8 @@ quest_status run_attention(const quest_paged_kv* kv, const void* q,
                            const int32_t* page_table, const int32_t* seq_lens,
                            const int32_t* sel, int list_len, float sm_scale,
                            float* out, void* workspace, size_t workspace_bytes,
-                           void* stream, const char* fn) {
+                           void* stream, const char* fn,
+                           const quest::AttnAppend* append = nullptr) {
   const size_t need = quest::attention_workspace_bytes(*kv, list_len);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
@@ -142,7 +143,7 @@ quest_status run_attention(const quest_paged_kv* kv, const void* q,
   return hip_status(
       quest::launch_attention(*kv, q, k_pool, v_pool, page_table, seq_lens, sel,
                               list_len, sm_scale, out, workspace,
-                              static_cast<hipStream_t>(stream)),
+                              static_cast<hipStream_t>(stream), append),
       fn);
 }
 
@@ -465,6 +466,28 @@ QUEST_API quest_status quest_decode_attn(const quest_paged_kv* kv,
   return run_attention(kv, q, k_pool, v_pool, page_table, seq_lens, nullptr,
                        kv->max_pages_per_seq, sm_scale, out, workspace,
                        workspace_bytes, stream, fn);
+}
+
+QUEST_API quest_status quest_append_decode_attn(
+    const quest_paged_kv* kv, void* k_pool, void* v_pool, void* kmin, void* kmax,
+    const int32_t* page_table, const int32_t* seq_lens, const void* k_new,
+    const void* v_new, const void* q, float sm_scale, float* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const char* fn = "quest_append_decode_attn";
+  quest_status s = check_attention_common(kv, q, k_pool, v_pool, page_table,
+                                          seq_lens, sm_scale, out, fn);
+  if (s != QUEST_OK) return s;
+  REQUIRE_PTR(kmin, aligned16(kmin));
+  REQUIRE_PTR(kmax, aligned16(kmax));
+  REQUIRE_PTR(k_new, aligned16(k_new));
+  REQUIRE_PTR(v_new, aligned16(v_new));
+  const quest::AttnAppend ap{static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
+                             static_cast<uint16_t*>(kmin), static_cast<uint16_t*>(kmax),
+                             static_cast<const uint16_t*>(k_new),
+                             static_cast<const uint16_t*>(v_new)};
+  return run_attention(kv, q, k_pool, v_pool, page_table, seq_lens, nullptr,
+                       kv->max_pages_per_seq, sm_scale, out, workspace,
+                       workspace_bytes, stream, fn, &ap);
 }
 
 QUEST_API quest_status quest_sparse_decode_step(

@@ -18,17 +18,46 @@
 namespace quest {
 namespace {
 
-template <DType T, int G, int PPW, int SUB>
+// One 32-bit word (two 16-bit values) of a box widened in place by the
+// token's word x: lo = min(x, lo, hi), hi = max(x, lo, hi) per value in the
+// ord16 order, as folding the three with fold8 gives, with a few registers
+// at a time.
+__device__ __forceinline__ void widen_word(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  uint32_t nlo = 0, nhi = 0;
+#pragma unroll
+  for (int sh = 0; sh < 32; sh += 16) {
+    const int32_t a = ord16(x >> sh), b = ord16(lo >> sh), c = ord16(hi >> sh);
+    nlo |= unord16(min(a, min(b, c))) << sh;
+    nhi |= unord16(max(a, max(b, c))) << sh;
+  }
+  lo = nlo;
+  hi = nhi;
+}
+
+// The pools' pointer type: restrict-qualified unless the append mode also
+// writes the pools through ap.
+template <bool APPEND>
+using PoolPtr = std::conditional_t<APPEND, const uint16_t*, const uint16_t* __restrict__>;
+
+// APPEND (dense only, quest_append_decode_attn): also append token L_b - 1
+// (ap.k_new / ap.v_new) to its page and widen that page's box, as
+// quest_update_page_meta's append mode does.  The wave that folds that page
+// loads the token with the page's tiles and puts it into the registers of
+// its slot before the fold (the slot's pool bytes are not used); after its
+// loop it writes the token into the pool and the widened box.  No other
+// workgroup reads that page, and nothing of the append is held in registers
+// across the loop, so the kernel keeps the plain instance's occupancy.
+template <DType T, int G, int PPW, int SUB, bool APPEND = false>
 __global__ void __launch_bounds__(256)
 attn_split_kernel(const uint16_t* __restrict__ q,
-                  const uint16_t* __restrict__ k_pool,
-                  const uint16_t* __restrict__ v_pool,
+                  PoolPtr<APPEND> k_pool,
+                  PoolPtr<APPEND> v_pool,
                   const int32_t* __restrict__ page_table,
                   const int32_t* __restrict__ seq_lens,
                   const int32_t* __restrict__ sel, int list_len, int Hkv,
                   int max_pages, int num_pool_pages, float qscale,
                   float* __restrict__ out, float* __restrict__ ws_o,
-                  float* __restrict__ ws_ml) {
+                  float* __restrict__ ws_ml, AttnAppend ap) {
   __shared__ AttnSmem<G> sm;
   const int unit = blockIdx.y;  // b * Hkv + g
   const int b = unit / Hkv, g = unit - (unit / Hkv) * Hkv;
@@ -45,6 +74,25 @@ attn_split_kernel(const uint16_t* __restrict__ q,
   const int64_t hi = (int64_t)(split + 1) * list_len / nsplit;
   const int L = seq_lens[b];
   constexpr int S = SUB * kTileRows;
+  // APPEND: jl = the appended token's logical page when this wave folds
+  // it (else -1), tl = its slot, pa = its pool page once a chunk has
+  // found it valid; k_tok / v_tok = the token's K and V rows
+  int jl = -1, tl = 0, pa = -1;
+  const uint16_t* k_tok = nullptr;
+  const uint16_t* v_tok = nullptr;
+  if constexpr (APPEND) {
+    const int pos = L - 1, j = pos >= 0 ? pos / S : -1;
+    if (j >= 0 && j < max_pages && j >= lo && j < hi &&
+        (int)((j - lo) % (kAttnWaves * PPW)) / PPW == wid) {
+      jl = j;
+      tl = pos - j * S;
+    }
+    // the same in every lane of the wave: scalar registers
+    jl = __builtin_amdgcn_readfirstlane(jl);
+    tl = __builtin_amdgcn_readfirstlane(tl);
+    k_tok = ap.k_new + ((int64_t)b * Hkv + g) * kHeadDim;
+    v_tok = ap.v_new + ((int64_t)b * Hkv + g) * kHeadDim;
+  }
   // q: packed words of one head (VALU path), the MFMA operand for a group
   AttnQ<G> qf;
   uint4 qb[4];
@@ -91,6 +139,54 @@ attn_split_kernel(const uint16_t* __restrict__ q,
     auto tile_valid = [&](int pi, int s) {
       return pj[pi] >= 0 ? min(kTileRows, L - pj[pi] * S - s * kTileRows) : 0;
     };
+    // APPEND: in the chunk that holds page jl, the token in the tiles'
+    // layout (channels 8c of lane c; a group's MFMA K tile: channels
+    // 32 s + 8 (lane / 16)), loaded with the tiles and put into the tile
+    // registers of its slot before the fold (the pool's slot is not used)
+    bool has = false;
+    uint4 tk[4], tv = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) tk[s2] = tv;
+    if constexpr (APPEND) {
+#pragma unroll
+      for (int pi = 0; pi < PPW; ++pi)
+        if (jl >= 0 && pj[pi] == jl) {
+          has = true;
+          pa = __builtin_amdgcn_readfirstlane((int)pp[pi]);  // a pool page: < num_pool_pages
+        }
+      if (has) {
+        tv = *reinterpret_cast<const uint4*>(v_tok + c * 8);
+        if constexpr (G >= 2) {
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            tk[s2] = *reinterpret_cast<const uint4*>(k_tok + 32 * s2 + 8 * (lane >> 4));
+        } else {
+          tk[0] = *reinterpret_cast<const uint4*>(k_tok + c * 8);
+        }
+      }
+    }
+    // the tile that holds slot tl gets the token (row t in the loaders'
+    // layouts: dev_attn.h, dev_attn_mfma.h)
+    auto put_token = [&](uint4 (&kt)[4], uint4 (&vt)[4]) {
+      const int t = tl % kTileRows;
+      if constexpr (G >= 2) {
+        const int jj = lane & 15;
+        if ((jj & 3) * 4 + (jj >> 2) == t) {
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) kt[s2] = tk[s2];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e == t / 4 && (lane >> 4) == t % 4) vt[e] = tv;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i == t / 4 && r == t % 4) {
+            kt[i] = tk[0];
+            vt[i] = tv;
+          }
+      }
+    };
     // The tile loads sit in one branch that depends on every page's table
     // entry, so all of them are in before the first tile load and no wait
     // separates the pages' loads.
@@ -109,6 +205,15 @@ attn_split_kernel(const uint16_t* __restrict__ q,
               mfma_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), lane,
                              kx[pi][s], vx[pi][s]);
       }
+      if constexpr (APPEND) {
+        if (has) {
+#pragma unroll
+          for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+            for (int s = 0; s < SUB; ++s)
+              if (pj[pi] == jl && s == tl / kTileRows) put_token(kx[pi][s], vx[pi][s]);
+        }
+      }
 #pragma unroll
       for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
@@ -126,6 +231,15 @@ attn_split_kernel(const uint16_t* __restrict__ q,
               attn_load_tile(k_pool, v_pool, attn_tile_offset<SUB>(pp[pi], Hkv, g, s), r, c,
                              kx[pi][s], vx[pi][s]);
       }
+      if constexpr (APPEND) {
+        if (has) {
+#pragma unroll
+          for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+            for (int s = 0; s < SUB; ++s)
+              if (pj[pi] == jl && s == tl / kTileRows) put_token(kx[pi][s], vx[pi][s]);
+        }
+      }
 #pragma unroll
       for (int pi = 0; pi < PPW; ++pi)
 #pragma unroll
@@ -133,6 +247,20 @@ attn_split_kernel(const uint16_t* __restrict__ q,
           const int v = tile_valid(pi, s);
           if (v > 0) attn_page<T, G>(vst, qf, kx[pi][s], vx[pi][s], v, r);
         }
+    }
+  }
+  // APPEND: the token and the page's old box, loaded here (no tile is live
+  // any more) and stored at the end
+  uint4 kn = make_uint4(0, 0, 0, 0), vn = kn, bmin = kn, bmax = kn;
+  if constexpr (APPEND) {
+    if (pa >= 0 && lane < 16) {
+      kn = *reinterpret_cast<const uint4*>(k_tok + lane * 8);
+      vn = *reinterpret_cast<const uint4*>(v_tok + lane * 8);
+      if (tl > 0) {
+        const int64_t m = ((int64_t)pa * Hkv + g) * kHeadDim + lane * 8;
+        bmin = *reinterpret_cast<const uint4*>(ap.kmin + m);
+        bmax = *reinterpret_cast<const uint4*>(ap.kmax + m);
+      }
     }
   }
   if constexpr (G >= 2) {
@@ -158,6 +286,25 @@ attn_split_kernel(const uint16_t* __restrict__ q,
         ws_ml[slot * 2] = M;
         ws_ml[slot * 2 + 1] = den;
       }
+    }
+  }
+  if constexpr (APPEND) {
+    if (pa >= 0 && lane < 16) {
+      const int64_t row = (((int64_t)pa * Hkv + g) * S + tl) * kHeadDim + lane * 8;
+      *reinterpret_cast<uint4*>(ap.k_pool + row) = kn;
+      *reinterpret_cast<uint4*>(ap.v_pool + row) = vn;
+      if (tl == 0) {  // slot 0 starts the box
+        bmin = kn;
+        bmax = kn;
+      } else {
+        widen_word(kn.x, bmin.x, bmax.x);
+        widen_word(kn.y, bmin.y, bmax.y);
+        widen_word(kn.z, bmin.z, bmax.z);
+        widen_word(kn.w, bmin.w, bmax.w);
+      }
+      const int64_t m = ((int64_t)pa * Hkv + g) * kHeadDim + lane * 8;
+      *reinterpret_cast<uint4*>(ap.kmin + m) = bmin;
+      *reinterpret_cast<uint4*>(ap.kmax + m) = bmax;
     }
   }
 }
@@ -225,9 +372,9 @@ using Plan = AttnPlan;
 }  // namespace
 
 namespace {
-// workgroups of the attention instance with `ppw` pages per wave that the
-// current GPU holds at once (defined below)
-int64_t dense_resident(const quest_paged_kv& kv, int ppw);
+// workgroups of the attention instance with `ppw` pages per wave (append
+// mode or not) that the current GPU holds at once (defined below)
+int64_t dense_resident(const quest_paged_kv& kv, int ppw, bool append = false);
 }  // namespace
 
 // Pages per wave: as many as the registers allow while the grid keeps at
@@ -271,7 +418,7 @@ namespace {
 // at once: the runtime's occupancy figure (from the kernel's registers and
 // LDS) per CU times the CUs, looked up once per instance and GPU.  Without
 // a GPU it falls back to one per CU of 256 CUs.
-template <DType T, int G, int PPW, int SUB>
+template <DType T, int G, int PPW, int SUB, bool APPEND = false>
 int64_t resident_wgs() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cached[kMaxDevices];
@@ -282,7 +429,8 @@ int64_t resident_wgs() {
   int per_cu = 0, cus = 0;
   if (dev < 0 ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(attn_split_kernel<T, G, PPW, SUB>), 256, 0) !=
+          &per_cu, reinterpret_cast<const void*>(attn_split_kernel<T, G, PPW, SUB, APPEND>), 256,
+          0) !=
           hipSuccess ||
       per_cu < 1)
     per_cu = 1;
@@ -296,13 +444,15 @@ int64_t resident_wgs() {
 
 // The same for the instance a plan of `ppw` pages per wave launches (4 only
 // for 16-token pages: max_ppw).
-int64_t dense_resident(const quest_paged_kv& kv, int ppw) {
+int64_t dense_resident(const quest_paged_kv& kv, int ppw, bool append) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
   auto by_g = [&](auto tt, auto ss) -> int64_t {
     constexpr DType TT = decltype(tt)::value;
     constexpr int SS = decltype(ss)::value;
     auto pick = [&](auto gg) -> int64_t {
       constexpr int GG = decltype(gg)::value;
+      if (append)  // the dense plan's shapes only (1 or 2 pages per wave)
+        return ppw >= 2 ? resident_wgs<TT, GG, 2, SS, true>() : resident_wgs<TT, GG, 1, SS, true>();
       if constexpr (SS == 1) {
         if (ppw >= 4) return resident_wgs<TT, GG, 4, SS>();
       }
@@ -334,13 +484,13 @@ int64_t dense_resident(const quest_paged_kv& kv, int ppw) {
 // Measured on a 32/8-head GQA layer at 32K: 34.1 us against 39.2 us for
 // 1024 workgroups of 2 pages per wave (two rounds), and 36.4 us when the
 // group kernel is held to 128 VGPRs to fit 4 per CU.
-AttnPlan dense_plan(const quest_paged_kv& kv) {
+AttnPlan dense_plan(const quest_paged_kv& kv, bool append = false) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
   const int ppw = (G == 1 && kv.page_size == kTileRows) ? 2 : 1;
   const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
   const int64_t chunks = (kv.max_pages_per_seq + kAttnWaves * ppw - 1) /
                          (kAttnWaves * ppw);
-  int64_t ns = dense_resident(kv, ppw) / units;
+  int64_t ns = dense_resident(kv, ppw, append) / units;
   if (ns > chunks) ns = chunks;
   if (ns > 65535) ns = 65535;
   return {ppw, (int)(ns < 1 ? 1 : ns)};
@@ -365,33 +515,36 @@ void launch_merge(const quest_paged_kv& kv, const float* ws_o,
 
 namespace {
 
-template <DType T, int G, int PPW, int SUB>
+template <DType T, int G, int PPW, int SUB, bool APPEND>
 void launch_split(const quest_paged_kv& kv, const void* q, const void* k_pool,
                   const void* v_pool, const int32_t* page_table,
                   const int32_t* seq_lens, const int32_t* sel, int list_len,
                   float qscale, float* out, float* ws_o, float* ws_ml,
-                  int nsplit, hipStream_t stream) {
+                  int nsplit, const AttnAppend& ap, hipStream_t stream) {
   dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
-  attn_split_kernel<T, G, PPW, SUB><<<grid, 256, 0, stream>>>(
+  attn_split_kernel<T, G, PPW, SUB, APPEND><<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), page_table, seq_lens, sel,
       list_len, kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages,
-      qscale, out, ws_o, ws_ml);
+      qscale, out, ws_o, ws_ml, ap);
 }
 
-template <DType T, int SUB>
+template <DType T, int SUB, bool APPEND>
 void dispatch(int G, int ppw, const quest_paged_kv& kv, const void* q,
               const void* k_pool, const void* v_pool,
               const int32_t* page_table, const int32_t* seq_lens,
               const int32_t* sel, int list_len, float qscale, float* out,
-              float* ws_o, float* ws_ml, int nsplit, hipStream_t stream) {
-#define QUEST_SPLIT(GG, PP)                                                        \
-  launch_split<T, GG, PP, SUB>(kv, q, k_pool, v_pool, page_table, seq_lens, sel,  \
-                               list_len, qscale, out, ws_o, ws_ml, nsplit, stream)
-  // ppw never exceeds max_ppw(SUB): only those variants are built
+              float* ws_o, float* ws_ml, int nsplit, const AttnAppend& ap,
+              hipStream_t stream) {
+#define QUEST_SPLIT(GG, PP)                                                              \
+  launch_split<T, GG, PP, SUB, APPEND>(kv, q, k_pool, v_pool, page_table, seq_lens, sel, \
+                                       list_len, qscale, out, ws_o, ws_ml, nsplit, ap,   \
+                                       stream)
+  // ppw never exceeds max_ppw(SUB) (the append mode: the dense plan's 1 or
+  // 2): only those variants are built
   auto by_ppw = [&](auto gg) {
     constexpr int GG = decltype(gg)::value;
-    if constexpr (SUB == 1) {
+    if constexpr (SUB == 1 && !APPEND) {
       if (ppw == 4) { QUEST_SPLIT(GG, 4); return; }
     }
     if (ppw == 2) QUEST_SPLIT(GG, 2);
@@ -420,7 +573,8 @@ static size_t partial_bytes(const quest_paged_kv& kv, int nsplit) {
 
 // The sparse plans (4-wave attention, 8-wave Top-K + attention) for
 // list_len entries; a list as long as the row (list_len >= max_pages_per_seq,
-// the size quest_decode_attn is asked with) also covers the dense plan.
+// the size quest_decode_attn and quest_append_decode_attn are asked with)
+// also covers the dense plans.
 size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len) {
   size_t need = partial_bytes(kv, attention_plan(kv, list_len).nsplit);
   const size_t t = partial_bytes(kv, attention_plan(kv, list_len, 8).nsplit);
@@ -428,6 +582,8 @@ size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len) {
   if (list_len >= kv.max_pages_per_seq) {
     const size_t d = partial_bytes(kv, dense_plan(kv).nsplit);
     if (d > need) need = d;
+    const size_t a = partial_bytes(kv, dense_plan(kv, true).nsplit);  // append mode
+    if (a > need) need = a;
   }
   return need;
 }
@@ -436,16 +592,29 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
                             const void* k_pool, const void* v_pool,
                             const int32_t* page_table, const int32_t* seq_lens,
                             const int32_t* sel, int list_len, float sm_scale,
-                            float* out, void* workspace, hipStream_t stream) {
+                            float* out, void* workspace, hipStream_t stream,
+                            const AttnAppend* append) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
-  const Plan pl = sel ? attention_plan(kv, list_len) : dense_plan(kv);
+  // the append mode is dense only
+  const bool app = append != nullptr && sel == nullptr;
+  const Plan pl = sel ? attention_plan(kv, list_len) : dense_plan(kv, app);
   const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = ws_o ? ws_o + attention_ml_offset(slots) : nullptr;
   const float qscale = sm_scale * kLog2e;
-#define QUEST_DISPATCH(TT, SS)                                                    \
-  dispatch<TT, SS>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens, sel,   \
-                   list_len, qscale, out, ws_o, ws_ml, pl.nsplit, stream)
+  const AttnAppend ap = app ? *append : AttnAppend{nullptr, nullptr, nullptr, nullptr,
+                                                   nullptr, nullptr};
+#define QUEST_DISPATCH(TT, SS)                                                          \
+  do {                                                                                  \
+    if (app)                                                                            \
+      dispatch<TT, SS, true>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,    \
+                             sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit, ap,    \
+                             stream);                                                   \
+    else                                                                                \
+      dispatch<TT, SS, false>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,   \
+                              sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit, ap,   \
+                              stream);                                                  \
+  } while (0)
   const bool s32 = kv.page_size == 32;
   if (kv.dtype == QUEST_F16) {
     if (s32) QUEST_DISPATCH(DType::F16, 2);

@@ -61,11 +61,22 @@ void launch_merge(const quest_paged_kv& kv, const float* ws_o,
                   hipStream_t stream);
 bool attention_supported(int group);
 size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len);
+// Append mode of the dense attention (quest_append_decode_attn): where the
+// step's token goes and the boxes it widens (null pointers otherwise).
+struct AttnAppend {
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  uint16_t* kmin;
+  uint16_t* kmax;
+  const uint16_t* k_new;  // [B][Hkv][128]
+  const uint16_t* v_new;
+};
 hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
                             const void* k_pool, const void* v_pool,
                             const int32_t* page_table, const int32_t* seq_lens,
                             const int32_t* sel, int list_len, float sm_scale,
-                            float* out, void* workspace, hipStream_t stream);
+                            float* out, void* workspace, hipStream_t stream,
+                            const AttnAppend* append = nullptr);
 
 // Top-K + sparse attention in one launch (each workgroup selects its row).
 constexpr int kTopkAttnMaxPages = 8192;

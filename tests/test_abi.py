@@ -258,6 +258,30 @@ def test_append_estimate_validation():
         assert name in qa.LIB.quest_last_error().decode()
 
 
+def test_append_decode_attn_validation():
+    k = kv()
+    P = ctypes.c_void_p
+    st, need = ws_size(k, k.max_pages_per_seq)
+    names = ["k_pool", "v_pool", "kmin", "kmax", "page_table", "seq_lens", "k_new",
+             "v_new", "q"]
+    args = [P(FAKE)] * len(names)
+    for i, name in enumerate(names):
+        bad = list(args)
+        bad[i] = None
+        assert qa.LIB.quest_append_decode_attn(ctypes.byref(k), *bad, 0.088, P(FAKE),
+                                               P(FAKE), need, None) == \
+            _abi.QUEST_ERR_INVALID_ARGUMENT
+        assert name in qa.LIB.quest_last_error().decode()
+    assert qa.LIB.quest_append_decode_attn(ctypes.byref(k), *args, 0.088, None, P(FAKE),
+                                           need, None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert qa.LIB.quest_append_decode_attn(ctypes.byref(k), *args, float("nan"), P(FAKE),
+                                           P(FAKE), need, None) == \
+        _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert qa.LIB.quest_append_decode_attn(ctypes.byref(k), *args, 0.088, P(FAKE),
+                                           P(FAKE), need - 16, None) == \
+        _abi.QUEST_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_last_error_is_per_thread():
     """Each host thread reads the message of its own last failed call."""
     import threading

@@ -247,7 +247,8 @@ def test_gqa_multistep_three_layers(path):
     sampled kv-heads.  "calls": the append by quest_update_page_meta, then
     the step; "append_step": the benchmark's own path -- the append folded
     into the bounds launch (quest_append_estimate), then the Top-K +
-    attention call."""
+    attention call, and on the dense layers into the attention launch
+    (quest_append_decode_attn)."""
     wl = synth.gqa_multistep_workload(layers=3, steps=3)
     G = wl.group
     heads = [1, 6]
@@ -276,12 +277,16 @@ def test_gqa_multistep_three_layers(path):
             c, kv = st["c"], st["kv"]
             q = synth.draw_query(wl, layer, "cuda", step=step)
             k_new, v_new = synth.draw_append_token(wl, layer, step, "cuda")
-            if layer < wl.dense_layers or path == "calls":
+            if path == "calls":
                 qa.quest_update_page_meta(kv, c["k_pool"], c["v_pool"], st["kmin"],
                                           st["kmax"], c["page_table"], lens,
                                           k_new=k_new, v_new=v_new)
-            if layer < wl.dense_layers:
+            if layer < wl.dense_layers and path == "calls":
                 out = st["dense"](q, c["k_pool"], c["v_pool"], c["page_table"], lens)
+            elif layer < wl.dense_layers:
+                out = st["dense"].append_step(q, c["k_pool"], c["v_pool"], st["kmin"],
+                                              st["kmax"], c["page_table"], lens,
+                                              k_new, v_new)
             elif path == "calls":
                 out = st["step"](q, c["k_pool"], c["v_pool"], st["kmin"],
                                   st["kmax"], c["page_table"], lens)
