@@ -390,7 +390,7 @@ int64_t dense_resident(const quest_paged_kv& kv, int ppw, bool append = false);
 // through its registers).  Measured on the 32-head layers: 8 splits of 2
 // pages per wave beat 16 of one at budgets up to 2048 tokens.
 // quest_workspace_size covers the 4-wave and the 8-wave plan of a list (and,
-// for whole rows, the dense plan).
+// for whole rows, the dense plans, plain and append).
 AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves) {
   const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
   const bool topk_wg = waves == 8;
@@ -414,7 +414,7 @@ AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves) {
 
 namespace {
 
-// Workgroups of attn_split_kernel<T, G, PPW, SUB> that the current GPU holds
+// Workgroups of attn_split_kernel<T, G, PPW, SUB, APPEND> that the current GPU holds
 // at once: the runtime's occupancy figure (from the kernel's registers and
 // LDS) per CU times the CUs, looked up once per instance and GPU.  Without
 // a GPU it falls back to one per CU of 256 CUs.

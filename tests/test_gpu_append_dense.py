@@ -2,10 +2,11 @@
 attention launch) against quest_update_page_meta (append mode) followed by
 quest_decode_attn, over 20 appended tokens that cross page and tile
 boundaries: K and V pools and boxes bit for bit, the attention up to the
-order of its split sums (the append kernel holds more registers, so its plan
-may split the rows differently), and the last step's attention against the
+order of its split sums (the two attention instances' plans need not split
+the rows alike: each takes its own occupancy), and the last step's attention against the
 oracle's dense attention ("Guide to Quest": §1 boxes, the attention
-equation)."""
+equation).  Also: appends whose page-table entry names no pool page are
+skipped by both."""
 import dataclasses
 import math
 
@@ -44,9 +45,11 @@ def make(name):
     return wl, C.draw(wl)
 
 
-@pytest.mark.parametrize("name", sorted(CASES))
-def test_append_decode_attn_equals_two_calls(name):
-    wl, c = make(name)
+def two_ways(wl, c):
+    """Every step by update_page_meta (append) + decode_attn on the draw's
+    buffers and by append_decode_attn on copies; the pools and boxes must
+    agree bit for bit, the outputs up to the order of their split sums.
+    Returns the last step's inputs and fused output."""
     kv = c["kv"]
     kmin_a, kmax_a = C.gpu_meta(c)
     kmin_b, kmax_b = kmin_a.clone(), kmax_a.clone()
@@ -67,9 +70,37 @@ def test_append_decode_attn_equals_two_calls(name):
         assert torch.equal(i16(kmin_a), i16(kmin_b)) and \
             torch.equal(i16(kmax_a), i16(kmax_b)), step
     assert torch.equal(i16(kp_a), i16(kp_b)) and torch.equal(i16(vp_a), i16(vp_b))
+    return q, kp_b, vp_b, lens, out_b
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_append_decode_attn_equals_two_calls(name):
+    wl, c = make(name)
+    q, kp, vp, lens, out = two_ways(wl, c)
     # the last step's attention against the oracle
     lens_h = lens.cpu().numpy().astype(np.int64)
-    ref = O.dense_attention(C.to64(q), C.to64(kp_b), C.to64(vp_b),
+    ref = O.dense_attention(C.to64(q), C.to64(kp), C.to64(vp),
                             c["page_table"].cpu().numpy().astype(np.int64), lens_h, SM,
                             wl.page_size)
-    C.assert_attention_close(out_b.cpu().numpy().astype(np.float64), ref)
+    C.assert_attention_close(out.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("entry", ["negative", "past_pool"])
+def test_append_into_an_absent_page(entry):
+    """A request whose appended tokens land in pages whose table entries
+    name no pool page appends nothing and attends over its other pages, in
+    both compositions; the other requests append as usual."""
+    wl, c = make("mha_f16")
+    kv = c["kv"]
+    r, S = 2, wl.page_size
+    v = -1 if entry == "negative" else kv.num_pool_pages
+    c["page_table"][r, wl.seq_lens[r] // S:] = v
+    kp0 = c["k_pool"].clone()
+    two_ways(wl, c)
+    # request r wrote nowhere: the pools changed only in the slots the other
+    # requests appended to
+    changed = (c["k_pool"].view(torch.int16) != kp0.view(torch.int16)).any(dim=-1)
+    pt = c["page_table"].cpu().numpy()
+    others = {int(pt[b, (L + t) // S]) for b, L in enumerate(wl.seq_lens)
+              if b != r and L > 0 for t in range(STEPS)}
+    assert set(torch.nonzero(changed.flatten(1).any(dim=1)).flatten().tolist()) <= others

@@ -1,7 +1,8 @@
 """quest_append_estimate == quest_update_page_meta (append) + quest_estimate,
 bit for bit (scores, boxes, K and V pools), over 20 appended tokens that
-cross page boundaries; and SparseDecodeStep.append_step equals the two-call
-composition."""
+cross page boundaries, also when the appended tokens' page-table entries
+name no pool page (both skip those appends); and
+SparseDecodeStep.append_step equals the two-call composition."""
 import dataclasses
 import math
 
@@ -43,9 +44,10 @@ def appended(wl, c, step):
     return lens, k_new, v_new
 
 
-@pytest.mark.parametrize("name", sorted(CASES))
-def test_append_estimate_equals_two_calls(name):
-    wl, c = make(name)
+def two_ways(wl, c):
+    """Every step by update_page_meta (append) + estimate on the draw's
+    buffers and by append_estimate on copies: scores, boxes and pools must
+    agree bit for bit."""
     kv = c["kv"]
     kmin_a, kmax_a = C.gpu_meta(c)
     kmin_b, kmax_b = kmin_a.clone(), kmax_a.clone()
@@ -68,6 +70,34 @@ def test_append_estimate_equals_two_calls(name):
         assert torch.equal(i16(kmin_a), i16(kmin_b)) and \
             torch.equal(i16(kmax_a), i16(kmax_b)), step
     assert torch.equal(i16(kp_a), i16(kp_b)) and torch.equal(i16(vp_a), i16(vp_b))
+    return s_b
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_append_estimate_equals_two_calls(name):
+    wl, c = make(name)
+    two_ways(wl, c)
+
+
+@pytest.mark.parametrize("entry", ["negative", "past_pool"])
+def test_append_into_an_absent_page(entry):
+    """A request whose appended tokens land in pages whose table entries
+    name no pool page appends nothing and scores those pages -inf, in both
+    compositions; the other requests append as usual."""
+    wl, c = make("mha_f16")
+    kv = c["kv"]
+    r, S = 2, wl.page_size
+    v = -1 if entry == "negative" else kv.num_pool_pages
+    first = wl.seq_lens[r] // S
+    c["page_table"][r, first:] = v
+    kp0 = c["k_pool"].clone()
+    scores = two_ways(wl, c)
+    assert torch.isneginf(scores[r, :, first:]).all()
+    changed = (c["k_pool"].view(torch.int16) != kp0.view(torch.int16)).flatten(1).any(dim=1)
+    pt = c["page_table"].cpu().numpy()
+    others = {int(pt[b, (L + t) // S]) for b, L in enumerate(wl.seq_lens)
+              if b != r and L > 0 for t in range(STEPS)}
+    assert set(torch.nonzero(changed).flatten().tolist()) <= others
 
 
 @pytest.mark.parametrize("select", ["attention", "separate"])

@@ -5,8 +5,9 @@ into the graph's input buffers, and eager work and synchronisations run
 between replays.  Every replay's output, kept lists and bounds, and the
 pools and boxes at the end, must equal eager steps on twin buffers bit for
 bit.  Covers the sparse append step (quest_append_estimate, then the Top-K
-and attention) and a dense layer of the multi-layer step (the append in
-quest_update_page_meta, then quest_decode_attn).  The graph is warmed up
+and attention) and a dense layer of the multi-layer step, both as two calls
+(the append in quest_update_page_meta, then quest_decode_attn) and as one
+(quest_append_decode_attn).  The graph is warmed up
 with the first step's inputs, which its first replay appends again:
 appending the same token twice leaves the same pools and boxes."""
 import dataclasses
@@ -89,10 +90,12 @@ def test_sparse_append_steps_from_a_graph(S, select):
     assert torch.equal(_i16(kmin_a), _i16(kmin_b)) and torch.equal(_i16(kmax_a), _i16(kmax_b))
 
 
-def test_dense_append_steps_from_a_graph():
-    wl, c = _setup(16)
+@pytest.mark.parametrize("path", ["calls", "fused"])
+@pytest.mark.parametrize("S", [16, 32])
+def test_dense_append_steps_from_a_graph(S, path):
+    wl, c = _setup(S)
     kv = c["kv"]
-    C.say(f"[case] graph append dense lens={wl.seq_lens} steps={STEPS}")
+    C.say(f"[case] graph append dense S={S} {path} lens={wl.seq_lens} steps={STEPS}")
     kmin_a, kmax_a = C.gpu_meta(c)
     kmin_b, kmax_b = kmin_a.clone(), kmax_a.clone()
     kp_a, vp_a = c["k_pool"], c["v_pool"]
@@ -102,6 +105,8 @@ def test_dense_append_steps_from_a_graph():
     b = qa.DenseDecode(kv, SM)
 
     def layer(d, q, kp, vp, kmin, kmax, lens, k_new, v_new):
+        if path == "fused":
+            return d.append_step(q, kp, vp, kmin, kmax, pt, lens, k_new, v_new)
         qa.quest_update_page_meta(kv, kp, vp, kmin, kmax, pt, lens,
                                   k_new=k_new, v_new=v_new)
         return d(q, kp, vp, pt, lens)
