@@ -55,9 +55,15 @@ def test_host_pools_match_device_pools(maker, name):
     assert torch.equal(d1.view(torch.int32), d2.view(torch.int32))
 
 
-def test_append_into_host_pool():
+@pytest.mark.parametrize("how", ["update_page_meta", "append_estimate",
+                                 "append_decode_attn"])
+def test_append_into_host_pool(how):
+    """Each append (the append kernel, and the appends inside the bounds and
+    the dense attention launches) writes host pools as it writes device
+    pools: the same boxes, slots and outputs, bit for bit."""
     wl, c = make16("gqa4_f16")
     kv = c["kv"]
+    C.say(f"[case] append into host pools via {how}")
     hk, hv = host_pools(c)
     kmin, kmax = C.gpu_meta(c)
     # one more token for requests whose last page has room (others pass
@@ -70,24 +76,42 @@ def test_append_into_host_pool():
                         device="cuda").to(c["k_pool"].dtype)
     v_new = torch.randn(kv.batch, kv.num_kv_heads, 128, generator=g,
                         device="cuda").to(c["k_pool"].dtype)
+    pt = c["page_table"]
     dk, dv = c["k_pool"].clone(), c["v_pool"].clone()
     dmin, dmax = kmin.clone(), kmax.clone()
-    qa.quest_update_page_meta(kv, dk, dv, dmin, dmax, c["page_table"], lens,
-                              k_new=k_new, v_new=v_new)
-    qa.quest_update_page_meta(kv, hk, hv, kmin, kmax, c["page_table"], lens,
-                              k_new=k_new, v_new=v_new)
+
+    def call(kp, vp, bmin, bmax):
+        if how == "update_page_meta":
+            qa.quest_update_page_meta(kv, kp, vp, bmin, bmax, pt, lens,
+                                      k_new=k_new, v_new=v_new)
+            return None
+        if how == "append_estimate":
+            scores = torch.empty(kv.batch, kv.num_kv_heads, kv.max_pages_per_seq,
+                                 device="cuda")
+            qa.quest_append_estimate(kv, kp, vp, bmin, bmax, pt, lens, k_new, v_new,
+                                     c["q"], scores)
+            return scores
+        return qa.DenseDecode(kv, SM).append_step(c["q"], kp, vp, bmin, bmax, pt, lens,
+                                                  k_new, v_new)
+
+    r_dev = call(dk, dv, dmin, dmax)
+    r_host = call(hk, hv, kmin, kmax)
     torch.cuda.synchronize()
+    if r_dev is not None:
+        assert torch.equal(r_dev.view(torch.int32), r_host.view(torch.int32))
     assert torch.equal(kmin.view(torch.int16), dmin.view(torch.int16))
     assert torch.equal(kmax.view(torch.int16), dmax.view(torch.int16))
-    pt = c["page_table"].cpu().long()
+    pt_h = pt.cpu().long()
     for b, L in enumerate(lens.cpu().tolist()):
         if L == 0:
             continue
-        p, slot = pt[b, (L - 1) // 16], (L - 1) % 16
+        p, slot = pt_h[b, (L - 1) // 16], (L - 1) % 16
         assert torch.equal(hk.tensor[p, :, slot].view(torch.int16),
                            dk[p, :, slot].cpu().view(torch.int16))
         assert torch.equal(hv.tensor[p, :, slot].view(torch.int16),
                            dv[p, :, slot].cpu().view(torch.int16))
+        assert torch.equal(hk.tensor[p, :, slot].view(torch.int16),
+                           k_new[b].cpu().view(torch.int16))
 
 
 @pytest.mark.parametrize("maker,name", [(make16, "gqa4_f16"), (make16, "mha_ragged_f16"),
