@@ -141,6 +141,46 @@ def append_bytes(batch, n_kv_heads, d=128, s=2):
     return batch * n_kv_heads * d * s * (2 + 4)
 
 
+def attention_recall(torch, q, k_pool, page_table, seq_lens, sel, page_size, sm_scale,
+                     top_m=16):
+    """How much of full attention a page selection keeps, per (request,
+    query head h) of a group of G = Hq / Hkv heads: w = softmax over the
+    request's valid tokens t of (q_h . k_t) * sm_scale (float32, outside any
+    timed region); `mass` = the sum of w over the tokens of the pages that
+    h attends (sel[b][h // G], -1 entries ignored), `top` = the share of the
+    top_m highest-weight tokens that lie in those pages.  Returns the mean
+    and the minimum of each over every (request, head) with tokens."""
+    B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    S = page_size
+    mass, top = [], []
+    lens = [int(x) for x in seq_lens.cpu()]
+    for b, L in enumerate(lens):
+        if L <= 0:
+            continue
+        n = -(-L // S)
+        pages = page_table[b, :n].long()
+        keys = k_pool[pages].float()                   # [n, Hkv, S, d]
+        keys = keys.permute(1, 0, 2, 3).reshape(Hkv, n * S, d)[:, :L]
+        tok_page = torch.arange(L, device=q.device) // S
+        m = min(top_m, L)
+        for g in range(Hkv):
+            kept = torch.zeros(n, dtype=torch.bool, device=q.device)
+            js = sel[b, g].long()
+            js = js[(js >= 0) & (js < n)]
+            kept[js] = True
+            kept_tok = kept[tok_page]
+            kt = keys[g].t().contiguous()              # [d, L]
+            z = torch.matmul(q[b, g * G:(g + 1) * G].float(), kt) * sm_scale
+            w = torch.softmax(z, dim=-1)               # [G, L]
+            mass += (w * kept_tok).sum(dim=-1).tolist()
+            idx = torch.topk(w, m, dim=-1).indices
+            top += (kept_tok[idx].float().mean(dim=-1)).tolist()
+    return {"mass_mean": sum(mass) / len(mass), "mass_min": min(mass),
+            "top%d_mean" % top_m: sum(top) / len(top), "top%d_min" % top_m: min(top)}
+
+
 def kv_cache_bytes(layers, heads, d, ctx, s=2):
     """K and V of every layer and head for ctx tokens."""
     return layers * 2 * heads * d * ctx * s
@@ -804,7 +844,9 @@ def bench_gqa_multistep(args, torch, qa, synth, full=True):
 
 def bench_gqa_union(args, torch, qa, synth):
     """One GQA layer (32 q-heads / 8 kv-heads, 32K, 2048-token budget): the
-    group-sum rule against the per-head + union rule, same caches."""
+    group-sum rule against the per-head + union rule, same caches: time,
+    bytes, and how much of full attention each rule's pages hold
+    (attention_recall)."""
     rot = args.rotate
     wls = [synth.gqa_multistep_workload(seed=4 + 1000 * i, layers=1, steps=0)
            for i in range(rot)]
@@ -879,6 +921,17 @@ def bench_gqa_union(args, torch, qa, synth):
                                      {"sel_read": Hkv * G * k * 4})}
     ku = {names[c_]: t_calls[c_] for c_ in t_calls}
     kb = {names[c_]: b_calls[c_] for c_ in b_calls}
+    # what each rule keeps of full attention, on every rotating cache
+    rec = {}
+    for name, steps in (("group_sum", sums), ("union", unions)):
+        per = [attention_recall(torch, insts[i]["q"], insts[i]["k_pool"],
+                                insts[i]["page_table"], insts[i]["seq_lens"],
+                                steps[i].sel, kv.page_size, sm) for i in range(rot)]
+        rec[name] = {}
+        for m_ in per[0]:
+            vals = [r[m_] for r in per]
+            rec[name][m_] = round(sum(vals) / len(vals) if m_.endswith("mean")
+                                  else min(vals), 4)
     return {
         "metric": "µs/decode step, GQA 32/8 layer, per-head Top-K + union vs "
                   "group-sum Top-K",
@@ -898,6 +951,11 @@ def bench_gqa_union(args, torch, qa, synth):
                       "effective_GBps": round(sm_["bytes"] / (sm_["us"] * 1e-6) / 1e9, 1),
                       "pages_per_kv_head": round(sm_["pages"], 1)},
         "union_pages_over_k": round(u["pages"] / k, 3),
+        "attention_recall": dict(rec, note="per (request, query head): the full-attention "
+                                 "weight (float32 softmax over every valid token) on the "
+                                 "pages the head attends, and the share of its 16 "
+                                 "highest-weight tokens in them; mean and min over heads "
+                                 "and rotating caches; synthetic data"),
         "union_call_us": {c_: round(v, 3) for c_, v in t_calls.items()},
         "roofline": roofline(ku, kb),
         "group": G, "gpu": torch.cuda.get_device_name(0)}
