@@ -5,8 +5,10 @@ boundaries: K and V pools and boxes bit for bit, the attention up to the
 order of its split sums (the two attention instances' plans need not split
 the rows alike: each takes its own occupancy), and the last step's attention against the
 oracle's dense attention ("Guide to Quest": §1 boxes, the attention
-equation).  Also: appends whose page-table entry names no pool page are
-skipped by both."""
+equation).  Every attention instance the append mode launches (both
+dtypes, groups of 1, 2, 4 and 8, 16- and 32-token pages) is covered.
+Also: appends whose page-table entry names no pool page are skipped by
+both."""
 import dataclasses
 import math
 
@@ -82,6 +84,27 @@ def test_append_decode_attn_equals_two_calls(name):
     ref = O.dense_attention(C.to64(q), C.to64(kp), C.to64(vp),
                             c["page_table"].cpu().numpy().astype(np.int64), lens_h, SM,
                             wl.page_size)
+    C.assert_attention_close(out.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("S", [16, 32])
+def test_every_append_instance(S, G, dt):
+    """Each attention instance the append mode launches (dtype x group size
+    x page size), over appends that cross a page boundary, equals the two
+    calls."""
+    Hkv = 2
+    lens = (S * 3 - 2, 5 * S + 7)                 # the first fills its page at step 1
+    wl = C.workload(2, G * Hkv, Hkv, lens, 128, dt, 5 + G, True, 4, 0,
+                    f"inst_{dt}_g{G}_p{S}", page_size=S)
+    wl = dataclasses.replace(wl, steps=STEPS)
+    C.say(f"[case] append_decode_attn instance S={S} G={G} {dt} lens={lens}")
+    c = C.draw(wl)
+    q, kp, vp, lens_t, out = two_ways(wl, c)
+    ref = O.dense_attention(C.to64(q), C.to64(kp), C.to64(vp),
+                            c["page_table"].cpu().numpy().astype(np.int64),
+                            lens_t.cpu().numpy().astype(np.int64), SM, S)
     C.assert_attention_close(out.cpu().numpy().astype(np.float64), ref)
 
 
