@@ -1,8 +1,9 @@
 """quest_append_estimate == quest_update_page_meta (append) + quest_estimate,
 bit for bit (scores, boxes, K and V pools), over 20 appended tokens that
 cross page boundaries, also when the appended tokens' page-table entries
-name no pool page (both skip those appends); and
-SparseDecodeStep.append_step equals the two-call composition."""
+name no pool page (both skip those appends), in every bounds instance the
+append mode launches; and SparseDecodeStep.append_step equals the two-call
+composition."""
 import dataclasses
 import math
 
@@ -77,6 +78,22 @@ def two_ways(wl, c):
 def test_append_estimate_equals_two_calls(name):
     wl, c = make(name)
     two_ways(wl, c)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("Hkv", [2, 4])          # 16-row and four-head mappings
+@pytest.mark.parametrize("S", [16, 32])
+def test_every_append_instance(S, Hkv, G, dt):
+    """Each bounds instance the append mode launches (dtype x group size x
+    work mapping, both page sizes), over appends that cross a page
+    boundary, equals the two calls bit for bit."""
+    lens = (S * 3 - 2, 5 * S + 7)                 # the first fills its page at step 1
+    wl = C.workload(2, G * Hkv, Hkv, lens, 128, dt, 5 + G, True, 4, 0,
+                    f"est_inst_{dt}_g{G}_h{Hkv}_p{S}", page_size=S)
+    wl = dataclasses.replace(wl, steps=STEPS)
+    C.say(f"[case] append_estimate instance S={S} Hkv={Hkv} G={G} {dt} lens={lens}")
+    two_ways(wl, C.draw(wl))
 
 
 @pytest.mark.parametrize("entry", ["negative", "past_pool"])
