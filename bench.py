@@ -857,7 +857,8 @@ def bench_gqa_union(args, torch, qa, synth):
     sm = 1.0 / math.sqrt(128)
     G = kv.num_q_heads // kv.num_kv_heads
     sums = [qa.SparseDecodeStep(kv, k, sm) for _ in range(rot)]
-    unions = [qa.UnionDecodeStep(kv, k, sm) for _ in range(rot)]
+    unions = [qa.UnionDecodeStep(kv, k, sm) for _ in range(rot)]   # fused union
+    seps = [qa.UnionDecodeStep(kv, k, sm, fused=False) for _ in range(rot)]
 
     def call(steps, i):
         c = insts[i]
@@ -865,7 +866,7 @@ def bench_gqa_union(args, torch, qa, synth):
                  c["page_table"], c["seq_lens"])
 
     res = {}
-    for name, steps in (("sum", sums), ("union", unions)):
+    for name, steps in (("sum", sums), ("union", unions), ("union_separate", seps)):
         for i in range(rot):
             call(steps, i)
         torch.cuda.synchronize()
@@ -878,7 +879,7 @@ def bench_gqa_union(args, torch, qa, synth):
                 for i in range(rot)]
         res[name] = dict(us=t["mean"], bytes=sum(b) / rot,
                          pages=sum(kept) / rot)
-    u, sm_ = res["union"], res["sum"]
+    u, sm_, us = res["union"], res["sum"], res["union_separate"]
 
     # the union step's calls one by one, for its roofline
     def e_heads(i):
@@ -901,9 +902,16 @@ def bench_gqa_union(args, torch, qa, synth):
                                     c["page_table"], c["seq_lens"], st.sel, G * k,
                                     sm, st.out, st.workspace)
 
+    def un_att(i):
+        c, st = insts[i], unions[i]
+        qa.quest_union_sparse_decode_attn(kv, c["q"], c["k_pool"], c["v_pool"],
+                                          c["page_table"], c["seq_lens"], st.sel_heads,
+                                          k, sm, st.sel, st.out, st.workspace)
+
     t_calls = {name: graph_batch(torch, f, rot, 100, warm=1)["mean"] for name, f in (
         ("quest_estimate_heads", e_heads), ("quest_topk_pages", tk_heads),
-        ("quest_union_pages", un), ("quest_sparse_decode_attn", att))}
+        ("quest_union_pages", un), ("quest_sparse_decode_attn", att),
+        ("quest_union_sparse_decode_attn", un_att))}
     lens = [int(x) for x in insts[0]["seq_lens"].cpu()]
     Hq, Hkv, mp = kv.num_q_heads, kv.num_kv_heads, kv.max_pages_per_seq
     sb = step_bytes(lens, Hkv, Hq, k, sel=unions[0].sel.cpu().numpy())
@@ -911,16 +919,24 @@ def bench_gqa_union(args, torch, qa, synth):
     names = {"quest_estimate_heads": "estimate_kernel (per head)",
              "quest_topk_pages": "topk_kernel",
              "quest_union_pages": "union_kernel",
-             "quest_sparse_decode_attn": "attn_split_kernel+attn_merge_kernel"}
+             "quest_sparse_decode_attn": "attn_split_kernel+attn_merge_kernel",
+             "quest_union_sparse_decode_attn":
+                 "attn_split_kernel+attn_merge_kernel (union inside)"}
     b_calls = {
         "quest_estimate_heads": (sb["meta"] + sb["q"] + sb["table"],
                                  {"scores_written": Hq * mp * 4}),
         "quest_topk_pages": (0, {"scores_read": Hq * mp * 4, "sel_written": Hq * k * 4}),
         "quest_union_pages": (0, {"sel_read": Hq * k * 4, "union_written": Hkv * G * k * 4}),
         "quest_sparse_decode_attn": (sb["kv"] + sb["q"] + sb["out"],
-                                     {"sel_read": Hkv * G * k * 4})}
-    ku = {names[c_]: t_calls[c_] for c_ in t_calls}
-    kb = {names[c_]: b_calls[c_] for c_ in b_calls}
+                                     {"sel_read": Hkv * G * k * 4}),
+        "quest_union_sparse_decode_attn": (sb["kv"] + sb["q"] + sb["out"],
+                                           {"sel_heads_read": Hq * k * 4,
+                                            "union_written": Hkv * G * k * 4})}
+    # the roofline: the step's calls but the two the fused call replaces
+    step_calls = [c_ for c_ in t_calls
+                  if c_ not in ("quest_union_pages", "quest_sparse_decode_attn")]
+    ku = {names[c_]: t_calls[c_] for c_ in step_calls}
+    kb = {names[c_]: b_calls[c_] for c_ in step_calls}
     # what each rule keeps of full attention, on every rotating cache
     rec = {}
     for name, steps in (("group_sum", sums), ("union", unions)):
@@ -945,7 +961,11 @@ def bench_gqa_union(args, torch, qa, synth):
                    "rotating_caches": rot},
         "union": {"us_per_step": round(u["us"], 3), "bytes_per_step": int(u["bytes"]),
                   "effective_GBps": round(u["bytes"] / (u["us"] * 1e-6) / 1e9, 1),
-                  "pages_per_kv_head": round(u["pages"], 1)},
+                  "pages_per_kv_head": round(u["pages"], 1),
+                  "step": "quest_estimate_heads, quest_topk_pages_ex per query head, "
+                          "quest_union_sparse_decode_attn (the union built inside "
+                          "the attention launch)"},
+        "union_separate_us_per_step": round(us["us"], 3),
         "group_sum": {"us_per_step": round(sm_["us"], 3),
                       "bytes_per_step": int(sm_["bytes"]),
                       "effective_GBps": round(sm_["bytes"] / (sm_["us"] * 1e-6) / 1e9, 1),

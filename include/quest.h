@@ -330,6 +330,26 @@ QUEST_API quest_status quest_decode_attn(
     void* stream);
 
 /*
+ * quest_union_pages followed by quest_sparse_decode_attn over its output, in
+ * one launch (+ the split merge), with the same results bit for bit ([G]
+ * Best Practices 2: every query head of a group attends the union of the
+ * group's per-head Top-K pages; [G] attention equation over their valid
+ * tokens).  sel_heads is int32 [batch][Hq][k_pages] as for
+ * quest_union_pages; sel_union, int32 [batch][Hkv][G * k_pages], receives
+ * the union lists (ascending, then -1); out and the workspace
+ * (quest_workspace_size(kv, G * k_pages) bytes) are those of
+ * quest_sparse_decode_attn with k_pages' = G * k_pages.  Every workgroup of
+ * a (request, kv-head) row builds the row's union in LDS, so the separate
+ * union launch and its round trip go away.  Requires G * k_pages <= 4096
+ * and max_pages_per_seq <= 32768 (QUEST_ERR_UNSUPPORTED otherwise).
+ */
+QUEST_API quest_status quest_union_sparse_decode_attn(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const int32_t* sel_heads, int32_t k_pages, float sm_scale, int32_t* sel_union,
+    float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * quest_update_page_meta in append mode followed by quest_decode_attn, in
  * one launch (+ the split merge), with the same results bit for bit: each
  * request appends token L_b - 1 (k_new / v_new [batch][Hkv][d], written

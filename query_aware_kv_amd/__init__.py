@@ -21,7 +21,7 @@ from ._abi import (  # noqa: F401
     quest_decode_attn, quest_estimate, quest_sparse_decode_attn,
     quest_sparse_decode_step, quest_step_workspace_size,
     quest_append_estimate, quest_append_decode_attn, quest_estimate_heads,
-    quest_union_pages,
+    quest_union_pages, quest_union_sparse_decode_attn, UNION_LIST_MAX,
     quest_stream_read_probe, quest_topk_pages, quest_topk_pages_ex,
     quest_topk_sparse_decode_attn, quest_topk_sparse_decode_attn_ex,
     quest_topk_sparse_decode_attn_splits, quest_merge_attn_splits,
@@ -142,11 +142,16 @@ class SparseDecodeStep:
 class UnionDecodeStep:
     """The GQA group rule of per-head selection + union ("Guide to Quest",
     Best Practices 2): quest_estimate_heads, quest_topk_pages_ex per query
-    head, quest_union_pages, then quest_sparse_decode_attn over the union
-    (up to G * k_pages pages per kv-head, shared by the group's heads)."""
+    head, then attention over the union of a group's lists (up to
+    G * k_pages pages per kv-head, shared by the group's heads).  The union
+    is built inside the attention launch (quest_union_sparse_decode_attn)
+    when G * k_pages <= UNION_LIST_MAX, else by quest_union_pages before
+    quest_sparse_decode_attn; `fused=False` takes the second path always.
+    Both give the same bits."""
 
     def __init__(self, kv: PagedKV, k_pages: int, sm_scale: float | None = None,
-                 device="cuda", n_sink: int = 0, n_local: int = 0):
+                 device="cuda", n_sink: int = 0, n_local: int = 0,
+                 fused: bool | None = None):
         self.kv = kv
         self.k_pages = int(k_pages)
         self.n_sink, self.n_local = int(n_sink), int(n_local)
@@ -166,6 +171,8 @@ class UnionDecodeStep:
         self.out = torch.empty(B, Hq, kv.head_dim, dtype=torch.float32,
                                device=device)
         self.workspace = alloc_workspace(kv, self.group * self.k_pages, device)
+        fits = self.group * self.k_pages <= UNION_LIST_MAX
+        self.fused = fits if fused is None else bool(fused) and fits
 
     def __call__(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_lens,
                  stream=None) -> torch.Tensor:
@@ -173,6 +180,12 @@ class UnionDecodeStep:
                              self.scores, stream)
         quest_topk_pages_ex(self.kv_heads, self.scores, seq_lens, self.k_pages,
                             self.n_sink, self.n_local, self.sel_heads, stream)
+        if self.fused:
+            quest_union_sparse_decode_attn(self.kv, q, k_pool, v_pool, page_table,
+                                           seq_lens, self.sel_heads, self.k_pages,
+                                           self.sm_scale, self.sel, self.out,
+                                           self.workspace, stream)
+            return self.out
         quest_union_pages(self.kv, self.sel_heads, self.k_pages, self.sel,
                           stream)
         quest_sparse_decode_attn(self.kv, q, k_pool, v_pool, page_table,

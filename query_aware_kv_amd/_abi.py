@@ -91,6 +91,8 @@ def _load():
         "quest_append_decode_attn": [KV, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                      P, P, ctypes.c_size_t, P],
         "quest_union_pages": [KV, P, I, P, P],
+        "quest_union_sparse_decode_attn": [KV, P, P, P, P, P, P, I, ctypes.c_float,
+                                           P, P, P, ctypes.c_size_t, P],
         "quest_topk_sparse_decode_attn_ex": [KV, P, P, P, P, P, P, I, I, I,
                                              ctypes.c_float, P, P, P,
                                              ctypes.c_size_t, P],
@@ -463,6 +465,32 @@ def quest_estimate_heads(kv: PagedKV, q, kmin, kmax, page_table, seq_lens,
         _ptr(seq_lens, "seq_lens", torch.int32, (kv.batch,)),
         _ptr(scores, "scores", torch.float32,
              (kv.batch, kv.num_q_heads, kv.max_pages_per_seq)),
+        _stream(stream)))
+
+
+# Longest union list (G * k_pages) quest_union_sparse_decode_attn builds.
+UNION_LIST_MAX = 4096
+
+
+def quest_union_sparse_decode_attn(kv: PagedKV, q, k_pool, v_pool, page_table,
+                                   seq_lens, sel_heads, k_pages: int, sm_scale: float,
+                                   sel_union, out, workspace, stream=None) -> None:
+    dt = kv.torch_dtype
+    i32 = torch.int32
+    G = kv.num_q_heads // kv.num_kv_heads
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.quest_union_sparse_decode_attn(
+        ctypes.byref(kv),
+        _ptr(q, "q", dt, (kv.batch, kv.num_q_heads, kv.head_dim)),
+        _ptr(k_pool, "k_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(v_pool, "v_pool", dt, _pool_shape(kv), host_ok=True),
+        _ptr(page_table, "page_table", i32, (kv.batch, kv.max_pages_per_seq)),
+        _ptr(seq_lens, "seq_lens", i32, (kv.batch,)),
+        _ptr(sel_heads, "sel_heads", i32, (kv.batch, kv.num_q_heads, k_pages)),
+        int(k_pages), float(sm_scale),
+        _ptr(sel_union, "sel_union", i32, (kv.batch, kv.num_kv_heads, G * k_pages)),
+        _ptr(out, "out", torch.float32, (kv.batch, kv.num_q_heads, kv.head_dim)),
+        _ptr(workspace, "workspace"), ctypes.c_size_t(ws_bytes),
         _stream(stream)))
 
 

@@ -124,13 +124,10 @@ quest_status check_attention_common(const quest_paged_kv* kv, const void* q,
   return QUEST_OK;
 }
 
-quest_status run_attention(const quest_paged_kv* kv, const void* q,
-                           const void* k_pool, const void* v_pool,
-                           const int32_t* page_table, const int32_t* seq_lens,
-                           const int32_t* sel, int list_len, float sm_scale,
-                           float* out, void* workspace, size_t workspace_bytes,
-                           void* stream, const char* fn,
-                           const quest::AttnAppend* append = nullptr) {
+// The attention workspace for a list of list_len entries.
+quest_status check_attention_workspace(const quest_paged_kv* kv, int list_len,
+                                       const void* workspace, size_t workspace_bytes,
+                                       const char* fn) {
   const size_t need = quest::attention_workspace_bytes(*kv, list_len);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
@@ -140,6 +137,19 @@ quest_status run_attention(const quest_paged_kv* kv, const void* q,
     if (!aligned16(workspace))
       return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: `workspace` is misaligned", fn);
   }
+  return QUEST_OK;
+}
+
+quest_status run_attention(const quest_paged_kv* kv, const void* q,
+                           const void* k_pool, const void* v_pool,
+                           const int32_t* page_table, const int32_t* seq_lens,
+                           const int32_t* sel, int list_len, float sm_scale,
+                           float* out, void* workspace, size_t workspace_bytes,
+                           void* stream, const char* fn,
+                           const quest::AttnAppend* append = nullptr) {
+  const quest_status s =
+      check_attention_workspace(kv, list_len, workspace, workspace_bytes, fn);
+  if (s != QUEST_OK) return s;
   return hip_status(
       quest::launch_attention(*kv, q, k_pool, v_pool, page_table, seq_lens, sel,
                               list_len, sm_scale, out, workspace,
@@ -323,6 +333,35 @@ QUEST_API quest_status quest_sparse_decode_attn(
   return run_attention(kv, q, k_pool, v_pool, page_table, seq_lens, sel_pages,
                        k_pages, sm_scale, out, workspace, workspace_bytes,
                        stream, fn);
+}
+
+QUEST_API quest_status quest_union_sparse_decode_attn(
+    const quest_paged_kv* kv, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+    const int32_t* sel_heads, int32_t k_pages, float sm_scale, int32_t* sel_union,
+    float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "quest_union_sparse_decode_attn";
+  quest_status s = check_attention_common(kv, q, k_pool, v_pool, page_table,
+                                          seq_lens, sm_scale, out, fn);
+  if (s != QUEST_OK) return s;
+  REQUIRE_PTR(sel_heads, aligned4(sel_heads));
+  REQUIRE_PTR(sel_union, aligned4(sel_union));
+  if (k_pages < 1)
+    return fail(QUEST_ERR_INVALID_ARGUMENT, "%s: k_pages must be >= 1", fn);
+  const int64_t G = kv->num_q_heads / kv->num_kv_heads;
+  if (G * k_pages > quest::kUnionListMax)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: G * k_pages = %lld > %d", fn,
+                (long long)(G * k_pages), quest::kUnionListMax);
+  if (kv->max_pages_per_seq > quest::kTopkMaxPages)
+    return fail(QUEST_ERR_UNSUPPORTED, "%s: max_pages_per_seq %d > %d", fn,
+                kv->max_pages_per_seq, quest::kTopkMaxPages);
+  s = check_attention_workspace(kv, (int)(G * k_pages), workspace, workspace_bytes, fn);
+  if (s != QUEST_OK) return s;
+  return hip_status(quest::launch_union_attention(*kv, q, k_pool, v_pool, page_table,
+                                                  seq_lens, sel_heads, k_pages, sm_scale,
+                                                  sel_union, out, workspace,
+                                                  static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 static quest_status run_topk_attention(

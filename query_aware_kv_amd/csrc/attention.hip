@@ -34,6 +34,13 @@ __device__ __forceinline__ void widen_word(uint32_t x, uint32_t& lo, uint32_t& h
   hi = nhi;
 }
 
+// UNION's LDS: a bitmap over the row's pages and the row's union list.
+struct UnionSmem {
+  uint32_t bm[kTopkMaxPages / 32];
+  uint32_t wsum[kAttnWaves];
+  int32_t list[kUnionListMax];
+};
+
 // The pools' pointer type: restrict-qualified unless the append mode also
 // writes the pools through ap.
 template <bool APPEND>
@@ -47,7 +54,15 @@ using PoolPtr = std::conditional_t<APPEND, const uint16_t*, const uint16_t* __re
 // loop it writes the token into the pool and the widened box.  No other
 // workgroup reads that page, and nothing of the append is held in registers
 // across the loop, so the kernel keeps the plain instance's occupancy.
-template <DType T, int G, int PPW, int SUB, bool APPEND = false>
+//
+// UNION (sparse only, quest_union_sparse_decode_attn): `sel` holds the
+// group's per-query-head lists ([b][g*G .. g*G+G-1][k], list_len = G*k
+// entries from unit * list_len), and the list the workgroup walks is their
+// union, built in LDS by every workgroup of the row as quest_union_pages
+// builds it: the listed pages in [0, max_pages) set bits of a bitmap, the
+// set bits are written out in ascending order, then -1 up to list_len.
+// Each workgroup also writes its range of that list to union_out.
+template <DType T, int G, int PPW, int SUB, bool APPEND = false, bool UNION = false>
 __global__ void __launch_bounds__(256)
 attn_split_kernel(const uint16_t* __restrict__ q,
                   PoolPtr<APPEND> k_pool,
@@ -57,8 +72,10 @@ attn_split_kernel(const uint16_t* __restrict__ q,
                   const int32_t* __restrict__ sel, int list_len, int Hkv,
                   int max_pages, int num_pool_pages, float qscale,
                   float* __restrict__ out, float* __restrict__ ws_o,
-                  float* __restrict__ ws_ml, AttnAppend ap) {
+                  float* __restrict__ ws_ml, AttnAppend ap,
+                  int32_t* __restrict__ union_out) {
   __shared__ AttnSmem<G> sm;
+  __shared__ std::conditional_t<UNION, UnionSmem, int> usm;
   const int unit = blockIdx.y;  // b * Hkv + g
   const int b = unit / Hkv, g = unit - (unit / Hkv) * Hkv;
   const int split = blockIdx.x, nsplit = gridDim.x;
@@ -104,6 +121,56 @@ attn_split_kernel(const uint16_t* __restrict__ q,
   AttnState<G> vst;
   if constexpr (G >= 2) mfma_attn_init(mst);
   else attn_init(vst);
+  if constexpr (UNION) {
+    // The entries go out 4 per thread at a time, unconditionally from
+    // clamped indices (the first 4 before the bitmap is cleared), so that
+    // each group costs one round trip.
+    const int32_t* src = sel + (int64_t)unit * list_len;
+    int e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) e[u] = src[min(u * 256 + tid, list_len - 1)];
+    const int words = (max_pages + 31) >> 5;
+    for (int w = tid; w < words; w += 256) usm.bm[w] = 0u;
+    __syncthreads();
+    for (int base = 0; base < list_len; base += 4 * 256) {
+      if (base > 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = src[min(base + u * 256 + tid, list_len - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * 256 + tid, p = e[u];
+        if (i < list_len && p >= 0 && p < max_pages) atomicOr(&usm.bm[p >> 5], 1u << (p & 31));
+      }
+    }
+    __syncthreads();
+    // thread t owns bitmap words [t * wpt, (t + 1) * wpt); one block scan of
+    // their bit counts gives each thread the list position of its first page
+    const int wpt = (words + 255) >> 8, w0 = tid * wpt;
+    uint32_t cnt = 0;
+    for (int w = w0; w < w0 + wpt && w < words; ++w) cnt += __popc(usm.bm[w]);
+    const uint32_t incl = wave_scan_incl(cnt);
+    if (lane == kWave - 1) usm.wsum[wid] = incl;
+    __syncthreads();
+    uint32_t off = incl - cnt, total = 0;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      if (w < wid) off += usm.wsum[w];
+      total += usm.wsum[w];
+    }
+    for (int w = w0; w < w0 + wpt && w < words; ++w) {
+      uint32_t bits = usm.bm[w];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1;
+        usm.list[off++] = w * 32 + bit;
+      }
+    }
+    for (int i = (int)total + tid; i < list_len; i += 256) usm.list[i] = -1;
+    __syncthreads();
+    for (int64_t i = lo + tid; i < hi; i += 256)
+      union_out[(int64_t)unit * list_len + i] = usm.list[i];
+  }
   for (int64_t c0 = lo; c0 < hi; c0 += kAttnWaves * PPW) {
     // List entries, then their table entries: neither waits for the length
     // (both are in bounds on their own); the length only masks afterwards.
@@ -116,7 +183,9 @@ attn_split_kernel(const uint16_t* __restrict__ q,
 #pragma unroll
     for (int pi = 0; pi < PPW; ++pi) {
       const int64_t i = i0 + pi;
-      if (sel) {
+      if constexpr (UNION) {
+        jr[pi] = i < hi ? usm.list[min(i, (int64_t)list_len - 1)] : -1;
+      } else if (sel) {
         const int e = sel[(int64_t)unit * list_len + min(i, (int64_t)list_len - 1)];
         jr[pi] = i < hi ? e : -1;
       } else {
@@ -515,31 +584,32 @@ void launch_merge(const quest_paged_kv& kv, const float* ws_o,
 
 namespace {
 
-template <DType T, int G, int PPW, int SUB, bool APPEND>
+template <DType T, int G, int PPW, int SUB, bool APPEND, bool UNION>
 void launch_split(const quest_paged_kv& kv, const void* q, const void* k_pool,
                   const void* v_pool, const int32_t* page_table,
                   const int32_t* seq_lens, const int32_t* sel, int list_len,
                   float qscale, float* out, float* ws_o, float* ws_ml,
-                  int nsplit, const AttnAppend& ap, hipStream_t stream) {
+                  int nsplit, const AttnAppend& ap, int32_t* union_out,
+                  hipStream_t stream) {
   dim3 grid((unsigned)nsplit, (unsigned)(kv.batch * kv.num_kv_heads));
-  attn_split_kernel<T, G, PPW, SUB, APPEND><<<grid, 256, 0, stream>>>(
+  attn_split_kernel<T, G, PPW, SUB, APPEND, UNION><<<grid, 256, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), page_table, seq_lens, sel,
       list_len, kv.num_kv_heads, kv.max_pages_per_seq, kv.num_pool_pages,
-      qscale, out, ws_o, ws_ml, ap);
+      qscale, out, ws_o, ws_ml, ap, union_out);
 }
 
-template <DType T, int SUB, bool APPEND>
+template <DType T, int SUB, bool APPEND, bool UNION>
 void dispatch(int G, int ppw, const quest_paged_kv& kv, const void* q,
               const void* k_pool, const void* v_pool,
               const int32_t* page_table, const int32_t* seq_lens,
               const int32_t* sel, int list_len, float qscale, float* out,
               float* ws_o, float* ws_ml, int nsplit, const AttnAppend& ap,
-              hipStream_t stream) {
-#define QUEST_SPLIT(GG, PP)                                                              \
-  launch_split<T, GG, PP, SUB, APPEND>(kv, q, k_pool, v_pool, page_table, seq_lens, sel, \
-                                       list_len, qscale, out, ws_o, ws_ml, nsplit, ap,   \
-                                       stream)
+              int32_t* union_out, hipStream_t stream) {
+#define QUEST_SPLIT(GG, PP)                                                               \
+  launch_split<T, GG, PP, SUB, APPEND, UNION>(kv, q, k_pool, v_pool, page_table, seq_lens, \
+                                              sel, list_len, qscale, out, ws_o, ws_ml,     \
+                                              nsplit, ap, union_out, stream)
   // ppw never exceeds max_ppw(SUB) (the append mode: the dense plan's 1 or
   // 2): only those variants are built
   auto by_ppw = [&](auto gg) {
@@ -588,15 +658,19 @@ size_t attention_workspace_bytes(const quest_paged_kv& kv, int list_len) {
   return need;
 }
 
-hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
-                            const void* k_pool, const void* v_pool,
-                            const int32_t* page_table, const int32_t* seq_lens,
-                            const int32_t* sel, int list_len, float sm_scale,
-                            float* out, void* workspace, hipStream_t stream,
-                            const AttnAppend* append) {
+namespace {
+
+// union_out non-null: the union mode (sel holds the per-head lists).
+hipError_t run_split_and_merge(const quest_paged_kv& kv, const void* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* page_table, const int32_t* seq_lens,
+                               const int32_t* sel, int list_len, float sm_scale,
+                               float* out, void* workspace, hipStream_t stream,
+                               const AttnAppend* append, int32_t* union_out) {
   const int G = kv.num_q_heads / kv.num_kv_heads;
-  // the append mode is dense only
+  // the append mode is dense only, the union mode sparse only
   const bool app = append != nullptr && sel == nullptr;
+  const bool uni = union_out != nullptr && sel != nullptr;
   const Plan pl = sel ? attention_plan(kv, list_len) : dense_plan(kv, app);
   const size_t slots = (size_t)kv.batch * kv.num_q_heads * pl.nsplit;
   float* ws_o = static_cast<float*>(workspace);
@@ -604,16 +678,20 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
   const float qscale = sm_scale * kLog2e;
   const AttnAppend ap = app ? *append : AttnAppend{nullptr, nullptr, nullptr, nullptr,
                                                    nullptr, nullptr};
-#define QUEST_DISPATCH(TT, SS)                                                          \
-  do {                                                                                  \
-    if (app)                                                                            \
-      dispatch<TT, SS, true>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,    \
-                             sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit, ap,    \
-                             stream);                                                   \
-    else                                                                                \
-      dispatch<TT, SS, false>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,   \
-                              sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit, ap,   \
-                              stream);                                                  \
+#define QUEST_DISPATCH(TT, SS)                                                               \
+  do {                                                                                       \
+    if (app)                                                                                 \
+      dispatch<TT, SS, true, false>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,  \
+                                    sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit, ap,  \
+                                    nullptr, stream);                                        \
+    else if (uni)                                                                            \
+      dispatch<TT, SS, false, true>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens,  \
+                                    sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit, ap,  \
+                                    union_out, stream);                                      \
+    else                                                                                     \
+      dispatch<TT, SS, false, false>(G, pl.ppw, kv, q, k_pool, v_pool, page_table, seq_lens, \
+                                     sel, list_len, qscale, out, ws_o, ws_ml, pl.nsplit, ap, \
+                                     nullptr, stream);                                       \
   } while (0)
   const bool s32 = kv.page_size == 32;
   if (kv.dtype == QUEST_F16) {
@@ -626,6 +704,33 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
 #undef QUEST_DISPATCH
   if (pl.nsplit > 1) launch_merge(kv, ws_o, ws_ml, pl.nsplit, out, stream);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
+                            const void* k_pool, const void* v_pool,
+                            const int32_t* page_table, const int32_t* seq_lens,
+                            const int32_t* sel, int list_len, float sm_scale,
+                            float* out, void* workspace, hipStream_t stream,
+                            const AttnAppend* append) {
+  return run_split_and_merge(kv, q, k_pool, v_pool, page_table, seq_lens, sel, list_len,
+                             sm_scale, out, workspace, stream, append, nullptr);
+}
+
+// The plan is the sparse plan for the G * k_pages entries of the union
+// list, as for quest_sparse_decode_attn over quest_union_pages' output, so
+// the two compositions give the same bits.
+hipError_t launch_union_attention(const quest_paged_kv& kv, const void* q,
+                                  const void* k_pool, const void* v_pool,
+                                  const int32_t* page_table, const int32_t* seq_lens,
+                                  const int32_t* sel_heads, int k_pages, float sm_scale,
+                                  int32_t* sel_union, float* out, void* workspace,
+                                  hipStream_t stream) {
+  const int G = kv.num_q_heads / kv.num_kv_heads;
+  return run_split_and_merge(kv, q, k_pool, v_pool, page_table, seq_lens, sel_heads,
+                             G * k_pages, sm_scale, out, workspace, stream, nullptr,
+                             sel_union);
 }
 
 }  // namespace quest

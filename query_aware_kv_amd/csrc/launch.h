@@ -77,6 +77,19 @@ hipError_t launch_attention(const quest_paged_kv& kv, const void* q,
                             const int32_t* sel, int list_len, float sm_scale,
                             float* out, void* workspace, hipStream_t stream,
                             const AttnAppend* append = nullptr);
+// Union mode (quest_union_sparse_decode_attn): each attention workgroup
+// builds its row's union of the group's per-head lists (sel_heads
+// [B][Hq][k_pages]) in LDS, walks its range of it as the sparse plan for
+// G * k_pages entries gives, and writes that range to sel_union
+// [B][Hkv][G * k_pages].  G * k_pages <= kUnionListMax, max_pages <=
+// kTopkMaxPages.
+constexpr int kUnionListMax = 4096;
+hipError_t launch_union_attention(const quest_paged_kv& kv, const void* q,
+                                  const void* k_pool, const void* v_pool,
+                                  const int32_t* page_table, const int32_t* seq_lens,
+                                  const int32_t* sel_heads, int k_pages, float sm_scale,
+                                  int32_t* sel_union, float* out, void* workspace,
+                                  hipStream_t stream);
 
 // Top-K + sparse attention in one launch (each workgroup selects its row).
 constexpr int kTopkAttnMaxPages = 8192;

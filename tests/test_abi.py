@@ -282,6 +282,40 @@ def test_append_decode_attn_validation():
         _abi.QUEST_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_union_sparse_decode_attn_validation():
+    k = kv(num_kv_heads=8)                          # groups of 4
+    P = ctypes.c_void_p
+    kp = 128
+    st, need = ws_size(k, 4 * kp)
+    assert st == 0 and need > 0
+    names = ["q", "k_pool", "v_pool", "page_table", "seq_lens", "sel_heads"]
+    args = [P(FAKE)] * len(names)
+    call = qa.LIB.quest_union_sparse_decode_attn
+    for i, name in enumerate(names):
+        bad = list(args)
+        bad[i] = None
+        assert call(ctypes.byref(k), *bad, kp, 0.088, P(FAKE), P(FAKE), P(FAKE), need,
+                    None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+        assert name in qa.LIB.quest_last_error().decode()
+    for pos in range(3):                             # sel_union, out, workspace
+        tail = [P(FAKE), P(FAKE), P(FAKE)]
+        tail[pos] = None
+        want = _abi.QUEST_ERR_WORKSPACE_TOO_SMALL if pos == 2 else \
+            _abi.QUEST_ERR_INVALID_ARGUMENT
+        assert call(ctypes.byref(k), *args, kp, 0.088, *tail, need, None) == want
+    assert call(ctypes.byref(k), *args, 0, 0.088, P(FAKE), P(FAKE), P(FAKE), need,
+                None) == _abi.QUEST_ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(k), *args, kp, 0.088, P(FAKE), P(FAKE), P(FAKE), need - 16,
+                None) == _abi.QUEST_ERR_WORKSPACE_TOO_SMALL
+    # the union list must fit the workgroups' LDS: G * k_pages <= 4096
+    assert call(ctypes.byref(k), *args, 1025, 0.088, P(FAKE), P(FAKE), P(FAKE), 1 << 40,
+                None) == _abi.QUEST_ERR_UNSUPPORTED
+    assert "4096" in qa.LIB.quest_last_error().decode()
+    big = kv(num_kv_heads=8, max_pages_per_seq=32769, num_pool_pages=32769)
+    assert call(ctypes.byref(big), *args, kp, 0.088, P(FAKE), P(FAKE), P(FAKE), 1 << 40,
+                None) == _abi.QUEST_ERR_UNSUPPORTED
+
+
 def test_last_error_is_per_thread():
     """Each host thread reads the message of its own last failed call."""
     import threading
