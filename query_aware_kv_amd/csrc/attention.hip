@@ -457,7 +457,12 @@ int64_t dense_resident(const quest_paged_kv& kv, int ppw, bool append = false);
 // row's selection each, so fewer, fuller ones pay there: at least 256 of
 // them (2048 waves), with at most 2 pages per wave (4 made the kernel slower
 // through its registers).  Measured on the 32-head layers: 8 splits of 2
-// pages per wave beat 16 of one at budgets up to 2048 tokens.
+// pages per wave beat 16 of one at budgets up to 2048 tokens.  Query
+// groups (G >= 2) take a candidate once the grid holds half the resident
+// count, which for their 2- and 4-page instances (2 workgroups per CU) is
+// one workgroup per CU: the union lists of a 32/8-head layer (8 rows of 512
+// entries) then run 32 splits of 4 pages per wave, whose merge is the
+// plain one, instead of 64 of 2 (union call 16.5 -> 15.5 us).
 // quest_workspace_size covers the 4-wave and the 8-wave plan of a list (and,
 // for whole rows, the dense plans, plain and append).
 AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves) {
@@ -468,8 +473,12 @@ AttnPlan attention_plan(const quest_paged_kv& kv, int list_len, int waves) {
   int ppw = 1;
   for (int cand = min(cap, max_ppw(kv.page_size / kTileRows)); cand > 1; cand /= 2) {
     const int64_t ns = (list_len + waves * cand - 1) / (waves * cand);
-    const int64_t need =
-        topk_wg ? min_wgs : std::min<int64_t>(min_wgs, dense_resident(kv, cand));
+    int64_t need = min_wgs;
+    if (!topk_wg) {
+      const int64_t resident = dense_resident(kv, cand);
+      need = std::min<int64_t>(min_wgs, kv.num_q_heads > kv.num_kv_heads ? resident / 2
+                                                                         : resident);
+    }
     if (units * ns >= need) { ppw = cand; break; }
   }
   int nsplit = (list_len + waves * ppw - 1) / (waves * ppw);
